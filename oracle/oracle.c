@@ -1,0 +1,259 @@
+/*
+ * Float64 CPU oracle for single-token (decode) grouped-query attention over a
+ * paged fp16 KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check
+ * and the bench's CPU-baseline leg load this code.  It shares no source,
+ * header, table or helper with the GPU library, and includes none of its
+ * headers.
+ *
+ * What it computes is the plain definition, with no blocking, fusion or
+ * reordering beyond it:
+ *
+ *  - Page-table gather (vllm-metal kernels page, cf-1.com/news/5525226,
+ *    section "什么是 Paged Attention"): token t of sequence s lives in
+ *    physical page block_tables[s][t / bs], slot t mod bs.  Pool layout
+ *    [num_blocks][Hkv][bs][D], fp16.
+ *  - GQA grouping (same page, section "Metal 并行模型", and the voxtral.c
+ *    page, dpshk.com/news/5521762, section "单 token attention 内核"): the
+ *    G = Hq/Hkv query heads of a group share one KV head; query head h reads
+ *    KV head h / G (consecutive heads form a group).
+ *  - Softmax attention over every token t < L: z_t = scale * (q . k_t),
+ *    out = sum_t exp(z_t - max z) v_t / sum_t exp(z_t - max z), computed in
+ *    two passes (max, then exp-sum and weighted sum), float64 throughout.
+ *    The log2-space folding that the vllm-metal page describes (section
+ *    "GQA 解码内核的四个提速技巧", item 1) changes no value: 2^(z log2 e) = e^z.
+ *  - Split-KV partials (same section, item 4): for each partition i of P
+ *    tokens, m_i is the partition's maximum score in log2 units (max z times
+ *    log2 e), l_i the partition's exp-sum relative to that maximum (a plain
+ *    sum, not its log), and o_i the partition's softmax-weighted V average
+ *    normalised by its own l_i.
+ *  - Merge of partials: M = max m_i, w_i = l_i 2^(m_i - M),
+ *    out = sum_i w_i o_i / sum_i w_i.
+ *
+ * fp16 values widen to double exactly (decoded from their bits below).
+ * Build with -O2 -ffp-contract=off and no fast-math.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_LOG2E 1.44269504088896340735992468100189214
+
+/* IEEE 754 binary16 -> double, exactly: sign, 5-bit exponent (bias 15),
+ * 10-bit fraction; exponent 0 is subnormal (no implicit 1), 31 is inf/NaN. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);               /* frac * 2^-10 * 2^-14 */
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/1024) 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const int32_t *block_tables, *seq_lens;
+    int S, Hq, Hkv, D, bs, max_blocks;
+    long long num_blocks;
+    double scale;
+    int P, NP;                      /* partials only */
+    double *out;                    /* [S][Hq][D] */
+    double *m, *l, *o;              /* partials: [S][Hq][NP], [S][Hq][NP], [S][Hq][NP][D] */
+    int nthreads, tid;
+    int status;
+} job_t;
+
+/* Address of element (block, kv head g, slot j, dim 0) in the pool. */
+static const uint16_t *row_ptr(const uint16_t *pool, long long block, int g, int j,
+                               int Hkv, int bs, int D)
+{
+    return pool + (((block * Hkv + g) * (long long)bs + j) * (long long)D);
+}
+
+/* Scores z_t for t in [t0, t1) of row (s, h).  Returns 0, or -1 when a page
+ * id is outside the pool. */
+static int scores(const job_t *J, int s, int h, int t0, int t1, double *z)
+{
+    int G = J->Hq / J->Hkv;
+    int g = h / G;
+    const uint16_t *qrow = J->q + ((long long)s * J->Hq + h) * J->D;
+    for (int t = t0; t < t1; ++t) {
+        long long b = J->block_tables[(long long)s * J->max_blocks + t / J->bs];
+        if (b < 0 || b >= J->num_blocks) return -1;
+        const uint16_t *krow = row_ptr(J->k, b, g, t % J->bs, J->Hkv, J->bs, J->D);
+        double dot = 0.0;
+        for (int d = 0; d < J->D; ++d)
+            dot += oracle_half_to_double(qrow[d]) * oracle_half_to_double(krow[d]);
+        z[t - t0] = J->scale * dot;
+    }
+    return 0;
+}
+
+/* Softmax-weighted average of V over tokens [t0, t1) with scores z, relative
+ * to the maximum score zmax.  Writes sum_t e_t v_t / sum_t e_t into res and
+ * returns the exp-sum sum_t e_t (e_t = exp(z_t - zmax)). */
+static double weighted_v(const job_t *J, int s, int h, int t0, int t1, const double *z,
+                         double zmax, double *acc, double *res)
+{
+    int G = J->Hq / J->Hkv;
+    int g = h / G;
+    double sum = 0.0;
+    for (int d = 0; d < J->D; ++d) acc[d] = 0.0;
+    for (int t = t0; t < t1; ++t) {
+        long long b = J->block_tables[(long long)s * J->max_blocks + t / J->bs];
+        const uint16_t *vrow = row_ptr(J->v, b, g, t % J->bs, J->Hkv, J->bs, J->D);
+        double e = exp(z[t - t0] - zmax);
+        sum += e;
+        for (int d = 0; d < J->D; ++d) acc[d] += e * oracle_half_to_double(vrow[d]);
+    }
+    for (int d = 0; d < J->D; ++d) res[d] = acc[d] / sum;
+    return sum;
+}
+
+static void *attention_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    int maxL = 0;
+    for (int s = 0; s < J->S; ++s) if (J->seq_lens[s] > maxL) maxL = J->seq_lens[s];
+    double *z = (double *)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->D);
+    if (!z || !acc) { J->status = -2; free(z); free(acc); return NULL; }
+    long long rows = (long long)J->S * J->Hq;
+    for (long long r = J->tid; r < rows; r += J->nthreads) {
+        int s = (int)(r / J->Hq), h = (int)(r % J->Hq);
+        int L = J->seq_lens[s];
+        double *dst = J->out + r * J->D;
+        if (L <= 0) {                       /* empty sequence: defined as zeros */
+            for (int d = 0; d < J->D; ++d) dst[d] = 0.0;
+            continue;
+        }
+        if (scores(J, s, h, 0, L, z) != 0) { J->status = -1; break; }
+        double zmax = -INFINITY;            /* pass 1: the maximum score */
+        for (int t = 0; t < L; ++t) if (z[t] > zmax) zmax = z[t];
+        weighted_v(J, s, h, 0, L, z, zmax, acc, dst);   /* pass 2 */
+    }
+    free(z);
+    free(acc);
+    return NULL;
+}
+
+static void *partials_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    double *z = (double *)malloc(sizeof(double) * (size_t)J->P);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->D);
+    if (!z || !acc) { J->status = -2; free(z); free(acc); return NULL; }
+    long long rows = (long long)J->S * J->Hq;
+    for (long long r = J->tid; r < rows; r += J->nthreads) {
+        int s = (int)(r / J->Hq);
+        int h = (int)(r % J->Hq);
+        int L = J->seq_lens[s];
+        int nparts = (L + J->P - 1) / J->P;
+        for (int i = 0; i < nparts && i < J->NP; ++i) {
+            int t0 = i * J->P;
+            int t1 = t0 + J->P < L ? t0 + J->P : L;
+            if (scores(J, s, h, t0, t1, z) != 0) { J->status = -1; goto done; }
+            double zmax = -INFINITY;
+            for (int t = t0; t < t1; ++t) if (z[t - t0] > zmax) zmax = z[t - t0];
+            long long pi = r * J->NP + i;
+            J->l[pi] = weighted_v(J, s, h, t0, t1, z, zmax, acc, J->o + pi * J->D);
+            J->m[pi] = ORACLE_LOG2E * zmax;
+        }
+    }
+done:
+    free(z);
+    free(acc);
+    return NULL;
+}
+
+static int run_jobs(job_t *base, int nthreads, void *(*fn)(void *))
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    job_t jobs[256];
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = *base;
+        jobs[i].nthreads = nthreads;
+        jobs[i].tid = i;
+        jobs[i].status = 0;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        if (pthread_create(&th[i], NULL, fn, &jobs[i]) != 0) return -3;
+    fn(&jobs[0]);
+    int st = jobs[0].status;
+    for (int i = 1; i < nthreads; ++i) {
+        pthread_join(th[i], NULL);
+        if (jobs[i].status != 0) st = jobs[i].status;
+    }
+    return st;
+}
+
+/* out[S][Hq][D] = softmax attention of every query head over its sequence's
+ * paged K/V.  Returns 0, -1 if a page id falls outside [0, num_blocks), -2 on
+ * allocation failure. */
+int oracle_paged_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *block_tables, const int32_t *seq_lens,
+                           int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                           long long num_blocks, double scale, double *out, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k_cache; J.v = v_cache;
+    J.block_tables = block_tables; J.seq_lens = seq_lens;
+    J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
+    J.num_blocks = num_blocks; J.scale = scale; J.out = out;
+    return run_jobs(&J, nthreads, attention_worker);
+}
+
+/* Per-partition triples for partitions i < ceil(L/P) (and i < NP); entries of
+ * partitions past a sequence's end are left as they were. */
+int oracle_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                    const int32_t *block_tables, const int32_t *seq_lens,
+                    int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                    long long num_blocks, double scale, int P, int NP,
+                    double *m, double *l, double *o, int nthreads)
+{
+    if (P <= 0 || NP <= 0) return -4;
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k_cache; J.v = v_cache;
+    J.block_tables = block_tables; J.seq_lens = seq_lens;
+    J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
+    J.num_blocks = num_blocks; J.scale = scale; J.P = P; J.NP = NP;
+    J.m = m; J.l = l; J.o = o;
+    return run_jobs(&J, nthreads, partials_worker);
+}
+
+/* Merge per-partition triples of every (s, h) into out[S][Hq][D]. */
+void oracle_merge(const double *m, const double *l, const double *o, const int32_t *seq_lens,
+                  int S, int Hq, int D, int P, int NP, double *out)
+{
+    for (long long r = 0; r < (long long)S * Hq; ++r) {
+        int L = seq_lens[r / Hq];
+        int nparts = (L + P - 1) / P;
+        if (nparts > NP) nparts = NP;
+        double *dst = out + r * D;
+        for (int d = 0; d < D; ++d) dst[d] = 0.0;
+        if (nparts <= 0) continue;
+        double M = -INFINITY;
+        for (int i = 0; i < nparts; ++i) if (m[r * NP + i] > M) M = m[r * NP + i];
+        double wsum = 0.0;
+        for (int i = 0; i < nparts; ++i) {
+            double w = l[r * NP + i] * exp2(m[r * NP + i] - M);
+            wsum += w;
+            for (int d = 0; d < D; ++d) dst[d] += w * o[(r * NP + i) * D + d];
+        }
+        for (int d = 0; d < D; ++d) dst[d] /= wsum;
+    }
+}
