@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: paged GQA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kernel auto|dot|mfma]
+
+One step = the whole path on device-resident inputs: partition plan (host),
+decode kernel, partition reduce kernel.  W untimed steps, then K steps timed
+between two device synchronisations.  Prints ONE JSON line:
+
+  value            KV-read throughput, GB/s: algorithmic K+V bytes of one step
+                   (4 * Hkv * D * sum L) / (timed wall time / K)
+  ms_per_step      timed wall time / K
+  roofline         the decode kernel against HBM peak (8 TB/s): algorithmic
+                   bytes per launch / mean launch duration (HIP events on the
+                   launch stream, inside the timed region); `traffic` is the
+                   HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE
+                   (profiles/), null if the kernel sources changed since
+  cpu_baseline     the float64 oracle on a bounded sample of the same workload,
+                   on this host's cores
+
+Default workload: 4 sequences x 131072 tokens, (16 q, 2 kv, 256) heads,
+block 32, the planner choosing the partition size.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DESCRIPTIONS = {
+    "tiny_1x64": "1 seq x 64 tokens, (32q, 8kv, 128), block 16, unsplit",
+    "batch8_2k": "8 seqs, L uniform in [1, 2048], (32q, 8kv, 128), block 16, P=512",
+    "long32_16k": "32 seqs, L uniform in [4096, 16384], (24q, 4kv, 256), block 32, K x3",
+    "mixed64_32k": "64 seqs, mixed L (25% L=1, 25% 1-3 token tails, rest up to 32768), "
+                   "(16q, 2kv, 128), block 8, P=512",
+    "long4_128k": "4 seqs x 131072 tokens, (16q, 2kv, 256), block 32, pool 2x, planner",
+}
+KERNEL_SOURCES = {
+    1: ["paged_gqa_kv_decode_amd/csrc/decode_dot.hip"],
+    2: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+}
+
+
+def sources_sha(kernel: int) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kernel, []) + ["paged_gqa_kv_decode_amd/csrc/vk_kernels.h"]:
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, partition: int, kernel: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_P{partition}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256_16") != sources_sha(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, sample_seqs: int):
+    """Time the float64 oracle on the first `sample_seqs` sequences."""
+    import numpy as np
+    import oracle
+    from paged_gqa_kv_decode_amd.workloads import kv_read_bytes
+    sub_sl = wl.seq_lens[:sample_seqs]
+    args = (wl.q[:sample_seqs], wl.k_cache, wl.v_cache, wl.block_tables[:sample_seqs], sub_sl,
+            wl.scale)
+    nthreads = oracle.default_threads()
+    t = time.perf_counter()
+    oracle.paged_attention_arrays(*args, nthreads=nthreads)
+    dt = time.perf_counter() - t
+    kv = kv_read_bytes(sub_sl, wl.num_kv_heads, wl.head_dim)
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s (KV-read)", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"first {sample_seqs} of {wl.num_seqs} sequences ({int(np.sum(sub_sl))} tokens, "
+                      f"all {wl.num_q_heads} q heads), 1 run, {dt:.2f} s wall",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long4_128k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--partition", type=int, default=None,
+                    help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this path runs on one GPU only (asked for {max(args.gpus, world)}); "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_gqa_kv_decode_amd import binding as vb
+    from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, make_workload
+
+    t0 = time.time()
+    wl = make_workload(args.workload)
+    gen_s = time.time() - t0
+    P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
+    kernel = {"auto": vb.KERNEL_AUTO, "dot": vb.KERNEL_DOT, "mfma": vb.KERNEL_MFMA}[args.kernel]
+    vb.select_decode_kernel(kernel)
+
+    dev = vb.device_inputs(wl)
+    q, k, v, bt, sl = dev
+    torch.cuda.synchronize()
+    kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+
+    # Scratch sized once from a first plan; every step plans again (host) and
+    # reuses it (the plan depends only on the host seq_lens).
+    step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out)
+    P, NP = step0.plan.partition_size, step0.plan.max_num_partitions
+
+    def one_step(ev=None):
+        plan = vb.plan_partitions(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                  wl.block_size, wl.max_blocks_per_seq, P_req, 0)
+        assert plan.partition_size == P and plan.max_num_partitions == NP
+        if ev is not None:
+            ev[0].record(stream)
+        if P:
+            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, P, NP, None, step0.max_logits,
+                                step0.exp_sums, step0.tmp_out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            vb.paged_gqa_reduce(step0.max_logits, step0.exp_sums, step0.tmp_out, sl, P, out,
+                                stream)
+        else:
+            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, 0, 1, out, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    kernel_ran = vb.last_plan().kernel
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(args.steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ms_per_step = wall * 1e3 / args.steps
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_mean_s = float(dec_ms.mean()) * 1e-3
+    achieved = kv_bytes / dec_mean_s / 1e9
+    traffic = load_traffic(args.workload, P, kernel_ran)
+
+    result = {
+        "metric": "decode-attention µs/step and KV-read HBM GB/s (% of MI355X peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0, sigma) fp16 K/V/q, shuffled pages)",
+        "config": {"workload": args.workload, "description": DESCRIPTIONS[args.workload],
+                   "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
+                   "partition_size": P, "max_num_partitions": NP,
+                   "decode_kernel": {1: "dot", 2: "mfma"}.get(kernel_ran, str(kernel_ran))},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "kernel_us": {"decode_mean": round(float(dec_ms.mean()) * 1e3, 2),
+                      "decode_median": round(float(np.median(dec_ms)) * 1e3, 2),
+                      "decode_p5": round(float(np.percentile(dec_ms, 5)) * 1e3, 2),
+                      "decode_p95": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
+                      "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)},
+        "kv_read_bytes": kv_bytes,
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, max(1, min(args.cpu_sample_seqs, wl.num_seqs)))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

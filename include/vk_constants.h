@@ -1,0 +1,34 @@
+/*
+ * Compile-time constants shared by the host library and the HIP kernels of
+ * libvkpaged, so that the two sides cannot drift apart.
+ *
+ * Sources (vllm-metal kernels page, cf-1.com/news/5525226):
+ *  - section "三大 Metal 内核": a default KV partition of 512 tokens and page
+ *    sizes 32, 16 and 8 are shared constants baked into both host and kernel;
+ *  - section "GQA 解码内核的四个提速技巧", item 4: split-KV partitions of 256
+ *    or 512 tokens;
+ *  - section "分发层": the admitted (query heads, KV heads, head dim) triples,
+ *    a fixed work budget of 33 simdgroups per GPU core, and a 512 MiB cap on
+ *    the scratch of one attention call.
+ */
+#ifndef VK_CONSTANTS_H
+#define VK_CONSTANTS_H
+
+#define VK_PARTITION_LARGE 512
+#define VK_PARTITION_SMALL 256
+
+#define VK_DEFAULT_BUDGET_PER_CU 33
+#define VK_DEFAULT_SCRATCH_CAP (512ull * 1024ull * 1024ull)
+
+/* Admitted geometries (Hq, Hkv, D).  Four geometries x three page sizes give
+ * twelve kernel specialisations. */
+#define VK_NUM_GEOMETRIES 4
+#define VK_GEOMETRY_LIST {{32, 8, 128}, {24, 4, 256}, {16, 2, 128}, {16, 2, 256}}
+#define VK_NUM_BLOCK_SIZES 3
+#define VK_BLOCK_SIZE_LIST {8, 16, 32}
+
+/* A KV page id outside [0, num_blocks), or a device seq_len the page table
+ * cannot hold, never reaches memory: the kernel reads page 0 instead and the
+ * affected (sequence, head) results become NaN. */
+
+#endif /* VK_CONSTANTS_H */

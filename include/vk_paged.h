@@ -1,0 +1,192 @@
+/*
+ * libvkpaged — single-token (decode) grouped-query attention over a paged fp16
+ * KV cache, for AMD Instinct MI355X (gfx950).  Plain C ABI: raw pointers and
+ * sizes, no C++ or framework types.
+ *
+ * What is computed (vllm-metal kernels page, cf-1.com/news/5525226):
+ *  - section "什么是 Paged Attention": the KV cache is split into fixed-size
+ *    pages; block_tables maps each logical page of a sequence to a physical
+ *    page of a shared pool;
+ *  - section "Metal 并行模型": one workgroup per (partition, KV head,
+ *    sequence), holding every query head of that KV head's group, so a K/V
+ *    page is fetched once for the whole group;
+ *  - section "GQA 解码内核的四个提速技巧": (1) online softmax in log2 space
+ *    (log2 e folded into the scale, every exponential an exp2, running max
+ *    and exp-sum kept in registers, one pass over K/V); (2) the loop advances
+ *    page by page with the page id read once and shared by the wave, and K/V
+ *    are read straight from device memory; (3) several tokens in flight per
+ *    loop step, with a masked tail; (4) split-KV partitions of 256 or 512
+ *    tokens whose partial results are (max in log2 units, exp-sum, output
+ *    normalised by that exp-sum), merged by a separate reduce step;
+ *  - section "分发层": admitted geometries, a partition-size choice against a
+ *    work budget of 33 per core that counts only full partitions, and a
+ *    512 MiB scratch cap.
+ * For each sequence s, query head h (KV head g = h / (Hq/Hkv)) and the
+ * L = seq_lens[s] tokens t < L:
+ *     z_t = scale * (q[s,h,:] . K[block_tables[s][t/bs], g, t%bs, :])
+ *     out[s,h,:] = sum_t softmax(z)_t * V[block_tables[s][t/bs], g, t%bs, :]
+ *
+ * Memory layouts (all row-major, element strides implied by the sizes):
+ *   q             fp16  [num_seqs, num_q_heads, head_dim]
+ *   k_cache       fp16  [num_blocks, num_kv_heads, block_size, head_dim]
+ *   v_cache       fp16  [num_blocks, num_kv_heads, block_size, head_dim]
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; only the first
+ *                 ceil(L/block_size) entries of a row are ever read
+ *   seq_lens      int32 [num_seqs]
+ *   out           fp32  [num_seqs, num_q_heads, head_dim]
+ *   max_logits    fp32  [num_seqs, num_q_heads, max_num_partitions]
+ *   exp_sums      fp32  [num_seqs, num_q_heads, max_num_partitions]
+ *   tmp_out       fp32  [num_seqs, num_q_heads, max_num_partitions, head_dim]
+ *
+ * Ownership and asynchrony: every tensor pointer is device memory owned by the
+ * caller.  The library allocates nothing, frees nothing and keeps no pointer
+ * after a call returns.  GPU calls only enqueue work on `stream` (a
+ * hipStream_t; NULL = the default stream) and never synchronise; the caller
+ * keeps buffers alive until that work has finished and must enqueue
+ * vk_paged_gqa_reduce on the same stream after vk_paged_gqa_decode.
+ *
+ * Errors: every function returns a vk_status.  All argument validation is
+ * host-only and happens before any HIP call, so a rejected call launches
+ * nothing and writes nothing.  A failed launch returns VK_ERR_HIP and
+ * vk_last_hip_error() returns the HIP error code.  Device-side values the
+ * host cannot see (seq_lens and block_tables contents) are guarded in the
+ * kernels: an entry outside [0, num_blocks), or a length above
+ * max_blocks_per_seq*block_size or above max_num_partitions*partition_size,
+ * makes the affected outputs NaN instead of reading out of bounds; a length
+ * <= 0 yields zeros.
+ *
+ * Thread safety: all functions are re-entrant; the only state is
+ * thread-local diagnostics (vk_last_plan, vk_last_hip_error).
+ */
+#ifndef VK_PAGED_H
+#define VK_PAGED_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vk_status;
+enum {
+    VK_OK = 0,
+    VK_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+    VK_ERR_BAD_DIM = 2,     /* a size is non-positive or inconsistent */
+    VK_ERR_GEOMETRY = 3,    /* (Hq, Hkv, D) is not an admitted geometry */
+    VK_ERR_BLOCK_SIZE = 4,  /* block_size not in {8, 16, 32} */
+    VK_ERR_PARTITION = 5,   /* partition size or count not allowed */
+    VK_ERR_SEQ_LEN = 6,     /* a host seq_len is < 1 or beyond the page table */
+    VK_ERR_SCRATCH_CAP = 7, /* split-KV scratch would exceed the cap */
+    VK_ERR_HIP = 8          /* a HIP runtime call or launch failed */
+};
+
+/* Decode kernel families; see vk_select_decode_kernel. */
+enum {
+    VK_KERNEL_AUTO = 0,
+    VK_KERNEL_DOT = 1,      /* VALU: lane-sliced fp16 dot2 products, DPP reductions */
+    VK_KERNEL_MFMA = 2      /* matrix cores for the QK and PV contractions */
+};
+
+typedef struct vk_plan {
+    int32_t  partition_size;     /* 0 = unsplit, else 256 or 512 */
+    int32_t  max_num_partitions; /* NP = ceil(max_s L_s / P); 1 when unsplit */
+    int64_t  work_full_parts;    /* W(P) = Hq * sum_s floor(L_s / P) at the chosen P */
+    int64_t  budget;             /* budget_per_cu * cu_count */
+    int32_t  cu_count;           /* compute units the budget was sized for */
+    int32_t  kernel;             /* decode: VK_KERNEL_* that ran; planner: 0 */
+    uint64_t scratch_bytes;      /* S * Hq * NP * (D + 2) * 4 */
+    int32_t  grid[3];            /* decode: launch grid (partitions, Hkv, S) */
+    int32_t  block;              /* decode: threads per workgroup */
+} vk_plan;
+
+/*
+ * vk_plan_partitions — choose the split-KV partition size for one call.
+ * Host-only: makes no HIP call when cu_count > 0.
+ *
+ * Rule (vllm-metal kernels page, section "分发层", read as stated in the
+ * design notes): budget B = budget_per_cu * cu_count.  Work W(P) =
+ * Hq * sum_s floor(L_s / P) counts only full partitions.  With
+ * partition_request == -1 the planner picks P = 512 when W(512) >= B, else
+ * P = 256; 0 asks for the unsplit path; 256 or 512 forces that size.
+ * NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
+ * exceed the cap (no fallback path exists).
+ *
+ *   seq_lens_host       host int32 [num_seqs], each in [1, max_blocks_per_seq*block_size]
+ *   cu_count            compute units; 0 = query the current HIP device
+ *   budget_per_cu       0 = 33
+ *   scratch_cap_bytes   0 = 512 MiB
+ *   plan_out            host struct, written on VK_OK only
+ * Also recorded as this thread's vk_last_plan.
+ */
+vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq,
+                             int32_t partition_request, int32_t cu_count,
+                             int32_t budget_per_cu, uint64_t scratch_cap_bytes,
+                             vk_plan* plan_out);
+
+/*
+ * vk_paged_gqa_decode — the decode kernel: for every (partition, KV head,
+ * sequence) one workgroup reads that KV head's pages of the partition once and
+ * serves all its query heads.
+ *
+ * partition_size == 0 (unsplit): each workgroup covers a whole sequence and
+ *   writes out[s, h, :] directly; max_logits/exp_sums/tmp_out may be NULL and
+ *   max_num_partitions must be 1.
+ * partition_size == 256 or 512 (split): partition i covers tokens
+ *   [i*P, min(L, (i+1)*P)); for each i < ceil(L/P) it writes
+ *     max_logits[s,h,i] = max over the partition of z_t * log2(e)
+ *     exp_sums[s,h,i]   = sum over the partition of 2^(z_t*log2(e) - max)
+ *     tmp_out[s,h,i,:]  = (sum 2^(z_t*log2(e) - max) * v_t) / exp_sums
+ *   and nothing for i >= ceil(L/P); `out` is not touched (may be NULL).
+ *   Requires max_num_partitions >= ceil(max L / P) (see vk_plan_partitions).
+ * scale is the softmax scale (usually 1/sqrt(head_dim)); the kernel applies
+ * scale*log2(e) (rounded once to fp32) to the fp32 dot products.
+ */
+vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                              int32_t partition_size, int32_t max_num_partitions,
+                              float* out, float* max_logits, float* exp_sums, float* tmp_out,
+                              void* stream);
+
+/*
+ * vk_paged_gqa_reduce — merge the split-KV partials (vllm-metal kernels page,
+ * section "GQA 解码内核的四个提速技巧", item 4: the GQA path reuses the
+ * split-KV reducer).  For each (s, h) with n = ceil(L/P) partitions:
+ *     M = max_i max_logits[i];  w_i = exp_sums[i] * 2^(max_logits[i] - M)
+ *     out[s,h,:] = sum_i w_i * tmp_out[i,:] / sum_i w_i
+ * reading only i < n (n == 1 copies tmp_out[0] exactly).  L <= 0 writes
+ * zeros.  head_dim must be 128 or 256; partition_size 256 or 512.
+ */
+vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums,
+                              const float* tmp_out, const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, void* stream);
+
+/*
+ * vk_select_decode_kernel — A/B switch for this thread's later decode calls
+ * (the pages describe an equivalent switch back to a former path for A/B
+ * comparison).  VK_KERNEL_AUTO picks the fastest family for the geometry.
+ * Returns the previous setting, or -1 for an unknown value (setting kept).
+ */
+int32_t vk_select_decode_kernel(int32_t kernel);
+
+/* Human-readable name of a status code (static storage). */
+const char* vk_status_string(vk_status s);
+
+/* HIP error code of this thread's last VK_ERR_HIP (0 if none). */
+int32_t vk_last_hip_error(void);
+
+/* This thread's last plan: from vk_plan_partitions, or the launch shape of
+ * the last vk_paged_gqa_decode (mirrors the pages' "last dispatch"
+ * diagnostics).  Returns VK_ERR_NULL_ARG if out is NULL. */
+vk_status vk_last_plan(vk_plan* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VK_PAGED_H */

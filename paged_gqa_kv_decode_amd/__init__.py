@@ -1,0 +1,11 @@
+"""paged_gqa_kv_decode_amd — paged GQA decode attention for AMD MI355X.
+
+The compute path is libvkpaged.so (HIP kernels for gfx950 behind a C ABI,
+include/vk_paged.h); `binding` marshals torch tensors into it.  `workloads`
+draws the seeded synthetic inputs.
+"""
+from .binding import (  # noqa: F401
+    DecodeStep, KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA, Plan, VkError, device_inputs, last_plan,
+    lib, paged_gqa_decode, paged_gqa_reduce, plan_partitions, select_decode_kernel,
+    status_string,
+)

@@ -1,0 +1,261 @@
+"""ctypes binding of libvkpaged (include/vk_paged.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libvkpaged.so.  torch provides device memory (tensors) and the
+stream handle.  If the library is not built, every call raises; there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvkpaged.so")
+
+VK_OK = 0
+STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_SIZE",
+                5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP"}
+KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
+
+EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_reduce",
+            "vk_select_decode_kernel", "vk_status_string", "vk_last_hip_error", "vk_last_plan")
+
+
+class VkError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str = ""):
+        name = STATUS_NAMES.get(code, str(code))
+        msg = f"{fn} failed: VK_ERR_{name} ({status_string(code)})"
+        if detail:
+            msg += f" {detail}"
+        super().__init__(msg)
+        self.code = code
+        self.name = name
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("partition_size", ctypes.c_int32), ("max_num_partitions", ctypes.c_int32),
+                ("work_full_parts", ctypes.c_int64), ("budget", ctypes.c_int64),
+                ("cu_count", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("scratch_bytes", ctypes.c_uint64), ("grid", ctypes.c_int32 * 3),
+                ("block", ctypes.c_int32)]
+
+
+@dataclass
+class Plan:
+    partition_size: int
+    max_num_partitions: int
+    work_full_parts: int
+    budget: int
+    cu_count: int
+    kernel: int
+    scratch_bytes: int
+    grid: tuple
+    block: int
+
+    @classmethod
+    def from_c(cls, p: _Plan) -> "Plan":
+        return cls(p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget,
+                   p.cu_count, p.kernel, p.scratch_bytes, tuple(p.grid), p.block)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvkpaged.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_gqa_kv_decode_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    L.vk_plan_partitions.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, u64,
+                                     ctypes.POINTER(_Plan)]
+    L.vk_plan_partitions.restype = i32
+    L.vk_paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                      ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
+    L.vk_paged_gqa_decode.restype = i32
+    L.vk_paged_gqa_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    L.vk_paged_gqa_reduce.restype = i32
+    L.vk_select_decode_kernel.argtypes = [i32]
+    L.vk_select_decode_kernel.restype = i32
+    L.vk_status_string.argtypes = [i32]
+    L.vk_status_string.restype = ctypes.c_char_p
+    L.vk_last_hip_error.argtypes = []
+    L.vk_last_hip_error.restype = i32
+    L.vk_last_plan.argtypes = [ctypes.POINTER(_Plan)]
+    L.vk_last_plan.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return lib().vk_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != VK_OK:
+        detail = ""
+        if code == 8:
+            detail = f"hip error {lib().vk_last_hip_error()}"
+        raise VkError(fn, code, detail)
+
+
+def select_decode_kernel(kernel: int) -> int:
+    prev = lib().vk_select_decode_kernel(int(kernel))
+    if prev < 0:
+        raise ValueError(f"unknown decode kernel {kernel}")
+    return prev
+
+
+def last_plan() -> Plan:
+    p = _Plan()
+    _check("vk_last_plan", lib().vk_last_plan(ctypes.byref(p)))
+    return Plan.from_c(p)
+
+
+def plan_partitions(seq_lens_host, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    block_size: int, max_blocks_per_seq: int, partition_request: int = -1,
+                    cu_count: int = 0, budget_per_cu: int = 0,
+                    scratch_cap_bytes: int = 0) -> Plan:
+    sl = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    p = _Plan()
+    code = lib().vk_plan_partitions(sl.ctypes.data if sl.size else None, int(sl.size),
+                                    num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, partition_request, cu_count,
+                                    budget_per_cu, scratch_cap_bytes, ctypes.byref(p))
+    _check("vk_plan_partitions", code)
+    return Plan.from_c(p)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name):
+    import torch
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    _ = torch
+
+
+def paged_gqa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                     partition_size: int, max_num_partitions: int, out=None, max_logits=None,
+                     exp_sums=None, tmp_out=None, stream=None) -> None:
+    """Enqueue the decode kernel.  Shapes are read from the tensors:
+    q [S,Hq,D] fp16, k/v [num_blocks,Hkv,bs,D] fp16, block_tables [S,max_blocks]
+    int32, seq_lens [S] int32; out [S,Hq,D] fp32 (unsplit) or max_logits /
+    exp_sums [S,Hq,NP], tmp_out [S,Hq,NP,D] fp32 (split)."""
+    import torch
+    for t, dt, n in ((q, torch.float16, "q"), (k_cache, torch.float16, "k_cache"),
+                     (v_cache, torch.float16, "v_cache"), (block_tables, torch.int32, "block_tables"),
+                     (seq_lens, torch.int32, "seq_lens"), (out, torch.float32, "out"),
+                     (max_logits, torch.float32, "max_logits"), (exp_sums, torch.float32, "exp_sums"),
+                     (tmp_out, torch.float32, "tmp_out")):
+        _need(t, dt, n)
+    S, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache / q shapes disagree")
+    if tuple(block_tables.shape[:1]) != (S,) or tuple(seq_lens.shape) != (S,):
+        raise ValueError("block_tables / seq_lens must have num_seqs rows")
+    if out is not None and tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be [S, Hq, D]")
+    if partition_size:
+        for t, shp, n in ((max_logits, (S, Hq, max_num_partitions), "max_logits"),
+                          (exp_sums, (S, Hq, max_num_partitions), "exp_sums"),
+                          (tmp_out, (S, Hq, max_num_partitions, D), "tmp_out")):
+            if t is not None and tuple(t.shape) != shp:
+                raise ValueError(f"{n} must be {shp}")
+    code = lib().vk_paged_gqa_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv,
+        D, bs, block_tables.shape[1], nb, float(scale), int(partition_size),
+        int(max_num_partitions), _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
+        _stream_handle(stream))
+    _check("vk_paged_gqa_decode", code)
+
+
+def paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: int, out,
+                     stream=None) -> None:
+    """Enqueue the partition reduce: out [S,Hq,D] fp32 from the split partials."""
+    import torch
+    for t, dt, n in ((max_logits, torch.float32, "max_logits"), (exp_sums, torch.float32, "exp_sums"),
+                     (tmp_out, torch.float32, "tmp_out"), (seq_lens, torch.int32, "seq_lens"),
+                     (out, torch.float32, "out")):
+        _need(t, dt, n)
+    S, Hq, NP, D = tmp_out.shape
+    if tuple(max_logits.shape) != (S, Hq, NP) or tuple(exp_sums.shape) != (S, Hq, NP):
+        raise ValueError("partials shapes disagree")
+    if tuple(out.shape) != (S, Hq, D) or tuple(seq_lens.shape) != (S,):
+        raise ValueError("out / seq_lens shapes disagree")
+    code = lib().vk_paged_gqa_reduce(_ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
+                                     _ptr(seq_lens), S, Hq, D, int(partition_size), NP,
+                                     _ptr(out), _stream_handle(stream))
+    _check("vk_paged_gqa_reduce", code)
+
+
+class DecodeStep:
+    """One decode step on device-resident inputs: plan once (host seq_lens),
+    hold the scratch, then `run()` enqueues decode (+ reduce when split)."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, seq_lens_host, scale: float,
+                 partition_request: int = -1, cu_count: int = 0, out=None):
+        import torch
+        S, Hq, D = q.shape
+        nb, Hkv, bs, _ = k_cache.shape
+        self.plan = plan_partitions(seq_lens_host, Hq, Hkv, D, bs, block_tables.shape[1],
+                                    partition_request, cu_count)
+        self.args = (q, k_cache, v_cache, block_tables, seq_lens)
+        self.scale = float(scale)
+        dev = q.device
+        self.out = out if out is not None else torch.empty((S, Hq, D), dtype=torch.float32,
+                                                           device=dev)
+        P, NP = self.plan.partition_size, self.plan.max_num_partitions
+        if P:
+            self.max_logits = torch.empty((S, Hq, NP), dtype=torch.float32, device=dev)
+            self.exp_sums = torch.empty((S, Hq, NP), dtype=torch.float32, device=dev)
+            self.tmp_out = torch.empty((S, Hq, NP, D), dtype=torch.float32, device=dev)
+        else:
+            self.max_logits = self.exp_sums = self.tmp_out = None
+
+    def run(self, stream=None):
+        P, NP = self.plan.partition_size, self.plan.max_num_partitions
+        q, k, v, bt, sl = self.args
+        if P:
+            paged_gqa_decode(q, k, v, bt, sl, self.scale, P, NP, None, self.max_logits,
+                             self.exp_sums, self.tmp_out, stream)
+            paged_gqa_reduce(self.max_logits, self.exp_sums, self.tmp_out, sl, P, self.out,
+                             stream)
+        else:
+            paged_gqa_decode(q, k, v, bt, sl, self.scale, 0, 1, self.out, stream=stream)
+        return self.out
+
+
+def device_inputs(wl, device="cuda"):
+    """Copy a Workload's host arrays to device tensors (q, k, v, bt, sl)."""
+    import torch
+    dev = torch.device(device)
+    return (torch.from_numpy(wl.q).to(dev), torch.from_numpy(wl.k_cache).to(dev),
+            torch.from_numpy(wl.v_cache).to(dev), torch.from_numpy(wl.block_tables).to(dev),
+            torch.from_numpy(wl.seq_lens).to(dev))

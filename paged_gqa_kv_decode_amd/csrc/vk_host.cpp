@@ -1,0 +1,256 @@
+// C-ABI entry points of libvkpaged: validation, partition planning and kernel
+// dispatch.  Everything here is host code; it launches on the caller's stream
+// and never synchronises.  Validation is complete before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "vk_constants.h"
+#include "vk_kernels.h"
+#include "vk_paged.h"
+
+namespace {
+
+thread_local vk_plan t_last_plan = {};
+thread_local int32_t t_last_hip_error = 0;
+thread_local int32_t t_kernel_choice = VK_KERNEL_AUTO;
+
+struct Geometry {
+    int hq, hkv, d;
+};
+constexpr Geometry kGeometries[VK_NUM_GEOMETRIES] = VK_GEOMETRY_LIST;
+constexpr int kBlockSizes[VK_NUM_BLOCK_SIZES] = VK_BLOCK_SIZE_LIST;
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("VK_LOG");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+vk_status geometry_status(int32_t hq, int32_t hkv, int32_t d) {
+    if (hq <= 0 || hkv <= 0 || d <= 0) return VK_ERR_BAD_DIM;
+    if (hq % hkv != 0) return VK_ERR_GEOMETRY;
+    for (const Geometry& g : kGeometries)
+        if (g.hq == hq && g.hkv == hkv && g.d == d) return VK_OK;
+    return VK_ERR_GEOMETRY;
+}
+
+bool block_size_ok(int32_t bs) {
+    for (int b : kBlockSizes)
+        if (b == bs) return true;
+    return false;
+}
+
+vk_status hip_fail(hipError_t e) {
+    t_last_hip_error = static_cast<int32_t>(e);
+    return VK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vk_status_string(vk_status s) {
+    switch (s) {
+        case VK_OK: return "ok";
+        case VK_ERR_NULL_ARG: return "null argument";
+        case VK_ERR_BAD_DIM: return "bad dimension";
+        case VK_ERR_GEOMETRY: return "geometry not admitted (Hq, Hkv, head_dim)";
+        case VK_ERR_BLOCK_SIZE: return "block size not in {8, 16, 32}";
+        case VK_ERR_PARTITION: return "partition size or count not allowed";
+        case VK_ERR_SEQ_LEN: return "sequence length outside [1, max_blocks_per_seq * block_size]";
+        case VK_ERR_SCRATCH_CAP: return "split-KV scratch over the cap";
+        case VK_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int32_t vk_last_hip_error(void) { return t_last_hip_error; }
+
+vk_status vk_last_plan(vk_plan* out) {
+    if (!out) return VK_ERR_NULL_ARG;
+    *out = t_last_plan;
+    return VK_OK;
+}
+
+int32_t vk_select_decode_kernel(int32_t kernel) {
+    if (kernel != VK_KERNEL_AUTO && kernel != VK_KERNEL_DOT) return -1;
+    const int32_t prev = t_kernel_choice;
+    t_kernel_choice = kernel;
+    return prev;
+}
+
+vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int32_t partition_request,
+                             int32_t cu_count, int32_t budget_per_cu, uint64_t scratch_cap_bytes,
+                             vk_plan* plan_out) {
+    if (!seq_lens_host || !plan_out) return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || max_blocks_per_seq <= 0) return VK_ERR_BAD_DIM;
+    vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
+    if (gs != VK_OK) return gs;
+    if (!block_size_ok(block_size)) return VK_ERR_BLOCK_SIZE;
+    if (partition_request != -1 && partition_request != 0 &&
+        partition_request != VK_PARTITION_SMALL && partition_request != VK_PARTITION_LARGE)
+        return VK_ERR_PARTITION;
+    if (cu_count < 0 || budget_per_cu < 0) return VK_ERR_BAD_DIM;
+    const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+    if (cap_tokens > INT32_MAX) return VK_ERR_BAD_DIM;
+
+    int64_t max_len = 0;
+    int64_t full512 = 0, full256 = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t L = seq_lens_host[s];
+        if (L < 1 || L > cap_tokens) return VK_ERR_SEQ_LEN;
+        if (L > max_len) max_len = L;
+        full512 += L / VK_PARTITION_LARGE;
+        full256 += L / VK_PARTITION_SMALL;
+    }
+
+    if (cu_count == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e);
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        cu_count = n;
+    }
+    const int64_t per_cu = budget_per_cu > 0 ? budget_per_cu : VK_DEFAULT_BUDGET_PER_CU;
+    const uint64_t cap = scratch_cap_bytes > 0 ? scratch_cap_bytes : VK_DEFAULT_SCRATCH_CAP;
+
+    vk_plan p = {};
+    p.cu_count = cu_count;
+    p.budget = per_cu * cu_count;
+    if (partition_request == 0) {
+        p.partition_size = 0;
+        p.max_num_partitions = 1;
+        p.work_full_parts = 0;
+        p.scratch_bytes = 0;
+    } else {
+        int32_t P = partition_request;
+        if (P == -1) {
+            // Largest partition first; it is kept only if its full partitions
+            // alone reach the budget, otherwise the smaller size is used.
+            P = ((int64_t)num_q_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
+        }
+        p.partition_size = P;
+        p.max_num_partitions = (int32_t)((max_len + P - 1) / P);
+        p.work_full_parts = (int64_t)num_q_heads * (P == VK_PARTITION_LARGE ? full512 : full256);
+        p.scratch_bytes = (uint64_t)num_seqs * (uint64_t)num_q_heads *
+                          (uint64_t)p.max_num_partitions * (uint64_t)(head_dim + 2) * 4u;
+        if (p.scratch_bytes > cap) return VK_ERR_SCRATCH_CAP;
+    }
+    *plan_out = p;
+    t_last_plan = p;
+    if (log_enabled())
+        std::fprintf(stderr, "[vkpaged] plan: P=%d NP=%d W=%lld budget=%lld cu=%d scratch=%llu\n",
+                     p.partition_size, p.max_num_partitions, (long long)p.work_full_parts,
+                     (long long)p.budget, p.cu_count, (unsigned long long)p.scratch_bytes);
+    return VK_OK;
+}
+
+vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, float* max_logits,
+                              float* exp_sums, float* tmp_out, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return VK_ERR_BAD_DIM;
+    if (num_seqs > 65535) return VK_ERR_BAD_DIM;  // grid.z limit
+    vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
+    if (gs != VK_OK) return gs;
+    if (!block_size_ok(block_size)) return VK_ERR_BLOCK_SIZE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return VK_ERR_BAD_DIM;
+    if (!std::isfinite(scale)) return VK_ERR_BAD_DIM;
+    if (partition_size == 0) {
+        if (!out) return VK_ERR_NULL_ARG;
+        if (max_num_partitions != 1) return VK_ERR_PARTITION;
+    } else if (partition_size == VK_PARTITION_SMALL || partition_size == VK_PARTITION_LARGE) {
+        if (!max_logits || !exp_sums || !tmp_out) return VK_ERR_NULL_ARG;
+        if (max_num_partitions < 1) return VK_ERR_PARTITION;
+        if ((int64_t)max_num_partitions * partition_size > (int64_t)INT32_MAX) return VK_ERR_PARTITION;
+    } else {
+        return VK_ERR_PARTITION;
+    }
+
+    vk::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    // log2(e) folded into the scale once, in double, then rounded to fp32.
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+
+    const int group = num_q_heads / num_kv_heads;
+    const dim3 grid(partition_size == 0 ? 1u : (unsigned)max_num_partitions, (unsigned)num_kv_heads,
+                    (unsigned)num_seqs);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool ok = false;
+    int block = 0;
+    const int32_t kernel = VK_KERNEL_DOT;
+    hipError_t e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
+    if (!ok) return VK_ERR_GEOMETRY;
+    if (e != hipSuccess) return hip_fail(e);
+
+    vk_plan p = {};
+    p.partition_size = partition_size;
+    p.max_num_partitions = max_num_partitions;
+    p.kernel = kernel;
+    p.scratch_bytes = partition_size == 0 ? 0
+                      : (uint64_t)num_seqs * num_q_heads * (uint64_t)max_num_partitions *
+                            (uint64_t)(head_dim + 2) * 4u;
+    p.grid[0] = (int32_t)grid.x;
+    p.grid[1] = (int32_t)grid.y;
+    p.grid[2] = (int32_t)grid.z;
+    p.block = block;
+    t_last_plan = p;
+    return VK_OK;
+}
+
+vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums, const float* tmp_out,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,
+                              float* out, void* stream) {
+    if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !out) return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_seqs > 65535) return VK_ERR_BAD_DIM;
+    if (head_dim != 128 && head_dim != 256) return VK_ERR_GEOMETRY;
+    if (partition_size != VK_PARTITION_SMALL && partition_size != VK_PARTITION_LARGE)
+        return VK_ERR_PARTITION;
+    if (max_num_partitions < 1) return VK_ERR_PARTITION;
+    vk::ReduceArgs a;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.num_q_heads = num_q_heads;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    bool ok = false;
+    hipError_t e = vk::launch_reduce(a, head_dim, dim3((unsigned)num_q_heads, (unsigned)num_seqs),
+                                     static_cast<hipStream_t>(stream), &ok);
+    if (!ok) return VK_ERR_GEOMETRY;
+    if (e != hipSuccess) return hip_fail(e);
+    return VK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI host code (vk_host.cpp) and the HIP
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vk {
+
+struct DecodeArgs {
+    const uint16_t* q;            // fp16 [S, Hq, D]
+    const uint16_t* k;            // fp16 [num_blocks, Hkv, BS, D]
+    const uint16_t* v;            // fp16 [num_blocks, Hkv, BS, D]
+    const int32_t* block_tables;  // [S, max_blocks_per_seq]
+    const int32_t* seq_lens;      // [S]
+    float* out;                   // [S, Hq, D]          (unsplit)
+    float* max_logits;            // [S, Hq, NP]         (split)
+    float* exp_sums;              // [S, Hq, NP]         (split)
+    float* tmp_out;               // [S, Hq, NP, D]      (split)
+    int64_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t partition_size;       // 0 = unsplit
+    int32_t max_num_partitions;
+    float scale_log2e;            // scale * log2(e), rounded once to fp32
+};
+
+struct ReduceArgs {
+    const float* max_logits;
+    const float* exp_sums;
+    const float* tmp_out;
+    const int32_t* seq_lens;
+    float* out;
+    int32_t num_q_heads;
+    int32_t partition_size;
+    int32_t max_num_partitions;
+};
+
+// Each launcher returns hipSuccess or the launch error; `geometry_ok` is
+// false when no specialisation exists for the shape (host code checks first).
+hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,
+                             dim3 grid, hipStream_t stream, bool* geometry_ok, int* block);
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
+                         bool* geometry_ok);
+
+}  // namespace vk

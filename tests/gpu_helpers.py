@@ -1,0 +1,79 @@
+"""Shared helpers of the GPU parity tests (HIP path through the C ABI vs the
+float64 oracle)."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+
+from paged_gqa_kv_decode_amd import binding as vb
+from paged_gqa_kv_decode_amd.workloads import make_workload
+
+# Stated tolerance of the fp32 output against the float64 oracle.
+ATOL = 2e-3          # max over all elements of |gpu - ref|
+RTOL_ROW = 1e-2      # per (s, h) row: ||gpu - ref||_2 / max(||ref||_2, 1e-6)
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=4)
+def named(name: str, canaries: bool = False, pad_value: int = -1):
+    return make_workload(name, canaries=canaries, pad_value=pad_value)
+
+
+def to_device(wl):
+    return vb.device_inputs(wl, "cuda")
+
+
+def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=False,
+            prefill_nan=True, cu_count=0):
+    """One decode step through libvkpaged.  Returns (out float64 numpy, plan,
+    partials or None)."""
+    import torch
+    if dev is None:
+        dev = to_device(wl)
+    q, k, v, bt, sl = dev
+    out = torch.full((wl.num_seqs, wl.num_q_heads, wl.head_dim),
+                     float("nan") if prefill_nan else 0.0, dtype=torch.float32, device="cuda")
+    prev = vb.select_decode_kernel(kernel) if kernel is not None else None
+    try:
+        step = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, partition_request,
+                             cu_count=cu_count, out=out)
+        if step.tmp_out is not None and prefill_nan:
+            step.max_logits.fill_(float("nan"))
+            step.exp_sums.fill_(float("nan"))
+            step.tmp_out.fill_(float("nan"))
+        step.run()
+        plan = vb.last_plan()
+        torch.cuda.synchronize()
+    finally:
+        if prev is not None:
+            vb.select_decode_kernel(prev)
+    parts = None
+    if keep_partials and step.tmp_out is not None:
+        parts = (step.max_logits.cpu().numpy().astype(np.float64),
+                 step.exp_sums.cpu().numpy().astype(np.float64),
+                 step.tmp_out.cpu().numpy().astype(np.float64))
+    return out.cpu().numpy().astype(np.float64), step.plan, plan, parts
+
+
+def err_stats(gpu, ref):
+    d = np.abs(gpu - ref)
+    max_abs = float(np.nanmax(d)) if d.size else 0.0
+    num = np.sqrt(((gpu - ref) ** 2).sum(axis=-1))
+    den = np.maximum(np.sqrt((ref ** 2).sum(axis=-1)), 1e-6)
+    row_rel = float(np.max(num / den)) if num.size else 0.0
+    frac = float(np.mean(np.abs(gpu - ref) <= ATOL + RTOL_ROW * np.abs(ref)))
+    return max_abs, row_rel, frac
+
+
+def assert_parity(gpu, ref, what):
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    max_abs, row_rel, frac = err_stats(gpu, ref)
+    say(f"  {what}: max_abs={max_abs:.3e} max_row_rel={row_rel:.3e} allclose_frac={frac:.6f}")
+    assert max_abs <= ATOL, f"{what}: max abs err {max_abs:.3e} > {ATOL}"
+    assert row_rel <= RTOL_ROW, f"{what}: row rel err {row_rel:.3e} > {RTOL_ROW}"

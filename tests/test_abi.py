@@ -1,0 +1,173 @@
+"""Host-side checks of libvkpaged that need no GPU: the library loads, exports
+every function include/vk_paged.h declares, its planner agrees with the
+oracle's planner rule, and argument validation rejects bad calls before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_gqa_kv_decode_amd import binding as vb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vk_paged.h")
+CODES = {v: k for k, v in vb.STATUS_NAMES.items()}
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = vb.lib()
+    names = declared_functions()
+    assert set(names) == set(vb.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings():
+    for code in range(9):
+        assert vb.status_string(code)
+    assert vb.status_string(99) == "unknown status"
+
+
+def test_select_decode_kernel_roundtrip():
+    prev = vb.select_decode_kernel(vb.KERNEL_DOT)
+    assert vb.select_decode_kernel(prev) == vb.KERNEL_DOT
+    with pytest.raises(ValueError):
+        vb.select_decode_kernel(77)
+
+
+def _c_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu=0, cap=0):
+    try:
+        p = vb.plan_partitions(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap)
+        return dict(partition_size=p.partition_size, max_num_partitions=p.max_num_partitions,
+                    work_full_parts=p.work_full_parts, budget=p.budget, cu_count=p.cu_count,
+                    scratch_bytes=p.scratch_bytes)
+    except vb.VkError as e:
+        return e.name
+
+
+def _o_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu=0, cap=0):
+    try:
+        return oracle.plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap)
+    except oracle.PlanError as e:
+        return e.code
+
+
+GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256)]
+
+
+def test_planner_matches_oracle_rule_random():
+    rng = np.random.default_rng(2024)
+    for it in range(3000):
+        Hq, Hkv, D = GEOMS[rng.integers(4)]
+        bs = int(rng.choice([8, 16, 32]))
+        S = int(rng.integers(1, 70))
+        hi = int(rng.choice([300, 3000, 40000, 200000]))
+        lens = rng.integers(1, hi, size=S).tolist()
+        mb = -(-max(lens) // bs) + int(rng.integers(0, 3))
+        req = int(rng.choice([-1, -1, -1, 0, 256, 512]))
+        cu = int(rng.choice([1, 8, 80, 256, 304]))
+        per_cu = int(rng.choice([0, 0, 1, 33, 64]))
+        cap = int(rng.choice([0, 0, 1 << 20, 64 << 20]))
+        if it % 50 == 0:
+            lens[0] = 0 if it % 100 == 0 else mb * bs + 1       # invalid lengths
+        a = _c_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap)
+        b = _o_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap)
+        assert a == b, (lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap, a, b)
+
+
+def test_planner_long_context_decisions():
+    # 4 x 131072 tokens (16q, 2kv, 256), bs 32 on 256 CUs: W(512) = 16384 >= 8448.
+    p = vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 256)
+    assert (p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget) == (512, 256, 16384, 8448)
+    # 8 seqs up to 2048 tokens: too few full 512 partitions -> 256.
+    p = vb.plan_partitions([2048, 1, 100, 1500, 2000, 512, 513, 7], 32, 8, 128, 16, 128, -1, 256)
+    assert p.partition_size == 256 and p.max_num_partitions == 8
+    assert vb.last_plan().partition_size == 256
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(geom=(32, 8, 64)), "GEOMETRY"),
+    (dict(geom=(30, 8, 128)), "GEOMETRY"),
+    (dict(geom=(0, 8, 128)), "BAD_DIM"),
+    (dict(bs=4), "BLOCK_SIZE"),
+    (dict(req=128), "PARTITION"),
+    (dict(lens=[0]), "SEQ_LEN"),
+    (dict(lens=[10 ** 6]), "SEQ_LEN"),
+    (dict(cap=1000, req=512, lens=[5000] * 8), "SCRATCH_CAP"),
+])
+def test_planner_rejections(args, code):
+    geom = args.get("geom", (32, 8, 128))
+    lens = args.get("lens", [100, 200])
+    got = _c_plan(lens, *geom, args.get("bs", 16), 1000, args.get("req", -1), 256, 0,
+                  args.get("cap", 0))
+    assert got == code
+
+
+def test_planner_null_args():
+    L = vb.lib()
+    assert L.vk_plan_partitions(None, 1, 32, 8, 128, 16, 4, -1, 256, 0, 0, None) == CODES["NULL_ARG"]
+    p = vb._Plan()
+    assert L.vk_last_plan(None) == CODES["NULL_ARG"]
+    assert L.vk_last_plan(ctypes.byref(p)) == 0
+
+
+# ---- decode / reduce validation (fake device pointers; CPU tier only) -------
+FAKE = 0x1000
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=32, Hkv=8, D=128, bs=16, mb=8,
+             nb=64, scale=0.088, P=512, NP=1, out=FAKE, ml=FAKE, es=FAKE, to=FAKE)
+    a.update(kw)
+    return vb.lib().vk_paged_gqa_decode(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"],
+                                        a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"], a["nb"],
+                                        a["scale"], a["P"], a["NP"], a["out"], a["ml"], a["es"],
+                                        a["to"], None)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), "NULL_ARG"), (dict(k=None), "NULL_ARG"), (dict(v=None), "NULL_ARG"),
+    (dict(bt=None), "NULL_ARG"), (dict(sl=None), "NULL_ARG"),
+    (dict(P=0, NP=1, out=None), "NULL_ARG"), (dict(P=512, ml=None), "NULL_ARG"),
+    (dict(P=256, to=None), "NULL_ARG"), (dict(P=512, es=None), "NULL_ARG"),
+    (dict(S=0), "BAD_DIM"), (dict(mb=0), "BAD_DIM"), (dict(nb=0), "BAD_DIM"),
+    (dict(S=70000), "BAD_DIM"), (dict(scale=float("nan")), "BAD_DIM"),
+    (dict(Hq=24, Hkv=8), "GEOMETRY"), (dict(Hq=16, Hkv=2, D=64), "GEOMETRY"),
+    (dict(bs=64), "BLOCK_SIZE"), (dict(P=128), "PARTITION"), (dict(P=512, NP=0), "PARTITION"),
+    (dict(P=0, NP=2), "PARTITION"), (dict(P=512, NP=5_000_000), "PARTITION"),
+    (dict(mb=200_000_000), "BAD_DIM"),
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == CODES[code]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+def test_reduce_validation():
+    R = vb.lib().vk_paged_gqa_reduce
+    assert R(None, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["NULL_ARG"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, None, None) == CODES["NULL_ARG"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 0, 32, 128, 512, 4, FAKE, None) == CODES["BAD_DIM"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 96, 512, 4, FAKE, None) == CODES["GEOMETRY"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 0, 4, FAKE, None) == CODES["PARTITION"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 0, FAKE, None) == CODES["PARTITION"]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_planner_device_query_without_gpu_is_hip_error():
+    code = _c_plan([100], 32, 8, 128, 16, 8, -1, 0)
+    assert code == "HIP"
