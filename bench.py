@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, --steps times (the "
+                         "known-size reference for the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -118,6 +121,21 @@ def main():
     import numpy as np
     import torch
     from paged_gqa_kv_decode_amd import binding as vb
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t) / args.steps
+        print(json.dumps({"copy_bytes": n, "steps": args.steps, "ms": round(dt * 1e3, 4),
+                          "read_GBps": round(n / dt / 1e9, 1)}), flush=True)
+        return
     from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, make_workload
 
     t0 = time.time()

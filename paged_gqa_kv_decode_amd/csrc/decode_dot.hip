@@ -52,6 +52,12 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A product that is rounded to fp32 and never fused into a later add.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 __device__ __forceinline__ float half_at(const uint4& v, int e) {
     const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
     return (float)__builtin_bit_cast(half2v, w)[e & 1];
@@ -109,7 +115,7 @@ struct DotKernel {
                 // Round the score once (no contraction into the later x - m):
                 // the running max and the exponent see the same value, so the
                 // maximal token gets a weight of exactly 1.
-                d = __fmul_rn(row16_sum(d), a.scale_log2e);
+                d = mul_rounded(row16_sum(d), a.scale_log2e);
                 x[n] = valid[n] ? d : -INFINITY;
             }
             float mx = x[0];
