@@ -3,16 +3,22 @@
 // are (max in log2 units, exp-sum, normalised output) and a shared reducer
 // merges them).
 //
-// One workgroup of 256 threads per (query head, sequence).  With n partitions:
-//   M   = max_i m_i                       (block max)
-//   w_i = l_i * 2^(m_i - M),  W = sum w_i (block sum)
-//   out = sum_i w_i o_i / W               (float4 lanes over the head dims,
-//                                          groups of lanes over partitions,
-//                                          LDS sum of the groups)
+// Grid (D / 64, Hq, S): a workgroup of 256 threads owns 64 output dims of one
+// (sequence, query head).  With n partitions:
+//   M   = max_i m_i                        (block max over the n values)
+//   w_i = l_i * 2^(m_i - M),  W = sum w_i  (block sum)
+//   out = sum_i w_i o_i / W
+// For the weighted sum, thread t handles float4 column t % 16 of the 64-dim
+// chunk for partitions i = t / 16 (mod 16), four partitions per loop trip so
+// several loads are in flight, then the 16 partition groups are summed in LDS.
 #include "vk_kernels.h"
 
 namespace vk {
 namespace {
+
+constexpr int kChunk = 64;                 // output dims per workgroup
+constexpr int kLanes = kChunk / 4;         // float4 columns
+constexpr int kGroups = 256 / kLanes;      // partition groups
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -26,30 +32,36 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ void fma4(float4& acc, float w, const float4& o) {
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
-    constexpr int LANES = D / 4;            // float4 lanes per head row
-    constexpr int GROUPS = 256 / LANES;     // partition groups
     __shared__ float s_red[4];
-    __shared__ float4 s_part[GROUPS][LANES];
+    __shared__ float4 s_part[kGroups][kLanes];
 
-    const int h = blockIdx.x, s = blockIdx.y;
+    const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
     const int64_t r = (int64_t)s * Hq + h;
-    float* dst = a.out + r * D;
     const int L = a.seq_lens[s];
+    float4* dst = reinterpret_cast<float4*>(a.out + r * D + chunk * kChunk);
     if (L <= 0) {
-        for (int d = tid; d < D; d += 256) dst[d] = 0.f;
+        if (tid < kLanes) dst[tid] = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
     const int n = min((int)(((int64_t)L + P - 1) / P), NP);
     const float* ml = a.max_logits + r * NP;
     const float* es = a.exp_sums + r * NP;
-    const float4* to = reinterpret_cast<const float4*>(a.tmp_out + r * NP * D);
-    float4* dst4 = reinterpret_cast<float4*>(dst);
+    // row i of this workgroup's 64-dim slice of tmp_out
+    const float4* to = reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * kChunk);
+    constexpr int kRow4 = D / 4;  // float4 stride between partitions
     if (n == 1) {  // a single partition is already normalised
-        if (tid < LANES) dst4[tid] = to[tid];
+        if (tid < kLanes) dst[tid] = to[tid];
         return;
     }
 
@@ -68,29 +80,34 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
     __syncthreads();
     const float W = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
 
-    const int dl = tid % LANES, grp = tid / LANES;
+    const int c = tid % kLanes, grp = tid / kLanes;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = grp; i < n; i += GROUPS) {
-        const float w = es[i] * __builtin_amdgcn_exp2f(ml[i] - M);
-        const float4 o = to[(int64_t)i * LANES + dl];
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
+    int i = grp;
+    for (; i + 3 * kGroups < n; i += 4 * kGroups) {
+        const float4 o0 = to[(int64_t)i * kRow4 + c];
+        const float4 o1 = to[(int64_t)(i + kGroups) * kRow4 + c];
+        const float4 o2 = to[(int64_t)(i + 2 * kGroups) * kRow4 + c];
+        const float4 o3 = to[(int64_t)(i + 3 * kGroups) * kRow4 + c];
+        fma4(acc, es[i] * __builtin_amdgcn_exp2f(ml[i] - M), o0);
+        fma4(acc, es[i + kGroups] * __builtin_amdgcn_exp2f(ml[i + kGroups] - M), o1);
+        fma4(acc, es[i + 2 * kGroups] * __builtin_amdgcn_exp2f(ml[i + 2 * kGroups] - M), o2);
+        fma4(acc, es[i + 3 * kGroups] * __builtin_amdgcn_exp2f(ml[i + 3 * kGroups] - M), o3);
     }
-    s_part[grp][dl] = acc;
+    for (; i < n; i += kGroups)
+        fma4(acc, es[i] * __builtin_amdgcn_exp2f(ml[i] - M), to[(int64_t)i * kRow4 + c]);
+    s_part[grp][c] = acc;
     __syncthreads();
-    if (tid < LANES) {
+    if (tid < kLanes) {
         float4 t = s_part[0][tid];
 #pragma unroll
-        for (int gi = 1; gi < GROUPS; ++gi) {
+        for (int gi = 1; gi < kGroups; ++gi) {
             const float4 u = s_part[gi][tid];
             t.x += u.x;
             t.y += u.y;
             t.z += u.z;
             t.w += u.w;
         }
-        dst4[tid] = make_float4(t.x / W, t.y / W, t.z / W, t.w / W);
+        dst[tid] = make_float4(t.x / W, t.y / W, t.z / W, t.w / W);
     }
 }
 
@@ -99,10 +116,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok) {
     *geometry_ok = true;
+    const dim3 g(head_dim / kChunk, grid.x, grid.y);
     if (head_dim == 128) {
-        hipLaunchKernelGGL(reduce_kernel<128>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(reduce_kernel<128>, g, dim3(256), 0, stream, a);
     } else if (head_dim == 256) {
-        hipLaunchKernelGGL(reduce_kernel<256>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(reduce_kernel<256>, g, dim3(256), 0, stream, a);
     } else {
         *geometry_ok = false;
         return hipSuccess;
