@@ -44,8 +44,11 @@ DESCRIPTIONS = {
 }
 KERNEL_SOURCES = {
     1: ["paged_gqa_kv_decode_amd/csrc/decode_dot.hip"],
-    2: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+    3: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+    4: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+    5: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
 }
+KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4"}
 
 
 def sources_sha(kernel: int) -> str:
@@ -104,7 +107,7 @@ def main():
     ap.add_argument("--workload", default="long4_128k", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--partition", type=int, default=None,
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -142,7 +145,9 @@ def main():
     wl = make_workload(args.workload)
     gen_s = time.time() - t0
     P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
-    kernel = {"auto": vb.KERNEL_AUTO, "dot": vb.KERNEL_DOT, "mfma": vb.KERNEL_MFMA}[args.kernel]
+    kernel = {"auto": vb.KERNEL_AUTO, "dot": vb.KERNEL_DOT, "mfma": vb.KERNEL_MFMA,
+              "mfma1": vb.KERNEL_MFMA_W1, "mfma2": vb.KERNEL_MFMA_W2,
+              "mfma4": vb.KERNEL_MFMA_W4}[args.kernel]
     vb.select_decode_kernel(kernel)
 
     dev = vb.device_inputs(wl)
@@ -217,7 +222,7 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "partition_size": P, "max_num_partitions": NP,
-                   "decode_kernel": {1: "dot", 2: "mfma"}.get(kernel_ran, str(kernel_ran))},
+                   "decode_kernel": KERNEL_NAMES.get(kernel_ran, str(kernel_ran))},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

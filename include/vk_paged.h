@@ -84,7 +84,10 @@ enum {
 enum {
     VK_KERNEL_AUTO = 0,
     VK_KERNEL_DOT = 1,      /* VALU: lane-sliced fp16 dot2 products, DPP reductions */
-    VK_KERNEL_MFMA = 2      /* matrix cores for the QK and PV contractions */
+    VK_KERNEL_MFMA = 2,     /* matrix cores for QK and PV; waves per workgroup chosen */
+    VK_KERNEL_MFMA_W1 = 3,  /* matrix cores, 1 wave64 per workgroup (A/B tuning) */
+    VK_KERNEL_MFMA_W2 = 4,  /* matrix cores, 2 wave64s per workgroup (A/B tuning) */
+    VK_KERNEL_MFMA_W4 = 5   /* matrix cores, 4 wave64s per workgroup (A/B tuning) */
 };
 
 typedef struct vk_plan {
@@ -93,7 +96,7 @@ typedef struct vk_plan {
     int64_t  work_full_parts;    /* W(P) = Hq * sum_s floor(L_s / P) at the chosen P */
     int64_t  budget;             /* budget_per_cu * cu_count */
     int32_t  cu_count;           /* compute units the budget was sized for */
-    int32_t  kernel;             /* decode: VK_KERNEL_* that ran; planner: 0 */
+    int32_t  kernel;             /* decode: VK_KERNEL_DOT or VK_KERNEL_MFMA_W* that ran; planner: 0 */
     uint64_t scratch_bytes;      /* S * Hq * NP * (D + 2) * 4 */
     int32_t  grid[3];            /* decode: launch grid (partitions, Hkv, S) */
     int32_t  block;              /* decode: threads per workgroup */

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvkpaged.so")
 ARCH = "gfx950"
 
-SOURCES = ["vk_host.cpp", "decode_dot.hip", "reduce.hip"]
+SOURCES = ["vk_host.cpp", "decode_dot.hip", "decode_mfma.hip", "reduce.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -1,0 +1,439 @@
+// Paged GQA decode attention on the gfx950 matrix cores (VK_KERNEL_MFMA).
+//
+// Why matrix cores: with G query heads per KV head the path does G flops per
+// KV byte (4, 6 or 8).  With packed fp32 off, the VALU ridge is ~9.8 flop/B,
+// so a VALU kernel spends most of its issue slots on arithmetic.  Both
+// contractions of a KV-group step are small dense products:
+//   S[t, h]  = sum_d K[t, d] Q[h, d]      (16 tokens x 16 heads x D)
+//   O^T[d,h] += sum_t V^T[d, t] P^T[t, h]   (16 dims  x 16 heads x T tokens)
+// and one v_mfma_f32_16x16x32_f16 (16x16x16 for T = 16) does each block,
+// leaving the VALU only the softmax.  The G <= 8 heads fill half (or less) of
+// the 16 columns; the matrix cores are far from busy either way.
+//
+// Workgroup = W wave64s per (partition, KV head, sequence) (vllm-metal
+// kernels page, cf-1.com/news/5525226, section "Metal 并行模型": all query
+// heads of the group share one pass over the group's K/V pages).  Each wave
+// takes every W-th step of T tokens (T = 32 for D = 128; T = 16 for D = 256,
+// which keeps a lane under 256 registers).  Per step and lane l (i = l % 16,
+// c = l / 16), shown for T = 32:
+//  * K: two 16-token tiles; lane l loads token i (and 16 + i), dims
+//    [32 kk + 8 c, +8) for kk < D/32: 16-byte loads that are exactly the MFMA
+//    A operand.  The B operand is Q^T: head i, the same dims (zero for
+//    i >= G), held in registers for the whole partition.
+//  * The QK output tile gives lane l head i and tokens 4c + r (r < 4); the two
+//    tiles give 8 tokens per lane.  That is exactly the B operand (P^T) of the
+//    PV product when k-slot j of lane group c is token (j < 4 ? 4c + j :
+//    16 + 4c + j - 4), so P needs no data movement, only fp16 packing.
+//  * V: lane l loads its 8 tokens' dims [128 dh + 8 i, +8) (whole 256-byte
+//    half-rows per 16 lanes) and transposes the 8x8 fp16 block in registers
+//    with v_perm_b32 into the PV A operands: tile (dh, e) holds
+//    d = 128 dh + 8 i + e for row i.
+//  * Online softmax in log2 space (section "GQA 解码内核的四个提速技巧",
+//    item 1): per head, max over the 32 tokens (in-lane, then across the 4
+//    lane groups), one rescale of the accumulators per step, exp2 of
+//    x - max, per-lane partial exp-sums (summed once at the end).
+// Page ids: each wave holds up to 64 page ids of the current chunk in one
+// register (lane k = page k, one coalesced load) and reads the step's 1-4 ids
+// with readlane, so no dependent table load precedes each K/V load (item 2).
+// Tokens past the end are masked by select (zeroed K/V registers, score -inf).
+#include "vk_constants.h"
+#include "vk_kernels.h"
+
+namespace vk {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A product rounded to fp32 and never fused into a later add, so the running
+// max and the exponent argument see the same score.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
+__device__ __forceinline__ floatx4 mfma32(const uint4& a, const uint4& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16(const uint2& a, const uint2& b, const floatx4& c) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                  __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t word(const uint4& v) {
+    return W == 0 ? v.x : W == 1 ? v.y : W == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// 8x8 fp16 transpose step: dims e of tokens 0..7 (lane group's k-slots) out of
+// 8 rows of 8 dims each.
+template <int E>
+__device__ __forceinline__ uint4 vt_operand(const uint4 (&v)[8]) {
+    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+    uint4 a;
+    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
+    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
+    a.z = __builtin_amdgcn_perm(word<E / 2>(v[5]), word<E / 2>(v[4]), sel);
+    a.w = __builtin_amdgcn_perm(word<E / 2>(v[7]), word<E / 2>(v[6]), sel);
+    return a;
+}
+
+// 4x8 fp16 transpose step for the 16x16x16 product: dim e of the lane
+// group's 4 tokens.
+template <int E>
+__device__ __forceinline__ uint2 vt_operand4(const uint4 (&v)[4]) {
+    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+    uint2 a;
+    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
+    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
+    return a;
+}
+
+template <int D, int G, int BS, int W, int T>
+struct MfmaKernel {
+    static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
+    static constexpr int NT = T / 16;     // 16-token QK tiles per step
+    static constexpr int NJ = T / 4;      // tokens per lane in the PV product
+    static constexpr int NKC = D / 32;    // QK k-chunks of 32 dims
+    static constexpr int NDH = D / 128;   // 128-dim halves of a V row
+    static constexpr int NPT = D / 16;    // PV output tiles (16 dims each)
+    static constexpr int CHP = 64;        // page ids per chunk (one per lane)
+    static constexpr int CH = CHP * BS;   // tokens per chunk
+    static_assert(CH % (W * T) == 0, "chunk must hold whole rounds of steps");
+
+    struct State {
+        floatx4 acc[NPT];
+        float m, l;
+    };
+
+    // Page id of token `tok` (0..31 within the step) from the step's ids.
+    static __device__ __forceinline__ int page_of(int tok, const int (&pid)[T / BS < 1 ? 1 : T / BS]) {
+        if constexpr (BS >= T) {
+            return pid[0];
+        } else {
+            int p = pid[0];
+#pragma unroll
+            for (int k = 1; k < T / BS; ++k) p = (tok >= k * BS) ? pid[k] : p;
+            return p;
+        }
+    }
+
+    template <bool FULL>
+    static __device__ __forceinline__ void step(const DecodeArgs& a, State& st,
+                                                const uint4 (&qb)[NKC], int pg, int g, int off,
+                                                int remain, int i, int c) {
+        constexpr int NPG = T / BS < 1 ? 1 : T / BS;
+        int pid[NPG];
+        const int k0 = off / BS;
+#pragma unroll
+        for (int k = 0; k < NPG; ++k) pid[k] = __builtin_amdgcn_readlane(pg, k0 + k);
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const uint16_t* kbase = a.k + (int64_t)g * BS * D;
+        const uint16_t* vbase = a.v + (int64_t)g * BS * D;
+        const int off_slot = off % BS;   // step start within its page (BS > T only)
+
+        // ---- K: NT tiles of 16 tokens, lane row i ----
+        uint4 kr[NT][NKC];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int tok = 16 * tt + i;
+            const bool ok = FULL || tok < remain;
+            const int page = page_of(tok, pid);
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                kbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk)
+                kr[tt][kk] = ok ? kp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
+        // ---- V: this lane's NJ tokens, dims [128 dh + 8 i, +8) ----
+        uint4 vr[NDH][NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int tok = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
+            const bool ok = FULL || tok < remain;
+            const int page = page_of(tok, pid);
+            const uint4* vp = reinterpret_cast<const uint4*>(
+                vbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) vr[dh][j] = ok ? vp[16 * dh + i] : make_uint4(0, 0, 0, 0);
+        }
+
+        // ---- S = K Q^T on the matrix cores ----
+        floatx4 sc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            sc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) sc[tt] = mfma32(kr[tt][kk], qb[kk], sc[tt]);
+        }
+
+        // ---- online softmax (log2 units) for head i, tokens of this lane ----
+        float x[NJ];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = mul_rounded(sc[tt][r], a.scale_log2e);
+                if (!FULL && (16 * tt + 4 * c + r) >= remain) v = -INFINITY;
+                x[4 * tt + r] = v;
+            }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2_fast(st.m - mref);
+        float p[NJ];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            p[j] = exp2_fast(x[j] - mref);
+            ps += p[j];
+        }
+        st.l = st.l * alpha + ps;
+        st.m = mnew;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
+
+        // ---- O^T += V^T P^T on the matrix cores ----
+        if constexpr (T == 32) {
+            uint4 pb;
+            pb.x = pack_half2(p[0], p[1]);
+            pb.y = pack_half2(p[2], p[3]);
+            pb.z = pack_half2(p[4], p[5]);
+            pb.w = pack_half2(p[6], p[7]);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) {
+                st.acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
+                st.acc[dh * 8 + 1] = mfma32(vt_operand<1>(vr[dh]), pb, st.acc[dh * 8 + 1]);
+                st.acc[dh * 8 + 2] = mfma32(vt_operand<2>(vr[dh]), pb, st.acc[dh * 8 + 2]);
+                st.acc[dh * 8 + 3] = mfma32(vt_operand<3>(vr[dh]), pb, st.acc[dh * 8 + 3]);
+                st.acc[dh * 8 + 4] = mfma32(vt_operand<4>(vr[dh]), pb, st.acc[dh * 8 + 4]);
+                st.acc[dh * 8 + 5] = mfma32(vt_operand<5>(vr[dh]), pb, st.acc[dh * 8 + 5]);
+                st.acc[dh * 8 + 6] = mfma32(vt_operand<6>(vr[dh]), pb, st.acc[dh * 8 + 6]);
+                st.acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
+            }
+        } else {
+            uint2 pb;
+            pb.x = pack_half2(p[0], p[1]);
+            pb.y = pack_half2(p[2], p[3]);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) {
+                st.acc[dh * 8 + 0] = mfma16(vt_operand4<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
+                st.acc[dh * 8 + 1] = mfma16(vt_operand4<1>(vr[dh]), pb, st.acc[dh * 8 + 1]);
+                st.acc[dh * 8 + 2] = mfma16(vt_operand4<2>(vr[dh]), pb, st.acc[dh * 8 + 2]);
+                st.acc[dh * 8 + 3] = mfma16(vt_operand4<3>(vr[dh]), pb, st.acc[dh * 8 + 3]);
+                st.acc[dh * 8 + 4] = mfma16(vt_operand4<4>(vr[dh]), pb, st.acc[dh * 8 + 4]);
+                st.acc[dh * 8 + 5] = mfma16(vt_operand4<5>(vr[dh]), pb, st.acc[dh * 8 + 5]);
+                st.acc[dh * 8 + 6] = mfma16(vt_operand4<6>(vr[dh]), pb, st.acc[dh * 8 + 6]);
+                st.acc[dh * 8 + 7] = mfma16(vt_operand4<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
+            }
+        }
+    }
+
+    static __device__ void run(const DecodeArgs& a) {
+        __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
+        __shared__ float s_m[W][G];
+        __shared__ float s_l[W][G];
+        __shared__ int s_bad[W];
+
+        const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int i = lane & 15, c = lane >> 4;
+        const int Hq = a.num_q_heads;
+        const int P = a.partition_size, NP = a.max_num_partitions;
+
+        int L = a.seq_lens[s];
+        bool poison = false;
+        const int cap = a.max_blocks_per_seq * BS;
+        if (L > cap) {
+            L = cap;
+            poison = true;
+        }
+        int t_begin = 0, t_end = L;
+        if (P > 0) {
+            t_begin = part * P;
+            t_end = min(L, t_begin + P);
+            if (part == NP - 1 && L > t_begin + P) poison = true;  // beyond the grid
+        }
+        if (t_end <= t_begin) {
+            if (P == 0) {  // empty sequence, unsplit: zeros
+                float* o = a.out + ((int64_t)s * Hq + g * G) * D;
+                for (int k = tid; k < G * D; k += 64 * W) o[k] = 0.f;
+            }
+            return;  // split: partitions past the end write nothing
+        }
+
+        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
+        uint4 qb[NKC];
+        {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
+
+        State st;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.f;
+        bool bad = false;
+
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+            const int c1 = min(t_end, c0 + CH);
+            const int np = (c1 - c0 + BS - 1) / BS;
+            int pg = 0;
+            if (lane < np) {
+                pg = bt[c0 / BS + lane];
+                if (pg < 0 || (int64_t)pg >= a.num_blocks) {
+                    pg = 0;
+                    bad = true;
+                }
+            }
+            int t0 = c0 + wave * T;
+            for (; t0 + T <= c1; t0 += W * T) step<true>(a, st, qb, pg, g, t0 - c0, T, i, c);
+            if (t0 < c1) step<false>(a, st, qb, pg, g, t0 - c0, c1 - t0, i, c);
+        }
+
+        // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
+        float lsum = st.l + __shfl_xor(st.l, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const bool wave_bad = __ballot(bad) != 0;
+
+        const int64_t row0 = (int64_t)s * Hq + g * G;   // first query head of the group
+        if constexpr (W == 1) {
+            const bool out_bad = poison || wave_bad;
+            if (i < G) {
+                const int64_t r = row0 + i;
+                float* dst;
+                if (P == 0) {
+                    dst = a.out + r * D;
+                } else {
+                    const int64_t pr = r * NP + part;
+                    dst = a.tmp_out + pr * D;
+                    if (c == 0) {
+                        a.max_logits[pr] = st.m;
+                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                    }
+                }
+#pragma unroll
+                for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int d = 128 * dh + 8 * (4 * c + rr) + e;
+                            dst[d] = out_bad ? __builtin_nanf("") : st.acc[dh * 8 + e][rr] / lsum;
+                        }
+            }
+        } else {
+            if (i < G) {
+#pragma unroll
+                for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            s_acc[wave][i][128 * dh + 8 * (4 * c + rr) + e] = st.acc[dh * 8 + e][rr];
+                if (c == 0) {
+                    s_m[wave][i] = st.m;
+                    s_l[wave][i] = lsum;
+                }
+            }
+            if (lane == 0) s_bad[wave] = wave_bad;
+            __syncthreads();
+            bool out_bad = poison;
+#pragma unroll
+            for (int w = 0; w < W; ++w) out_bad = out_bad || s_bad[w];
+            for (int idx = tid; idx < G * D; idx += 64 * W) {
+                const int h = idx / D, d = idx % D;
+                float M = s_m[0][h];
+#pragma unroll
+                for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+                float num = 0.f, den = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const float mw = s_m[w][h];
+                    const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+                    num += sc * s_acc[w][h][d];
+                    den += sc * s_l[w][h];
+                }
+                const float o = out_bad ? __builtin_nanf("") : num / den;
+                const int64_t r = row0 + h;
+                if (P == 0) {
+                    a.out[r * D + d] = o;
+                } else {
+                    const int64_t pr = r * NP + part;
+                    a.tmp_out[pr * D + d] = o;
+                    if (d == 0) {
+                        a.max_logits[pr] = M;
+                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : den;
+                    }
+                }
+            }
+        }
+    }
+};
+
+// 16-token steps for D = 256 keep a lane under 256 registers (two waves per
+// SIMD); D = 128 fits 32-token steps at that occupancy.
+// At least two resident waves per SIMD: caps a lane at 256 registers.
+template <int D, int G, int BS, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel(DecodeArgs a) {
+    MfmaKernel<D, G, BS, W, (D == 256 ? 16 : 32)>::run(a);
+}
+
+template <int D, int G, int W>
+hipError_t launch_bs(const DecodeArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    *ok = true;
+    const dim3 block(64 * W);
+    switch (bs) {
+        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W>), grid, block, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W>), grid, block, 0, st, a); break;
+        default: *ok = false; return hipSuccess;
+    }
+    return hipGetLastError();
+}
+
+template <int W>
+hipError_t launch_w(const DecodeArgs& a, int group, int head_dim, int bs, dim3 grid,
+                    hipStream_t st, bool* ok) {
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4, W>(a, bs, grid, st, ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6, W>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8, W>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8, W>(a, bs, grid, st, ok);
+    *ok = false;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
+                              int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
+                              int* block) {
+    *block = 64 * waves;
+    switch (waves) {
+        case 1: return launch_w<1>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 2: return launch_w<2>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 4: return launch_w<4>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        default: *geometry_ok = false; return hipSuccess;
+    }
+}
+
+}  // namespace vk

@@ -9,8 +9,9 @@
 //   w_i = l_i * 2^(m_i - M),  W = sum w_i  (block sum)
 //   out = sum_i w_i o_i / W
 // For the weighted sum, thread t handles float4 column t % 16 of the 64-dim
-// chunk for partitions i = t / 16 (mod 16), four partitions per loop trip so
-// several loads are in flight, then the 16 partition groups are summed in LDS.
+// chunk for partitions i = t / 16 (mod 16).  Its first 16 partitions' values
+// are loaded before the statistics are read, so every load of a workgroup is
+// in flight at once; the 16 partition groups are then summed in LDS.
 #include "vk_kernels.h"
 
 namespace vk {
@@ -19,6 +20,7 @@ namespace {
 constexpr int kChunk = 64;                 // output dims per workgroup
 constexpr int kLanes = kChunk / 4;         // float4 columns
 constexpr int kGroups = 256 / kLanes;      // partition groups
+constexpr int kPre = 16;                   // partitions per thread loaded up front
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -65,6 +67,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
         return;
     }
 
+    // Issue every load first: the first kPre partitions' float4 of this
+    // thread (they do not depend on the weights), then the statistics.
+    const int c = tid % kLanes, grp = tid / kLanes;
+    float4 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int i = grp + k * kGroups;
+        pre[k] = i < n ? to[(int64_t)i * kRow4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float mx = -INFINITY;
     for (int i = tid; i < n; i += 256) mx = fmaxf(mx, ml[i]);
     mx = wave_max(mx);
@@ -80,9 +91,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
     __syncthreads();
     const float W = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
 
-    const int c = tid % kLanes, grp = tid / kLanes;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int i = grp;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int i = grp + k * kGroups;
+        if (i < n) fma4(acc, es[i] * __builtin_amdgcn_exp2f(ml[i] - M), pre[k]);
+    }
+    int i = grp + kPre * kGroups;
     for (; i + 3 * kGroups < n; i += 4 * kGroups) {
         const float4 o0 = to[(int64_t)i * kRow4 + c];
         const float4 o1 = to[(int64_t)(i + kGroups) * kRow4 + c];

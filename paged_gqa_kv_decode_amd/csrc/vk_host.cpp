@@ -79,7 +79,7 @@ vk_status vk_last_plan(vk_plan* out) {
 }
 
 int32_t vk_select_decode_kernel(int32_t kernel) {
-    if (kernel != VK_KERNEL_AUTO && kernel != VK_KERNEL_DOT) return -1;
+    if (kernel < VK_KERNEL_AUTO || kernel > VK_KERNEL_MFMA_W4) return -1;
     const int32_t prev = t_kernel_choice;
     t_kernel_choice = kernel;
     return prev;
@@ -206,8 +206,19 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool ok = false;
     int block = 0;
-    const int32_t kernel = VK_KERNEL_DOT;
-    hipError_t e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
+    int32_t kernel = t_kernel_choice;
+    if (kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA) {
+        // One wave per workgroup when the sequence is already split into
+        // partitions; four waves share a whole sequence when unsplit.
+        kernel = partition_size == 0 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W1;
+    }
+    hipError_t e;
+    if (kernel == VK_KERNEL_DOT) {
+        e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
+    } else {
+        const int waves = kernel == VK_KERNEL_MFMA_W1 ? 1 : kernel == VK_KERNEL_MFMA_W2 ? 2 : 4;
+        e = vk::launch_decode_mfma(a, group, head_dim, block_size, waves, grid, st, &ok, &block);
+    }
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);
 

@@ -41,6 +41,10 @@ struct ReduceArgs {
 // false when no specialisation exists for the shape (host code checks first).
 hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,
                              dim3 grid, hipStream_t stream, bool* geometry_ok, int* block);
+// waves: 1, 2 or 4 wave64s per workgroup.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
+                              int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
+                              int* block);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok);
 

@@ -20,7 +20,7 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-@functools.lru_cache(maxsize=4)
+@functools.lru_cache(maxsize=8)
 def named(name: str, canaries: bool = False, pad_value: int = -1):
     return make_workload(name, canaries=canaries, pad_value=pad_value)
 

@@ -15,12 +15,22 @@ from paged_gqa_kv_decode_amd.workloads import make_custom, make_onehot_probe
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = [vb.KERNEL_DOT]
+KERNELS = [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4]
 
 NAMED = [("tiny_1x64", 0), ("batch8_2k", 512), ("long32_16k", 256), ("long32_16k", 512),
          ("mixed64_32k", 512), ("long4_128k", -1)]
 
 _refs = {}
+_probes = {}
+
+
+def _probe(name, seed):
+    key = (name, seed)
+    if key not in _probes:
+        if len(_probes) >= 2:
+            _probes.pop(next(iter(_probes)))
+        _probes[key] = make_onehot_probe(named(name, canaries=True), seed=seed)
+    return _probes[key]
 
 
 def oracle_ref(orc, name):
@@ -43,11 +53,12 @@ def test_named_workload_parity(orc, name, P, kernel):
     assert_parity(gpu, ref, f"{name} P={plan.partition_size}")
 
 
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512), ("long32_16k", 256)])
-def test_partials_match_oracle(orc, name, P):
-    say(f"[partials] {name} P={P}")
+def test_partials_match_oracle(orc, name, P, kernel):
+    say(f"[partials] {name} P={P} kernel={kernel}")
     wl = named(name)
-    _, plan, _, (m, l, o) = run_hip(wl, P, keep_partials=True)
+    _, plan, _, (m, l, o) = run_hip(wl, P, keep_partials=True, kernel=kernel)
     NP = plan.max_num_partitions
     om, ol, oo = orc.partials(wl, P, NP)
     for s, L in enumerate(wl.seq_lens):
@@ -66,13 +77,13 @@ def test_partials_match_oracle(orc, name, P):
 @pytest.mark.parametrize("name,P", [("tiny_1x64", 0), ("batch8_2k", 512), ("batch8_2k", 0),
                                     ("long32_16k", 256), ("mixed64_32k", 512),
                                     ("long4_128k", 512), ("long4_128k", 0)])
-def test_onehot_probe_bit_exact(name, P):
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+def test_onehot_probe_bit_exact(name, P, kernel):
     """Page-table indexing: every output decodes to exactly the (block, slot,
     KV head) the page table names for the target token."""
-    say(f"[probe] {name} P={P}")
-    base = named(name, canaries=True)
-    wl, targets = make_onehot_probe(base, seed=7 + P)
-    gpu, _, _, _ = run_hip(wl, P)
+    say(f"[probe] {name} P={P} kernel={kernel}")
+    wl, targets = _probe(name, 7 + P)
+    gpu, _, _, _ = run_hip(wl, P, kernel=kernel)
     bs, G = wl.block_size, wl.group
     for s in range(wl.num_seqs):
         t = targets[s]
@@ -83,9 +94,10 @@ def test_onehot_probe_bit_exact(name, P):
         assert np.all(gpu[s, :, 4:] == 0.0)
 
 
-def test_single_token_rows_bit_exact():
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+def test_single_token_rows_bit_exact(kernel):
     wl = named("mixed64_32k")
-    gpu, _, _, _ = run_hip(wl, 512)
+    gpu, _, _, _ = run_hip(wl, 512, kernel=kernel)
     ones = np.nonzero(wl.seq_lens == 1)[0]
     assert len(ones) == 16
     for s in ones:
@@ -95,10 +107,11 @@ def test_single_token_rows_bit_exact():
             assert np.array_equal(gpu[s, h], v0)
 
 
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512)])
-def test_page_permutation_bit_identical(name, P):
+def test_page_permutation_bit_identical(name, P, kernel):
     wl = named(name)
-    base, _, _, _ = run_hip(wl, P)
+    base, _, _, _ = run_hip(wl, P, kernel=kernel)
     rng = np.random.default_rng(99)
     perm = rng.permutation(wl.num_blocks)
     import copy
@@ -110,48 +123,52 @@ def test_page_permutation_bit_identical(name, P):
     bt = wl.block_tables.copy()
     bt[bt >= 0] = perm[bt[bt >= 0]]
     w2.block_tables = bt
-    out, _, _, _ = run_hip(w2, P)
+    out, _, _, _ = run_hip(w2, P, kernel=kernel)
     assert np.array_equal(out, base)
 
 
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
 @pytest.mark.parametrize("name,Pa,Pb", [("batch8_2k", 0, 512), ("long32_16k", 256, 512),
                                         ("batch8_2k", 256, 512)])
-def test_split_vs_unsplit(name, Pa, Pb):
+def test_split_vs_unsplit(name, Pa, Pb, kernel):
     wl = named(name)
-    a, _, _, _ = run_hip(wl, Pa)
-    b, _, _, _ = run_hip(wl, Pb)
+    a, _, _, _ = run_hip(wl, Pa, kernel=kernel)
+    b, _, _, _ = run_hip(wl, Pb, kernel=kernel)
     assert_parity(a, b, f"{name} P={Pa} vs P={Pb}")
 
 
-def test_v_scaled_by_two_is_exact():
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+def test_v_scaled_by_two_is_exact(kernel):
     import copy
     wl = named("batch8_2k")
-    base, _, _, _ = run_hip(wl, 512)
+    base, _, _, _ = run_hip(wl, 512, kernel=kernel)
     w2 = copy.copy(wl)
     w2.v_cache = (wl.v_cache.astype(np.float32) * 2).astype(np.float16)
-    out, _, _, _ = run_hip(w2, 512)
+    out, _, _, _ = run_hip(w2, 512, kernel=kernel)
     assert np.array_equal(out, 2 * base)
 
 
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512)])
-def test_repeat_runs_bit_identical(name, P):
+def test_repeat_runs_bit_identical(name, P, kernel):
     wl = named(name)
     dev = to_device(wl)
-    a, _, _, _ = run_hip(wl, P, dev=dev)
-    b, _, _, _ = run_hip(wl, P, dev=dev)
+    a, _, _, _ = run_hip(wl, P, dev=dev, kernel=kernel)
+    b, _, _, _ = run_hip(wl, P, dev=dev, kernel=kernel)
     assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("tiny_1x64", 0), ("long4_128k", 512),
                                     ("mixed64_32k", 512)])
 @pytest.mark.parametrize("pad", ["minus1", "block"])
-def test_canaries_never_read(name, P, pad):
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+def test_canaries_never_read(name, P, pad, kernel):
     """NaN in unused blocks and in the slots past L; padding entries of the
     page table -1 or the id of a block that is unused (NaN) where one exists.
     The output must be bit-identical to the run without canaries."""
     say(f"[canary] {name} P={P} pad={pad}")
     plain = named(name)
-    base, _, _, _ = run_hip(plain, P)
+    base, _, _, _ = run_hip(plain, P, kernel=kernel)
     pad_value = -1
     if pad == "block":
         used = np.zeros(plain.num_blocks, bool)
@@ -160,7 +177,7 @@ def test_canaries_never_read(name, P, pad):
         unused = np.nonzero(~used)[0]
         pad_value = int(unused[0]) if len(unused) else 0
     wl = named(name, canaries=True, pad_value=pad_value)
-    out, _, _, _ = run_hip(wl, P, prefill_nan=True)
+    out, _, _, _ = run_hip(wl, P, prefill_nan=True, kernel=kernel)
     assert np.all(np.isfinite(out)), "a canary leaked into the output"
     assert np.array_equal(out, base)
 
@@ -222,7 +239,8 @@ def test_all_specialisations_ragged(orc, geom, bs, kernel):
         assert_parity(gpu, ref, f"{geom} bs{bs} P{P}")
 
 
-def test_device_side_guards():
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
+def test_device_side_guards(kernel):
     """Values the host cannot validate: a length <= 0 gives zeros; a page id
     outside the pool or a length beyond the page table gives NaN for that
     sequence only, without reading out of bounds."""
@@ -234,6 +252,7 @@ def test_device_side_guards():
     bt_h = wl.block_tables.copy()
     bt_h[2, 1] = wl.num_blocks + 5          # out of the pool
     bt_dev = torch.from_numpy(bt_h).cuda()
+    prev = vb.select_decode_kernel(kernel)
     for P in (0, 512):
         out = torch.full((4, 16, 128), 7.0, device="cuda")
         if P == 0:
@@ -251,6 +270,7 @@ def test_device_side_guards():
         assert np.all(o[1] == 0.0), f"P={P}: empty sequence must be zeros"
         assert np.all(np.isnan(o[2])), f"P={P}: bad page id must poison its sequence"
         assert np.all(np.isnan(o[3])), f"P={P}: length beyond the page table must poison"
+    vb.select_decode_kernel(prev)
 
 
 def test_errors_on_real_tensors():
