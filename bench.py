@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20          # MI355X Infinity Cache
 DESCRIPTIONS = {
     "tiny_1x64": "1 seq x 64 tokens, (32q, 8kv, 128), block 16, unsplit",
     "batch8_2k": "8 seqs, L uniform in [1, 2048], (32q, 8kv, 128), block 16, P=512",
@@ -79,6 +80,80 @@ def load_traffic(workload: str, partition: int, kernel: int):
         return None
 
 
+def _bench_lib():
+    import ctypes
+    path = os.path.join(ROOT, "paged_gqa_kv_decode_amd", "libvkbench.so")
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.vkb_stream_read.argtypes = [vp, i64, vp, i32, vp]
+    L.vkb_page_read.argtypes = [vp, i64, vp, i64, i32, i64, vp, vp]
+    L.vkb_fill.argtypes = [vp, i64, ctypes.c_uint32, vp]
+    return L
+
+
+def ceilings(wl, dev, P, reps=10):
+    """Read-bandwidth ceilings of this machine for the workload's KV pools:
+    a streaming read of both pools, the exact page list of the decode
+    (partition-major, P/bs pages per workgroup), and the same pages sorted."""
+    import numpy as np
+    import torch
+    L = _bench_lib()
+    q, k, v, bt, sl = dev
+    st = torch.cuda.current_stream()
+    h = st.cuda_stream
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    blocks = 256 * 16
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    bs, D, Hkv = wl.block_size, wl.head_dim, wl.num_kv_heads
+    page_bytes = bs * D * 2
+    pool_pages = wl.num_blocks * Hkv
+    ppg = max(1, (P if P > 0 else 512) // bs)
+    ids = []
+    for s_ in range(wl.num_seqs):
+        n = -(-int(wl.seq_lens[s_]) // bs)
+        for g in range(Hkv):
+            ids.append(wl.block_tables[s_, :n].astype(np.int64) * Hkv + g)
+    ids = np.concatenate(ids).astype(np.int32)
+    ids_dev = torch.from_numpy(ids).cuda()
+    ids_sorted = torch.from_numpy(np.sort(ids)).cuda()
+    groups = -(-len(ids) // ppg)
+    psink = torch.empty(groups * 256, dtype=torch.int32, device="cuda")
+
+    L.vkb_fill(flush.data_ptr(), flush.numel(), 0, h)
+    fsink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            L.vkb_stream_read(flush.data_ptr(), flush.numel(), fsink.data_ptr(), 4096, h)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    pool_bytes = k.numel() * 2
+    t_stream = timed(lambda: (L.vkb_stream_read(k.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h),
+                              L.vkb_stream_read(v.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h)))
+    page_total = 2 * len(ids) * page_bytes
+
+    def pages(idt):
+        L.vkb_page_read(k.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg, page_bytes,
+                        psink.data_ptr(), h)
+        L.vkb_page_read(v.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg, page_bytes,
+                        psink.data_ptr(), h)
+
+    t_pages = timed(lambda: pages(ids_dev))
+    t_sorted = timed(lambda: pages(ids_sorted))
+    return {"stream_read_GBps": round(2 * pool_bytes / t_stream / 1e9, 1),
+            "page_read_GBps": round(page_total / t_pages / 1e9, 1),
+            "page_read_sorted_GBps": round(page_total / t_sorted / 1e9, 1),
+            "page_bytes": page_bytes, "pages_per_group": ppg,
+            "flushed": "512 MiB read before each timed run"}
+
+
 def cpu_baseline(wl, sample_seqs: int):
     """Time the float64 oracle on the first `sample_seqs` sequences."""
     import numpy as np
@@ -110,6 +185,12 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--max-copies", type=int, default=256,
+                    help="cap on the rotated K/V pool copies")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also measure the box's read-bandwidth ceilings on the KV pools")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time the decode with a 512 MiB cache flush before each run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, --steps times (the "
                          "known-size reference for the HBM byte counters)")
@@ -152,8 +233,14 @@ def main():
 
     dev = vb.device_inputs(wl)
     q, k, v, bt, sl = dev
-    torch.cuda.synchronize()
     kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim)
+    # Successive steps rotate over identical copies of the K/V pools so that at
+    # least 4x the 256 MB Infinity Cache is read between two reads of the same
+    # page: every step streams its KV from HBM, as a layer's decode does when
+    # the other layers' caches are read in between.
+    ncopies = max(2, min(args.max_copies, -(-(4 * MALL_BYTES) // kv_bytes)))
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(ncopies - 1)]
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
 
@@ -162,7 +249,11 @@ def main():
     step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out)
     P, NP = step0.plan.partition_size, step0.plan.max_num_partitions
 
+    counter = [0]
+
     def one_step(ev=None):
+        k, v = pools[counter[0] % ncopies]
+        counter[0] += 1
         plan = vb.plan_partitions(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                   wl.block_size, wl.max_blocks_per_seq, P_req, 0)
         assert plan.partition_size == P and plan.max_num_partitions == NP
@@ -232,8 +323,25 @@ def main():
                       "decode_p95": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
                       "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)},
         "kv_read_bytes": kv_bytes,
+        "kv_pool_copies": ncopies,
+        "bytes_read_between_reuse": (ncopies - 1) * kv_bytes,
         "input_gen_s": round(gen_s, 1),
     }
+    if args.ceiling:
+        result["ceiling"] = ceilings(wl, dev, P)
+    if args.flush:
+        L = _bench_lib()
+        flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+        fsink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+        fl = []
+        for _ in range(20):
+            L.vkb_stream_read(flush.data_ptr(), flush.numel(), fsink.data_ptr(), 4096,
+                              stream.cuda_stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            one_step(ev)
+            torch.cuda.synchronize()
+            fl.append(ev[0].elapsed_time(ev[1]))
+        result["kernel_us"]["decode_median_flushed"] = round(float(np.median(fl)) * 1e3, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, max(1, min(args.cpu_sample_seqs, wl.num_seqs)))
     else:

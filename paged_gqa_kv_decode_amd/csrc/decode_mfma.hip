@@ -39,6 +39,23 @@
 #include "vk_constants.h"
 #include "vk_kernels.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef VK_MFMA_T128
+#define VK_MFMA_T128 16          // tokens per wave step, D = 128
+#endif
+#ifndef VK_MFMA_T256
+#define VK_MFMA_T256 16          // tokens per wave step, D = 256
+#endif
+#ifndef VK_MFMA_WAVES_PER_EU
+#define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
+#endif
+#ifndef VK_MFMA_PIPELINE
+#define VK_MFMA_PIPELINE 0       // 1: two register buffers, loads one step ahead
+#endif
+#ifndef VK_MFMA_Q_LDS256
+#define VK_MFMA_Q_LDS256 0       // 1: Q^T operand in LDS for D = 256
+#endif
+
 namespace vk {
 namespace {
 
@@ -63,6 +80,15 @@ __device__ __forceinline__ floatx4 mfma16(const uint2& a, const uint2& b, const 
     typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
                                                   __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+// K and V are read exactly once per step: nontemporal (streaming) loads.  On
+// MI355X a plain streaming read tops out near 6.0 TB/s and a nontemporal one
+// near 6.5 TB/s.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int W>
@@ -100,6 +126,19 @@ __device__ __forceinline__ uint2 vt_operand4(const uint4 (&v)[4]) {
     return a;
 }
 
+// The Q^T operand of one lane: in registers, or (to keep a lane under 256
+// registers when D = 256) in the lane's own LDS slots, read back per use.
+template <int NKC>
+struct QRegs {
+    uint4 v[NKC];
+    __device__ __forceinline__ uint4 operator[](int kk) const { return v[kk]; }
+};
+template <int NKC>
+struct QLds {
+    const uint4* p;   // this lane's slot of kk = 0; slots are 64 uint4 apart
+    __device__ __forceinline__ uint4 operator[](int kk) const { return p[kk * 64]; }
+};
+
 template <int D, int G, int BS, int W, int T>
 struct MfmaKernel {
     static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
@@ -129,10 +168,17 @@ struct MfmaKernel {
         }
     }
 
+    // K/V registers of one step.
+    struct Buf {
+        uint4 kr[NT][NKC];
+        uint4 vr[NDH][NJ];
+    };
+
+    // Issue the K/V loads of the step at chunk offset `off` (`remain` valid
+    // tokens when not FULL).
     template <bool FULL>
-    static __device__ __forceinline__ void step(const DecodeArgs& a, State& st,
-                                                const uint4 (&qb)[NKC], int pg, int g, int off,
-                                                int remain, int i, int c) {
+    static __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int pg, int g,
+                                                 int off, int remain, int i, int c) {
         constexpr int NPG = T / BS < 1 ? 1 : T / BS;
         int pid[NPG];
         const int k0 = off / BS;
@@ -144,7 +190,7 @@ struct MfmaKernel {
         const int off_slot = off % BS;   // step start within its page (BS > T only)
 
         // ---- K: NT tiles of 16 tokens, lane row i ----
-        uint4 kr[NT][NKC];
+        auto& kr = b.kr;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int tok = 16 * tt + i;
@@ -154,10 +200,10 @@ struct MfmaKernel {
                 kbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
 #pragma unroll
             for (int kk = 0; kk < NKC; ++kk)
-                kr[tt][kk] = ok ? kp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+                kr[tt][kk] = ok ? load_stream(kp + 4 * kk + c) : make_uint4(0, 0, 0, 0);
         }
         // ---- V: this lane's NJ tokens, dims [128 dh + 8 i, +8) ----
-        uint4 vr[NDH][NJ];
+        auto& vr = b.vr;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int tok = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
@@ -166,9 +212,17 @@ struct MfmaKernel {
             const uint4* vp = reinterpret_cast<const uint4*>(
                 vbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
 #pragma unroll
-            for (int dh = 0; dh < NDH; ++dh) vr[dh][j] = ok ? vp[16 * dh + i] : make_uint4(0, 0, 0, 0);
+            for (int dh = 0; dh < NDH; ++dh) vr[dh][j] = ok ? load_stream(vp + 16 * dh + i) : make_uint4(0, 0, 0, 0);
         }
 
+    }
+
+    // QK, online softmax and PV of one step whose loads `b` were issued.
+    template <bool FULL, class Q>
+    static __device__ __forceinline__ void compute(const DecodeArgs& a, State& st, const Buf& b,
+                                                   const Q& qb, int remain, int c) {
+        const auto& kr = b.kr;
+        const auto& vr = b.vr;
         // ---- S = K Q^T on the matrix cores ----
         floatx4 sc[NT];
 #pragma unroll
@@ -244,7 +298,59 @@ struct MfmaKernel {
         }
     }
 
+    static constexpr bool kQInLds = (D == 256) && VK_MFMA_Q_LDS256;
+
+    template <class Q>
+    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const Q& qb,
+                                                int t_begin, int t_end, int g, int s, int wave,
+                                                int lane, int i, int c, bool& bad) {
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+            const int c1 = min(t_end, c0 + CH);
+            const int np = (c1 - c0 + BS - 1) / BS;
+            int pg = 0;
+            if (lane < np) {
+                pg = bt[c0 / BS + lane];
+                if (pg < 0 || (int64_t)pg >= a.num_blocks) {
+                    pg = 0;
+                    bad = true;
+                }
+            }
+            // Full steps of this wave (optionally software-pipelined over two
+            // register buffers, the next step's loads in flight while the
+            // current step computes), then at most one partial step.
+            const int first = c0 + wave * T;
+            constexpr int stride = W * T;
+            const int nfull = (first + T <= c1) ? (c1 - T - first) / stride + 1 : 0;
+            if (!VK_MFMA_PIPELINE) {
+                for (int k = 0; k < nfull; ++k) {
+                    Buf b0;
+                    issue<true>(a, b0, pg, g, first + k * stride - c0, T, i, c);
+                    compute<true>(a, st, b0, qb, T, c);
+                }
+            } else if (nfull > 0) {
+                Buf b0, b1;
+                issue<true>(a, b0, pg, g, first - c0, T, i, c);
+                int k = 0;
+                for (; k + 2 <= nfull; k += 2) {
+                    issue<true>(a, b1, pg, g, first + (k + 1) * stride - c0, T, i, c);
+                    compute<true>(a, st, b0, qb, T, c);
+                    if (k + 2 < nfull) issue<true>(a, b0, pg, g, first + (k + 2) * stride - c0, T, i, c);
+                    compute<true>(a, st, b1, qb, T, c);
+                }
+                if (k < nfull) compute<true>(a, st, b0, qb, T, c);
+            }
+            const int tl = first + nfull * stride;
+            if (tl < c1) {
+                Buf bl;
+                issue<false>(a, bl, pg, g, tl - c0, c1 - tl, i, c);
+                compute<false>(a, st, bl, qb, c1 - tl, c);
+            }
+        }
+    }
+
     static __device__ void run(const DecodeArgs& a) {
+        __shared__ uint4 s_q[kQInLds ? W : 1][kQInLds ? NKC : 1][64];
         __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
         __shared__ float s_m[W][G];
         __shared__ float s_l[W][G];
@@ -278,11 +384,17 @@ struct MfmaKernel {
         }
 
         // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
-        uint4 qb[NKC];
+        QRegs<NKC> qreg;
         {
             const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
 #pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+            for (int kk = 0; kk < NKC; ++kk) qreg.v[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
+        QLds<NKC> qlds;
+        qlds.p = &s_q[kQInLds ? wave : 0][0][lane];
+        if constexpr (kQInLds) {
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) s_q[wave][kk][lane] = qreg.v[kk];
         }
 
         State st;
@@ -292,22 +404,10 @@ struct MfmaKernel {
         st.l = 0.f;
         bool bad = false;
 
-        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
-            const int c1 = min(t_end, c0 + CH);
-            const int np = (c1 - c0 + BS - 1) / BS;
-            int pg = 0;
-            if (lane < np) {
-                pg = bt[c0 / BS + lane];
-                if (pg < 0 || (int64_t)pg >= a.num_blocks) {
-                    pg = 0;
-                    bad = true;
-                }
-            }
-            int t0 = c0 + wave * T;
-            for (; t0 + T <= c1; t0 += W * T) step<true>(a, st, qb, pg, g, t0 - c0, T, i, c);
-            if (t0 < c1) step<false>(a, st, qb, pg, g, t0 - c0, c1 - t0, i, c);
-        }
+        if constexpr (kQInLds)
+            scan(a, st, qlds, t_begin, t_end, g, s, wave, lane, i, c, bad);
+        else
+            scan(a, st, qreg, t_begin, t_end, g, s, wave, lane, i, c, bad);
 
         // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
         float lsum = st.l + __shfl_xor(st.l, 16);
@@ -389,13 +489,11 @@ struct MfmaKernel {
     }
 };
 
-// 16-token steps for D = 256 keep a lane under 256 registers (two waves per
-// SIMD); D = 128 fits 32-token steps at that occupancy.
 // At least two resident waves per SIMD: caps a lane at 256 registers.
 template <int D, int G, int BS, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(VK_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(DecodeArgs a) {
-    MfmaKernel<D, G, BS, W, (D == 256 ? 16 : 32)>::run(a);
+    MfmaKernel<D, G, BS, W, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128)>::run(a);
 }
 
 template <int D, int G, int W>

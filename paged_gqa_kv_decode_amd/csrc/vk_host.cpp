@@ -208,9 +208,13 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     int block = 0;
     int32_t kernel = t_kernel_choice;
     if (kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA) {
-        // One wave per workgroup when the sequence is already split into
-        // partitions; four waves share a whole sequence when unsplit.
-        kernel = partition_size == 0 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W1;
+        // Waves per workgroup from the grid size (measured on MI355X, 256
+        // CUs, two resident waves per SIMD = 2048 wave slots): small grids
+        // (few sequences or unsplit) spread a workgroup's tokens over 4
+        // waves; a grid that fills the slots about once keeps 1 wave per
+        // workgroup; larger grids balance better with 2.
+        const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+        kernel = wgs <= 1024 ? VK_KERNEL_MFMA_W4 : wgs <= 2048 ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2;
     }
     hipError_t e;
     if (kernel == VK_KERNEL_DOT) {
