@@ -4,11 +4,13 @@
 // merges them into
 //   out = sum_i l_i 2^(m_i - M) o_i / sum_i l_i 2^(m_i - M),  M = max_i m_i).
 //
-// Grid (D / 16, Hq, S), one wave64 per 16 output dims of one (sequence, query
-// head).  Lane l owns float4 column l % 4 and partitions i = l / 4 (mod 16).
+// Grid (D / 32, Hq, S), one wave64 per 32 output dims (one 128-byte line of
+// every partial row, so no line is split between waves on different XCDs)
+// of one (sequence, query head).  Lane l owns float4 column l % 8 and
+// partitions i = l / 8 (mod 8).
 // It folds its partitions into a running (max, exp-sum, weighted sum) in one
 // pass (the same log2-space merge the decode uses between tokens), with the
-// loads of up to 8 partitions issued ahead of the arithmetic; the 16 lane
+// loads of up to 16 partitions issued ahead of the arithmetic; the 8 lane
 // states of a column are then merged with lane shuffles.  No LDS, no
 // barriers: the wave's whole working set is in flight at once.
 #include "vk_kernels.h"
@@ -16,9 +18,10 @@
 namespace vk {
 namespace {
 
-constexpr int kDims = 16;        // output dims per wave
-constexpr int kGroups = 16;      // partition groups (lanes per column)
-constexpr int kBatch = 8;        // partitions per lane loaded ahead
+constexpr int kDims = 32;        // output dims per wave
+constexpr int kCols = kDims / 4; // float4 columns
+constexpr int kGroups = 64 / kCols;  // partition groups (lanes per column)
+constexpr int kBatch = 16;       // partitions per lane loaded ahead
 
 struct Merge {
     float m, l;
@@ -57,13 +60,13 @@ template <int D>
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
     const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int lane = threadIdx.x;
-    const int c = lane & 3, grp = lane >> 2;
+    const int c = lane % kCols, grp = lane / kCols;
     const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
     const int64_t r = (int64_t)s * Hq + h;
     const int L = a.seq_lens[s];
     float4* dst = reinterpret_cast<float4*>(a.out + r * D + chunk * kDims);
     if (L <= 0) {
-        if (lane < 4) dst[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane < kCols) dst[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
     const int n = min((int)(((int64_t)L + P - 1) / P), NP);
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
     const float4* to = reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * kDims);
     constexpr int kRow4 = D / 4;   // float4 stride between partitions
     if (n == 1) {                  // a single partition is already normalised
-        if (lane < 4) dst[lane] = to[lane];
+        if (lane < kCols) dst[lane] = to[lane];
         return;
     }
 
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
             if (m[k] != -INFINITY) fold(st, m[k], l[k], o[k]);
     }
 #pragma unroll
-    for (int off = 4; off < 64; off <<= 1) {
+    for (int off = kCols; off < 64; off <<= 1) {
         Merge t;
         t.m = __shfl_xor(st.m, off);
         t.l = __shfl_xor(st.l, off);
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
         t.acc.w = __shfl_xor(st.acc.w, off);
         fold_state(st, t);
     }
-    if (lane < 4)
+    if (lane < kCols)
         dst[lane] = make_float4(st.acc.x / st.l, st.acc.y / st.l, st.acc.z / st.l, st.acc.w / st.l);
 }
 
