@@ -54,7 +54,8 @@ KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4"}
 
 def sources_sha(kernel: int) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES.get(kernel, []) + ["paged_gqa_kv_decode_amd/csrc/vk_kernels.h"]:
+    for rel in KERNEL_SOURCES.get(kernel, []) + ["paged_gqa_kv_decode_amd/csrc/vk_kernels.h",
+                                                 "paged_gqa_kv_decode_amd/csrc/mfma_ops.h"]:
         p = os.path.join(ROOT, rel)
         if os.path.exists(p):
             h.update(open(p, "rb").read())

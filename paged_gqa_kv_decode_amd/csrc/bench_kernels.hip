@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
 // mode 0: each load instruction of a wave reads 1 KiB contiguous;
 // mode 1: each reads 64 B from each of 16 rows of `row_bytes` (the shape of
 //         the decode kernel's K loads).
-template <int MODE>
+template <int MODE, bool NT = false>
 __global__ __launch_bounds__(256) void page_read_kernel(const uint8_t* __restrict__ pool,
                                                         int64_t pool_pages,
                                                         const int32_t* __restrict__ ids,
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void page_read_kernel(const uint8_t* __restric
         }
         int64_t i = t;
         for (; i + 3 * 256 < n16; i += 4 * 256) {
-            const uint4 a = pg[i], b = pg[i + 256], c = pg[i + 512], d = pg[i + 768];
+            const uint4 a = load16<NT>(pg + i), b = load16<NT>(pg + i + 256),
+                        c = load16<NT>(pg + i + 512), d = load16<NT>(pg + i + 768);
             x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
         }
         for (; i < n16; i += 256) {
@@ -133,6 +134,19 @@ int vkb_page_read(const void* pool, int64_t pool_pages, const int32_t* ids_dev, 
     hipLaunchKernelGGL(page_read_kernel<0>, dim3((unsigned)groups), dim3(256), 0, (hipStream_t)stream,
                        (const uint8_t*)pool, pool_pages, ids_dev, n_pages, ppg, page_bytes,
                        page_bytes, (uint32_t*)sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Mode-0 page read with nontemporal loads.
+int vkb_page_read_nt(const void* pool, int64_t pool_pages, const int32_t* ids_dev, int64_t n_pages,
+                     int ppg, int64_t page_bytes, void* sink, void* stream) {
+    if (!pool || !ids_dev || !sink || n_pages <= 0 || ppg <= 0 || page_bytes <= 0 ||
+        page_bytes % 16 || pool_pages <= 0)
+        return 1;
+    const int64_t groups = (n_pages + ppg - 1) / ppg;
+    hipLaunchKernelGGL((page_read_kernel<0, true>), dim3((unsigned)groups), dim3(256), 0,
+                       (hipStream_t)stream, (const uint8_t*)pool, pool_pages, ids_dev, n_pages, ppg,
+                       page_bytes, page_bytes, (uint32_t*)sink);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -36,6 +36,7 @@
 // register (lane k = page k, one coalesced load) and reads the step's 1-4 ids
 // with readlane, so no dependent table load precedes each K/V load (item 2).
 // Tokens past the end are masked by select (zeroed K/V registers, score -inf).
+#include "mfma_ops.h"
 #include "vk_constants.h"
 #include "vk_kernels.h"
 
@@ -49,95 +50,11 @@
 #ifndef VK_MFMA_WAVES_PER_EU
 #define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
 #endif
-#ifndef VK_MFMA_PIPELINE
-#define VK_MFMA_PIPELINE 0       // 1: two register buffers, loads one step ahead
-#endif
-#ifndef VK_MFMA_Q_LDS256
-#define VK_MFMA_Q_LDS256 0       // 1: Q^T operand in LDS for D = 256
-#endif
 
 namespace vk {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// A product rounded to fp32 and never fused into a later add, so the running
-// max and the exponent argument see the same score.
-__device__ __forceinline__ float mul_rounded(float a, float b) {
-#pragma clang fp contract(off)
-    return a * b;
-}
-
-__device__ __forceinline__ floatx4 mfma32(const uint4& a, const uint4& b, const floatx4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
-                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ floatx4 mfma16(const uint2& a, const uint2& b, const floatx4& c) {
-    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
-                                                  __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
-}
-
-// K and V are read exactly once per step: nontemporal (streaming) loads.  On
-// MI355X a plain streaming read tops out near 6.0 TB/s and a nontemporal one
-// near 6.5 TB/s.
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <int W>
-__device__ __forceinline__ uint32_t word(const uint4& v) {
-    return W == 0 ? v.x : W == 1 ? v.y : W == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
-    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-    half2_t h = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-// 8x8 fp16 transpose step: dims e of tokens 0..7 (lane group's k-slots) out of
-// 8 rows of 8 dims each.
-template <int E>
-__device__ __forceinline__ uint4 vt_operand(const uint4 (&v)[8]) {
-    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-    uint4 a;
-    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
-    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
-    a.z = __builtin_amdgcn_perm(word<E / 2>(v[5]), word<E / 2>(v[4]), sel);
-    a.w = __builtin_amdgcn_perm(word<E / 2>(v[7]), word<E / 2>(v[6]), sel);
-    return a;
-}
-
-// 4x8 fp16 transpose step for the 16x16x16 product: dim e of the lane
-// group's 4 tokens.
-template <int E>
-__device__ __forceinline__ uint2 vt_operand4(const uint4 (&v)[4]) {
-    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-    uint2 a;
-    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
-    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
-    return a;
-}
-
-// The Q^T operand of one lane: in registers, or (to keep a lane under 256
-// registers when D = 256) in the lane's own LDS slots, read back per use.
-template <int NKC>
-struct QRegs {
-    uint4 v[NKC];
-    __device__ __forceinline__ uint4 operator[](int kk) const { return v[kk]; }
-};
-template <int NKC>
-struct QLds {
-    const uint4* p;   // this lane's slot of kk = 0; slots are 64 uint4 apart
-    __device__ __forceinline__ uint4 operator[](int kk) const { return p[kk * 64]; }
-};
+using namespace mfma;
 
 template <int D, int G, int BS, int W, int T>
 struct MfmaKernel {
@@ -149,7 +66,6 @@ struct MfmaKernel {
     static constexpr int NPT = D / 16;    // PV output tiles (16 dims each)
     static constexpr int CHP = 64;        // page ids per chunk (one per lane)
     static constexpr int CH = CHP * BS;   // tokens per chunk
-    static_assert(CH % (W * T) == 0, "chunk must hold whole rounds of steps");
 
     struct State {
         floatx4 acc[NPT];
@@ -174,55 +90,74 @@ struct MfmaKernel {
         uint4 vr[NDH][NJ];
     };
 
-    // Issue the K/V loads of the step at chunk offset `off` (`remain` valid
-    // tokens when not FULL).
-    template <bool FULL>
-    static __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int pg, int g,
-                                                 int off, int remain, int i, int c) {
-        constexpr int NPG = T / BS < 1 ? 1 : T / BS;
-        int pid[NPG];
+    // Page ids of the step at chunk offset `off`, read from the chunk's page
+    // list (lane k = page k) with readlane: wave-uniform, no memory access.
+    struct StepPages {
+        int pid[T / BS < 1 ? 1 : T / BS];
+        int off_slot;   // step start within its page (BS > T only)
+    };
+    static __device__ __forceinline__ StepPages step_pages(int pg, int off) {
+        StepPages sp;
         const int k0 = off / BS;
 #pragma unroll
-        for (int k = 0; k < NPG; ++k) pid[k] = __builtin_amdgcn_readlane(pg, k0 + k);
+        for (int k = 0; k < (T / BS < 1 ? 1 : T / BS); ++k)
+            sp.pid[k] = __builtin_amdgcn_readlane(pg, k0 + k);
+        sp.off_slot = off % BS;
+        return sp;
+    }
+
+    // Issue the K loads of a step (`remain` valid tokens when not FULL).
+    template <bool FULL>
+    static __device__ __forceinline__ void issue_k(const DecodeArgs& a, Buf& b, const StepPages& sp,
+                                                   int g, int remain, int i, int c) {
         const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
         const uint16_t* kbase = a.k + (int64_t)g * BS * D;
-        const uint16_t* vbase = a.v + (int64_t)g * BS * D;
-        const int off_slot = off % BS;   // step start within its page (BS > T only)
-
-        // ---- K: NT tiles of 16 tokens, lane row i ----
-        auto& kr = b.kr;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int tok = 16 * tt + i;
             const bool ok = FULL || tok < remain;
-            const int page = page_of(tok, pid);
             const uint4* kp = reinterpret_cast<const uint4*>(
-                kbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
+                kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
 #pragma unroll
             for (int kk = 0; kk < NKC; ++kk)
-                kr[tt][kk] = ok ? load_stream(kp + 4 * kk + c) : make_uint4(0, 0, 0, 0);
+                b.kr[tt][kk] = ok ? load_stream(kp + 4 * kk + c) : make_uint4(0, 0, 0, 0);
         }
-        // ---- V: this lane's NJ tokens, dims [128 dh + 8 i, +8) ----
-        auto& vr = b.vr;
+    }
+
+    // Issue the V loads of a step: this lane's NJ tokens, dims [128 dh + 8 i, +8).
+    template <bool FULL>
+    static __device__ __forceinline__ void issue_v(const DecodeArgs& a, Buf& b, const StepPages& sp,
+                                                   int g, int remain, int i, int c) {
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const uint16_t* vbase = a.v + (int64_t)g * BS * D;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int tok = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
             const bool ok = FULL || tok < remain;
-            const int page = page_of(tok, pid);
             const uint4* vp = reinterpret_cast<const uint4*>(
-                vbase + (int64_t)page * page_stride + (int64_t)((off_slot + tok) % BS) * D);
+                vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
 #pragma unroll
-            for (int dh = 0; dh < NDH; ++dh) vr[dh][j] = ok ? load_stream(vp + 16 * dh + i) : make_uint4(0, 0, 0, 0);
+            for (int dh = 0; dh < NDH; ++dh)
+                b.vr[dh][j] = ok ? load_stream(vp + 16 * dh + i) : make_uint4(0, 0, 0, 0);
         }
-
     }
 
-    // QK, online softmax and PV of one step whose loads `b` were issued.
-    template <bool FULL, class Q>
-    static __device__ __forceinline__ void compute(const DecodeArgs& a, State& st, const Buf& b,
-                                                   const Q& qb, int remain, int c) {
+    template <bool FULL>
+    static __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int pg, int g,
+                                                 int off, int remain, int i, int c) {
+        const StepPages sp = step_pages(pg, off);
+        issue_k<FULL>(a, b, sp, g, remain, i, c);
+        issue_v<FULL>(a, b, sp, g, remain, i, c);
+    }
+
+    // QK and the online-softmax update of one step; returns the fp16 weights
+    // packed as the PV B operand (x, y used for 16-token steps).
+    template <bool FULL>
+    static __device__ __forceinline__ uint4 qk_softmax(const DecodeArgs& a, State& st, const Buf& b,
+                                                       const uint4 (&qb)[NKC], int remain, int c) {
         const auto& kr = b.kr;
-        const auto& vr = b.vr;
         // ---- S = K Q^T on the matrix cores ----
         floatx4 sc[NT];
 #pragma unroll
@@ -261,14 +196,22 @@ struct MfmaKernel {
         st.m = mnew;
 #pragma unroll
         for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
-
-        // ---- O^T += V^T P^T on the matrix cores ----
+        uint4 pb;
+        pb.x = pack_half2(p[0], p[1]);
+        pb.y = pack_half2(p[2], p[3]);
         if constexpr (T == 32) {
-            uint4 pb;
-            pb.x = pack_half2(p[0], p[1]);
-            pb.y = pack_half2(p[2], p[3]);
             pb.z = pack_half2(p[4], p[5]);
             pb.w = pack_half2(p[6], p[7]);
+        } else {
+            pb.z = pb.w = 0;
+        }
+        return pb;
+    }
+
+    // ---- O^T += V^T P^T on the matrix cores ----
+    static __device__ __forceinline__ void pv(State& st, const Buf& b, const uint4& pb) {
+        const auto& vr = b.vr;
+        if constexpr (T == 32) {
 #pragma unroll
             for (int dh = 0; dh < NDH; ++dh) {
                 st.acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
@@ -281,64 +224,51 @@ struct MfmaKernel {
                 st.acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
             }
         } else {
-            uint2 pb;
-            pb.x = pack_half2(p[0], p[1]);
-            pb.y = pack_half2(p[2], p[3]);
+            const uint2 pb2 = make_uint2(pb.x, pb.y);
 #pragma unroll
             for (int dh = 0; dh < NDH; ++dh) {
-                st.acc[dh * 8 + 0] = mfma16(vt_operand4<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
-                st.acc[dh * 8 + 1] = mfma16(vt_operand4<1>(vr[dh]), pb, st.acc[dh * 8 + 1]);
-                st.acc[dh * 8 + 2] = mfma16(vt_operand4<2>(vr[dh]), pb, st.acc[dh * 8 + 2]);
-                st.acc[dh * 8 + 3] = mfma16(vt_operand4<3>(vr[dh]), pb, st.acc[dh * 8 + 3]);
-                st.acc[dh * 8 + 4] = mfma16(vt_operand4<4>(vr[dh]), pb, st.acc[dh * 8 + 4]);
-                st.acc[dh * 8 + 5] = mfma16(vt_operand4<5>(vr[dh]), pb, st.acc[dh * 8 + 5]);
-                st.acc[dh * 8 + 6] = mfma16(vt_operand4<6>(vr[dh]), pb, st.acc[dh * 8 + 6]);
-                st.acc[dh * 8 + 7] = mfma16(vt_operand4<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
+                st.acc[dh * 8 + 0] = mfma16(vt_operand4<0>(vr[dh]), pb2, st.acc[dh * 8 + 0]);
+                st.acc[dh * 8 + 1] = mfma16(vt_operand4<1>(vr[dh]), pb2, st.acc[dh * 8 + 1]);
+                st.acc[dh * 8 + 2] = mfma16(vt_operand4<2>(vr[dh]), pb2, st.acc[dh * 8 + 2]);
+                st.acc[dh * 8 + 3] = mfma16(vt_operand4<3>(vr[dh]), pb2, st.acc[dh * 8 + 3]);
+                st.acc[dh * 8 + 4] = mfma16(vt_operand4<4>(vr[dh]), pb2, st.acc[dh * 8 + 4]);
+                st.acc[dh * 8 + 5] = mfma16(vt_operand4<5>(vr[dh]), pb2, st.acc[dh * 8 + 5]);
+                st.acc[dh * 8 + 6] = mfma16(vt_operand4<6>(vr[dh]), pb2, st.acc[dh * 8 + 6]);
+                st.acc[dh * 8 + 7] = mfma16(vt_operand4<7>(vr[dh]), pb2, st.acc[dh * 8 + 7]);
             }
         }
     }
 
-    static constexpr bool kQInLds = (D == 256) && VK_MFMA_Q_LDS256;
+    template <bool FULL>
+    static __device__ __forceinline__ void compute(const DecodeArgs& a, State& st, const Buf& b,
+                                                   const uint4 (&qb)[NKC], int remain, int c) {
+        const uint4 pb = qk_softmax<FULL>(a, st, b, qb, remain, c);
+        pv(st, b, pb);
+    }
 
-    template <class Q>
-    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const Q& qb,
+    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const uint4 (&qb)[NKC],
                                                 int t_begin, int t_end, int g, int s, int wave,
-                                                int lane, int i, int c, bool& bad) {
+                                                int lane, int i, int c, int pg_first, bool& bad) {
         const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
         for (int c0 = t_begin; c0 < t_end; c0 += CH) {
             const int c1 = min(t_end, c0 + CH);
             const int np = (c1 - c0 + BS - 1) / BS;
             int pg = 0;
             if (lane < np) {
-                pg = bt[c0 / BS + lane];
+                pg = (c0 == t_begin) ? pg_first : bt[c0 / BS + lane];
                 if (pg < 0 || (int64_t)pg >= a.num_blocks) {
                     pg = 0;
                     bad = true;
                 }
             }
-            // Full steps of this wave (optionally software-pipelined over two
-            // register buffers, the next step's loads in flight while the
-            // current step computes), then at most one partial step.
+            // Full steps of this wave, then at most one partial step.
             const int first = c0 + wave * T;
             constexpr int stride = W * T;
             const int nfull = (first + T <= c1) ? (c1 - T - first) / stride + 1 : 0;
-            if (!VK_MFMA_PIPELINE) {
-                for (int k = 0; k < nfull; ++k) {
-                    Buf b0;
-                    issue<true>(a, b0, pg, g, first + k * stride - c0, T, i, c);
-                    compute<true>(a, st, b0, qb, T, c);
-                }
-            } else if (nfull > 0) {
-                Buf b0, b1;
-                issue<true>(a, b0, pg, g, first - c0, T, i, c);
-                int k = 0;
-                for (; k + 2 <= nfull; k += 2) {
-                    issue<true>(a, b1, pg, g, first + (k + 1) * stride - c0, T, i, c);
-                    compute<true>(a, st, b0, qb, T, c);
-                    if (k + 2 < nfull) issue<true>(a, b0, pg, g, first + (k + 2) * stride - c0, T, i, c);
-                    compute<true>(a, st, b1, qb, T, c);
-                }
-                if (k < nfull) compute<true>(a, st, b0, qb, T, c);
+            for (int k = 0; k < nfull; ++k) {
+                Buf b;
+                issue<true>(a, b, pg, g, first + k * stride - c0, T, i, c);
+                compute<true>(a, st, b, qb, T, c);
             }
             const int tl = first + nfull * stride;
             if (tl < c1) {
@@ -349,19 +279,33 @@ struct MfmaKernel {
         }
     }
 
-    static __device__ void run(const DecodeArgs& a) {
-        __shared__ uint4 s_q[kQInLds ? W : 1][kQInLds ? NKC : 1][64];
+    static __device__ void item(const DecodeArgs& a, const int part, const int g, const int s) {
         __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
         __shared__ float s_m[W][G];
         __shared__ float s_l[W][G];
         __shared__ int s_bad[W];
 
-        const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int i = lane & 15, c = lane >> 4;
         const int Hq = a.num_q_heads;
         const int P = a.partition_size, NP = a.max_num_partitions;
 
+        // Issue the independent loads together: the sequence length, the
+        // first chunk's page ids (its start does not depend on the length;
+        // the index is clamped into the table row and the ids are used only
+        // below ceil(L/bs)) and the query.  The first K/V loads then wait for
+        // one round trip, not for the length and then the table.
+        const int t_first = P > 0 ? part * P : 0;
+        const int32_t pg_first =
+            a.block_tables[(int64_t)s * a.max_blocks_per_seq +
+                           min(t_first / BS + lane, a.max_blocks_per_seq - 1)];
+        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
+        uint4 qb[NKC];
+        {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
         int L = a.seq_lens[s];
         bool poison = false;
         const int cap = a.max_blocks_per_seq * BS;
@@ -383,19 +327,6 @@ struct MfmaKernel {
             return;  // split: partitions past the end write nothing
         }
 
-        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
-        QRegs<NKC> qreg;
-        {
-            const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
-#pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) qreg.v[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
-        }
-        QLds<NKC> qlds;
-        qlds.p = &s_q[kQInLds ? wave : 0][0][lane];
-        if constexpr (kQInLds) {
-#pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) s_q[wave][kk][lane] = qreg.v[kk];
-        }
 
         State st;
 #pragma unroll
@@ -404,10 +335,7 @@ struct MfmaKernel {
         st.l = 0.f;
         bool bad = false;
 
-        if constexpr (kQInLds)
-            scan(a, st, qlds, t_begin, t_end, g, s, wave, lane, i, c, bad);
-        else
-            scan(a, st, qreg, t_begin, t_end, g, s, wave, lane, i, c, bad);
+        scan(a, st, qb, t_begin, t_end, g, s, wave, lane, i, c, pg_first, bad);
 
         // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
         float lsum = st.l + __shfl_xor(st.l, 16);
@@ -487,6 +415,8 @@ struct MfmaKernel {
             }
         }
     }
+
+    static __device__ void run(const DecodeArgs& a) { item(a, blockIdx.x, blockIdx.y, blockIdx.z); }
 };
 
 // At least two resident waves per SIMD: caps a lane at 256 registers.

@@ -1,0 +1,79 @@
+// Device helpers shared by the matrix-core decode kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vk {
+namespace mfma {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A product rounded to fp32 and never fused into a later add, so the running
+// max and the exponent argument see the same score.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
+__device__ __forceinline__ floatx4 mfma32(const uint4& a, const uint4& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16(const uint2& a, const uint2& b, const floatx4& c) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                  __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+// K and V are read exactly once per step: nontemporal (streaming) loads.  On
+// MI355X a plain streaming read tops out near 6.0 TB/s and a nontemporal one
+// near 6.5 TB/s.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t word(const uint4& v) {
+    return W == 0 ? v.x : W == 1 ? v.y : W == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// 8x8 fp16 transpose step: dims e of tokens 0..7 (lane group's k-slots) out of
+// 8 rows of 8 dims each.
+template <int E>
+__device__ __forceinline__ uint4 vt_operand(const uint4 (&v)[8]) {
+    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+    uint4 a;
+    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
+    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
+    a.z = __builtin_amdgcn_perm(word<E / 2>(v[5]), word<E / 2>(v[4]), sel);
+    a.w = __builtin_amdgcn_perm(word<E / 2>(v[7]), word<E / 2>(v[6]), sel);
+    return a;
+}
+
+// 4x8 fp16 transpose step for the 16x16x16 product: dim e of the lane
+// group's 4 tokens.
+template <int E>
+__device__ __forceinline__ uint2 vt_operand4(const uint4 (&v)[4]) {
+    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+    uint2 a;
+    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
+    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
+    return a;
+}
+
+
+}  // namespace mfma
+}  // namespace vk

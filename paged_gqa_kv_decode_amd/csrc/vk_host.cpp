@@ -195,6 +195,7 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
+    a.num_seqs = num_seqs;
     a.partition_size = partition_size;
     a.max_num_partitions = max_num_partitions;
     // log2(e) folded into the scale once, in double, then rounded to fp32.

@@ -21,6 +21,7 @@ struct DecodeArgs {
     int32_t max_blocks_per_seq;
     int32_t num_q_heads;
     int32_t num_kv_heads;
+    int32_t num_seqs;
     int32_t partition_size;       // 0 = unsplit
     int32_t max_num_partitions;
     float scale_log2e;            // scale * log2(e), rounded once to fp32

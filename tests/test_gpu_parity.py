@@ -16,6 +16,7 @@ from paged_gqa_kv_decode_amd.workloads import make_custom, make_onehot_probe
 pytestmark = pytest.mark.gpu
 
 KERNELS = [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4]
+FAMILIES = [vb.KERNEL_DOT, vb.KERNEL_MFMA]
 
 NAMED = [("tiny_1x64", 0), ("batch8_2k", 512), ("long32_16k", 256), ("long32_16k", 512),
          ("mixed64_32k", 512), ("long4_128k", -1)]
@@ -77,7 +78,7 @@ def test_partials_match_oracle(orc, name, P, kernel):
 @pytest.mark.parametrize("name,P", [("tiny_1x64", 0), ("batch8_2k", 512), ("batch8_2k", 0),
                                     ("long32_16k", 256), ("mixed64_32k", 512),
                                     ("long4_128k", 512), ("long4_128k", 0)])
-@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+@pytest.mark.parametrize("kernel", FAMILIES)
 def test_onehot_probe_bit_exact(name, P, kernel):
     """Page-table indexing: every output decodes to exactly the (block, slot,
     KV head) the page table names for the target token."""
@@ -127,7 +128,7 @@ def test_page_permutation_bit_identical(name, P, kernel):
     assert np.array_equal(out, base)
 
 
-@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+@pytest.mark.parametrize("kernel", FAMILIES)
 @pytest.mark.parametrize("name,Pa,Pb", [("batch8_2k", 0, 512), ("long32_16k", 256, 512),
                                         ("batch8_2k", 256, 512)])
 def test_split_vs_unsplit(name, Pa, Pb, kernel):
@@ -161,7 +162,7 @@ def test_repeat_runs_bit_identical(name, P, kernel):
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("tiny_1x64", 0), ("long4_128k", 512),
                                     ("mixed64_32k", 512)])
 @pytest.mark.parametrize("pad", ["minus1", "block"])
-@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA])
+@pytest.mark.parametrize("kernel", FAMILIES)
 def test_canaries_never_read(name, P, pad, kernel):
     """NaN in unused blocks and in the slots past L; padding entries of the
     page table -1 or the id of a block that is unused (NaN) where one exists.
@@ -240,12 +241,14 @@ def test_all_specialisations_ragged(orc, geom, bs, kernel):
 
 
 @pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
-def test_device_side_guards(kernel):
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_device_side_guards(kernel, head_dim):
     """Values the host cannot validate: a length <= 0 gives zeros; a page id
     outside the pool or a length beyond the page table gives NaN for that
     sequence only, without reading out of bounds."""
     import torch
-    wl = make_custom(seq_lens=[40, 40, 40, 40], num_q_heads=16, num_kv_heads=2, head_dim=128,
+    wl = make_custom(seq_lens=[40, 40, 40, 40], num_q_heads=16, num_kv_heads=2,
+                     head_dim=head_dim,
                      block_size=16, seed=5, pool_factor=2.0)
     q, k, v, bt, sl = to_device(wl)
     sl_dev = torch.tensor([40, 0, 40, 40 + 16 * 10], dtype=torch.int32, device="cuda")
@@ -254,14 +257,15 @@ def test_device_side_guards(kernel):
     bt_dev = torch.from_numpy(bt_h).cuda()
     prev = vb.select_decode_kernel(kernel)
     for P in (0, 512):
-        out = torch.full((4, 16, 128), 7.0, device="cuda")
+        D = wl.head_dim
+        out = torch.full((4, 16, D), 7.0, device="cuda")
         if P == 0:
             vb.paged_gqa_decode(q, k, v, bt_dev, sl_dev, wl.scale, 0, 1, out)
         else:
             NP = 1
             ml = torch.empty((4, 16, NP), device="cuda")
             es = torch.empty((4, 16, NP), device="cuda")
-            to = torch.empty((4, 16, NP, 128), device="cuda")
+            to = torch.empty((4, 16, NP, D), device="cuda")
             vb.paged_gqa_decode(q, k, v, bt_dev, sl_dev, wl.scale, P, NP, None, ml, es, to)
             vb.paged_gqa_reduce(ml, es, to, sl_dev, P, out)
         torch.cuda.synchronize()
