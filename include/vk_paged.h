@@ -170,6 +170,34 @@ vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums,
                               int32_t max_num_partitions, float* out, void* stream);
 
 /*
+ * vk_paged_kv_append — write each sequence's new token into the paged cache
+ * (vllm-metal kernels page, section "什么是 Paged Attention": the token at
+ * position pos of sequence s lives in physical page block_tables[s][pos/bs],
+ * slot pos % bs; the voxtral.c page, dpshk.com/news/5521762, sections
+ * "模型结构与解码瓶颈" and "下一步优化方向": every decode step writes the new
+ * K/V, and rotary embedding of K is fused into that write).
+ *
+ *   k_new, v_new   fp16 [num_seqs, num_kv_heads, head_dim], device
+ *   positions      int32 [num_seqs], device: the token's index in its
+ *                  sequence (the sequence length before the append); a
+ *                  negative position skips the sequence
+ *   rope_theta     <= 0: K is copied as is; > 0: each pair (d, d + D/2) of K
+ *                  is rotated by pos * rope_theta^(-2d/D) (rotate-half form),
+ *                  computed in float64 and rounded once to fp16
+ *   k_cache, v_cache  the pools of vk_paged_gqa_decode, written in place
+ * Only slot (block_tables[s][pos/bs], pos % bs) of each KV head is written.
+ * Device-side values the host cannot see are guarded: a position at or past
+ * max_blocks_per_seq*block_size, or a page id outside [0, num_blocks),
+ * writes nothing for that sequence.  head_dim must be even and at most 256;
+ * the geometry need not be one of the decode's admitted ones.
+ */
+vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,
+                             const int32_t* positions, int32_t num_seqs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, double rope_theta, void* k_cache, void* v_cache,
+                             void* stream);
+
+/*
  * vk_select_decode_kernel — A/B switch for this thread's later decode calls
  * (the pages describe an equivalent switch back to a former path for A/B
  * comparison).  VK_KERNEL_AUTO picks the fastest family for the geometry.

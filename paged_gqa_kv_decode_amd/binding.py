@@ -23,7 +23,8 @@ KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4 = 3, 4, 5
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_reduce",
-            "vk_select_decode_kernel", "vk_status_string", "vk_last_hip_error", "vk_last_plan")
+            "vk_paged_kv_append", "vk_select_decode_kernel", "vk_status_string",
+            "vk_last_hip_error", "vk_last_plan")
 
 
 class VkError(RuntimeError):
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_decode.restype = i32
     L.vk_paged_gqa_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     L.vk_paged_gqa_reduce.restype = i32
+    L.vk_paged_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64,
+                                     ctypes.c_double, vp, vp, vp]
+    L.vk_paged_kv_append.restype = i32
     L.vk_select_decode_kernel.argtypes = [i32]
     L.vk_select_decode_kernel.restype = i32
     L.vk_status_string.argtypes = [i32]
@@ -214,6 +218,28 @@ def paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: in
                                      _ptr(seq_lens), S, Hq, D, int(partition_size), NP,
                                      _ptr(out), _stream_handle(stream))
     _check("vk_paged_gqa_reduce", code)
+
+
+def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache,
+                    rope_theta: float = 0.0, stream=None) -> None:
+    """Enqueue the append: k_new / v_new [S,Hkv,D] fp16, positions [S] int32,
+    written into k_cache / v_cache [num_blocks,Hkv,bs,D] in place."""
+    import torch
+    for t, dt, n in ((k_new, torch.float16, "k_new"), (v_new, torch.float16, "v_new"),
+                     (block_tables, torch.int32, "block_tables"), (positions, torch.int32, "positions"),
+                     (k_cache, torch.float16, "k_cache"), (v_cache, torch.float16, "v_cache")):
+        _need(t, dt, n)
+    S, Hkv, D = k_new.shape
+    nb, Hkv2, bs, D2 = k_cache.shape
+    if tuple(v_new.shape) != (S, Hkv, D) or (Hkv2, D2) != (Hkv, D) or \
+            tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_new / v_new / cache shapes disagree")
+    if block_tables.shape[0] != S or tuple(positions.shape) != (S,):
+        raise ValueError("block_tables / positions must have num_seqs rows")
+    code = lib().vk_paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
+                                    S, Hkv, D, bs, block_tables.shape[1], nb, float(rope_theta),
+                                    _ptr(k_cache), _ptr(v_cache), _stream_handle(stream))
+    _check("vk_paged_kv_append", code)
 
 
 class DecodeStep:

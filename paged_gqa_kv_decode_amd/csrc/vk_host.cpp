@@ -242,6 +242,38 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     return VK_OK;
 }
 
+vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,
+                             const int32_t* positions, int32_t num_seqs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, double rope_theta, void* k_cache, void* v_cache,
+                             void* stream) {
+    if (!k_new || !v_new || !block_tables || !positions || !k_cache || !v_cache)
+        return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return VK_ERR_BAD_DIM;
+    if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return VK_ERR_BAD_DIM;
+    if (!block_size_ok(block_size)) return VK_ERR_BLOCK_SIZE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return VK_ERR_BAD_DIM;
+    if (!std::isfinite(rope_theta)) return VK_ERR_BAD_DIM;
+    vk::AppendArgs a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.block_tables = block_tables;
+    a.positions = positions;
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.rope_theta = rope_theta;
+    hipError_t e = vk::launch_kv_append(a, num_seqs, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return VK_OK;
+}
+
 vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums, const float* tmp_out,
                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                               int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,

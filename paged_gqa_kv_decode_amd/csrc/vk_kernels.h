@@ -38,6 +38,21 @@ struct ReduceArgs {
     int32_t max_num_partitions;
 };
 
+struct AppendArgs {
+    const uint16_t* k_new;        // fp16 [S, Hkv, D]
+    const uint16_t* v_new;        // fp16 [S, Hkv, D]
+    const int32_t* block_tables;  // [S, max_blocks_per_seq]
+    const int32_t* positions;     // [S]
+    uint16_t* k_cache;            // fp16 [num_blocks, Hkv, BS, D]
+    uint16_t* v_cache;
+    int64_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    double rope_theta;            // <= 0: no rotary embedding
+};
+
 // Each launcher returns hipSuccess or the launch error; `geometry_ok` is
 // false when no specialisation exists for the shape (host code checks first).
 hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,
@@ -46,6 +61,7 @@ hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int b
 hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
                               int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
                               int* block);
+hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok);
 
