@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kernel auto|dot|mfma]
 
 One step = the whole path on device-resident inputs: partition plan (host),
-decode kernel, partition reduce kernel.  W untimed steps, then K steps timed
+decode kernel, partition reduce kernel (or, with --fused, the single launch
+that merges the partials in place).  W untimed steps, then K steps timed
 between two device synchronisations.  Prints ONE JSON line:
 
   value            KV-read throughput, GB/s: algorithmic K+V bytes of one step
@@ -55,17 +56,19 @@ KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4"}
 def sources_sha(kernel: int) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(kernel, []) + ["paged_gqa_kv_decode_amd/csrc/vk_kernels.h",
-                                                 "paged_gqa_kv_decode_amd/csrc/mfma_ops.h"]:
+                                                 "paged_gqa_kv_decode_amd/csrc/mfma_ops.h",
+                                                 "paged_gqa_kv_decode_amd/csrc/merge_ops.h"]:
         p = os.path.join(ROOT, rel)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, partition: int, kernel: int):
+def load_traffic(workload: str, partition: int, kernel: int, fused: bool = False):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     or None if absent or stale."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_P{partition}_traffic.txt")
+    tag = "_fused" if fused else ""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_P{partition}{tag}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -155,24 +158,38 @@ def ceilings(wl, dev, P, reps=10):
             "flushed": "512 MiB read before each timed run"}
 
 
-def cpu_baseline(wl, sample_seqs: int):
-    """Time the float64 oracle on the first `sample_seqs` sequences."""
+def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
+    """Time the float64 oracle, as it stands, on a bounded sample of the
+    workload: whole sequences, taken in order and cycling over the batch,
+    until at least `min_seconds` of wall time (a sequence is not started when
+    the estimate says it would end past `max_seconds`)."""
     import numpy as np
     import oracle
     from paged_gqa_kv_decode_amd.workloads import kv_read_bytes
-    sub_sl = wl.seq_lens[:sample_seqs]
-    args = (wl.q[:sample_seqs], wl.k_cache, wl.v_cache, wl.block_tables[:sample_seqs], sub_sl,
-            wl.scale)
     nthreads = oracle.default_threads()
-    t = time.perf_counter()
-    oracle.paged_attention_arrays(*args, nthreads=nthreads)
-    dt = time.perf_counter() - t
-    kv = kv_read_bytes(sub_sl, wl.num_kv_heads, wl.head_dim)
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s (KV-read)", "cores": nthreads,
-            "kind": "oracle",
-            "sample": f"first {sample_seqs} of {wl.num_seqs} sequences ({int(np.sum(sub_sl))} tokens, "
-                      f"all {wl.num_q_heads} q heads), 1 run, {dt:.2f} s wall",
-            "seconds": round(dt, 3)}
+    done_tokens, done_bytes, runs, total = 0, 0, 0, 0.0
+    per_token = None
+    while total < min_seconds:
+        s = runs % wl.num_seqs
+        L = int(wl.seq_lens[s])
+        if per_token is not None and total + per_token * L > max_seconds:
+            break
+        t = time.perf_counter()
+        oracle.paged_attention_arrays(wl.q[s:s + 1], wl.k_cache, wl.v_cache,
+                                      wl.block_tables[s:s + 1], wl.seq_lens[s:s + 1], wl.scale,
+                                      nthreads=nthreads)
+        dt = time.perf_counter() - t
+        total += dt
+        runs += 1
+        done_tokens += L
+        done_bytes += kv_read_bytes(wl.seq_lens[s:s + 1], wl.num_kv_heads, wl.head_dim)
+        per_token = total / max(done_tokens, 1)
+    return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s (KV-read)",
+            "cores": nthreads, "kind": "oracle",
+            "sample": f"{runs} single-sequence oracle calls cycling over the {wl.num_seqs} "
+                      f"sequences ({done_tokens} tokens, all {wl.num_q_heads} q heads), "
+                      f"{total:.2f} s wall",
+            "seconds": round(total, 3)}
 
 
 def main():
@@ -185,7 +202,19 @@ def main():
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle sample (cpu_baseline)")
+    ap.add_argument("--append", action="store_true",
+                    help="each step first appends one token per sequence to the paged cache "
+                         "(vk_paged_kv_append with rotary K, theta 10000): it rewrites slot L-1 "
+                         "with that token's K rotated for position L-1 and its V, the same "
+                         "values every step; reported as append_us_median")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (no host "
+                         "launch overhead between steps): us_per_step_graph")
+    ap.add_argument("--fused", action="store_true",
+                    help="single launch: decode with the partials merged in place "
+                         "(vk_paged_gqa_decode_fused) instead of decode + reduce")
     ap.add_argument("--max-copies", type=int, default=256,
                     help="cap on the rotated K/V pool copies")
     ap.add_argument("--ceiling", action="store_true",
@@ -247,20 +276,37 @@ def main():
 
     # Scratch sized once from a first plan; every step plans again (host) and
     # reuses it (the plan depends only on the host seq_lens).
-    step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out)
+    step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out,
+                          fused=args.fused)
     P, NP = step0.plan.partition_size, step0.plan.max_num_partitions
 
     counter = [0]
+    if args.append:
+        # the K/V rows at slot L-1 of the workload and their positions
+        last = torch.from_numpy((wl.seq_lens - 1).astype(np.int32)).cuda()
+        blk = wl.block_tables[np.arange(wl.num_seqs), (wl.seq_lens - 1) // wl.block_size]
+        slot = (wl.seq_lens - 1) % wl.block_size
+        k_new = torch.from_numpy(np.ascontiguousarray(wl.k_cache[blk, :, slot, :])).cuda()
+        v_new = torch.from_numpy(np.ascontiguousarray(wl.v_cache[blk, :, slot, :])).cuda()
 
-    def one_step(ev=None):
+    def one_step(ev=None, stream=stream):
         k, v = pools[counter[0] % ncopies]
         counter[0] += 1
+        if args.append:
+            if ev is not None:
+                ev[3].record(stream)
+            vb.paged_kv_append(k_new, v_new, bt, last, k, v, 10000.0, stream)
         plan = vb.plan_partitions(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                   wl.block_size, wl.max_blocks_per_seq, P_req, 0)
         assert plan.partition_size == P and plan.max_num_partitions == NP
         if ev is not None:
             ev[0].record(stream)
-        if P:
+        if args.fused:
+            vb.paged_gqa_decode_fused(q, k, v, bt, sl, wl.scale, P, NP, out, step0.max_logits,
+                                      step0.exp_sums, step0.tmp_out, step0.counters, stream)
+            if ev is not None:
+                ev[1].record(stream)
+        elif P:
             vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, P, NP, None, step0.max_logits,
                                 step0.exp_sums, step0.tmp_out, stream)
             if ev is not None:
@@ -279,7 +325,7 @@ def main():
     torch.cuda.synchronize()
     kernel_ran = vb.last_plan().kernel
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t = time.perf_counter()
     for i in range(args.steps):
@@ -289,11 +335,12 @@ def main():
 
     dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    app_ms = np.array([e[3].elapsed_time(e[0]) for e in events]) if args.append else None
     ms_per_step = wall * 1e3 / args.steps
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     dec_mean_s = float(dec_ms.mean()) * 1e-3
     achieved = kv_bytes / dec_mean_s / 1e9
-    traffic = load_traffic(args.workload, P, kernel_ran)
+    traffic = load_traffic(args.workload, P, kernel_ran, args.fused)
 
     result = {
         "metric": "decode-attention µs/step and KV-read HBM GB/s (% of MI355X peak)",
@@ -314,7 +361,8 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "partition_size": P, "max_num_partitions": NP,
-                   "decode_kernel": KERNEL_NAMES.get(kernel_ran, str(kernel_ran))},
+                   "decode_kernel": KERNEL_NAMES.get(kernel_ran, str(kernel_ran)),
+                   "single_launch": bool(args.fused), "with_append": bool(args.append)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -323,11 +371,29 @@ def main():
                       "decode_p5": round(float(np.percentile(dec_ms, 5)) * 1e3, 2),
                       "decode_p95": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
                       "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)},
+        **({"append_us_median": round(float(np.median(app_ms)) * 1e3, 2)} if args.append else {}),
         "kv_read_bytes": kv_bytes,
         "kv_pool_copies": ncopies,
         "bytes_read_between_reuse": (ncopies - 1) * kv_bytes,
         "input_gen_s": round(gen_s, 1),
     }
+    if args.graph:
+        # One step per pool copy captured back to back; replayed until K steps.
+        cap = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(ncopies):
+                one_step(stream=cap)
+        reps = max(1, -(-args.steps // ncopies))
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        result["us_per_step_graph"] = round((time.perf_counter() - t) * 1e6 / (reps * ncopies), 2)
     if args.ceiling:
         result["ceiling"] = ceilings(wl, dev, P)
     if args.flush:
@@ -338,13 +404,13 @@ def main():
         for _ in range(20):
             L.vkb_stream_read(flush.data_ptr(), flush.numel(), fsink.data_ptr(), 4096,
                               stream.cuda_stream)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             one_step(ev)
             torch.cuda.synchronize()
             fl.append(ev[0].elapsed_time(ev[1]))
         result["kernel_us"]["decode_median_flushed"] = round(float(np.median(fl)) * 1e3, 2)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, max(1, min(args.cpu_sample_seqs, wl.num_seqs)))
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, 3 * args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -37,6 +37,7 @@
  *   max_logits    fp32  [num_seqs, num_q_heads, max_num_partitions]
  *   exp_sums      fp32  [num_seqs, num_q_heads, max_num_partitions]
  *   tmp_out       fp32  [num_seqs, num_q_heads, max_num_partitions, head_dim]
+ *   counters      uint32 [num_seqs, num_kv_heads] (single-launch form only)
  *
  * Ownership and asynchrony: every tensor pointer is device memory owned by the
  * caller.  The library allocates nothing, frees nothing and keeps no pointer
@@ -168,6 +169,46 @@ vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums,
                               const float* tmp_out, const int32_t* seq_lens, int32_t num_seqs,
                               int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
                               int32_t max_num_partitions, float* out, void* stream);
+
+/*
+ * vk_paged_gqa_decode_fused — decode and reduce in one launch (the voxtral.c
+ * page, dpshk.com/news/5521762, sections "模型结构与解码瓶颈" and "融合内核如何
+ * 工作": a token-by-token decode step pays per launch, and fusing small
+ * kernels cuts launches and buffer round trips; vllm-metal kernels page,
+ * section "GQA 解码内核的四个提速技巧", item 4: the partials are merged by the
+ * same split-KV reduction).
+ *
+ * Arguments are those of vk_paged_gqa_decode, plus
+ *   counters   uint32 [num_seqs * num_kv_heads], device, owned by the caller;
+ *              required when partition_size > 0, ignored (may be NULL) when 0.
+ *              Must be all zero before the first call; every completed call
+ *              leaves it all zero again, so one buffer serves any number of
+ *              later calls on the same stream without clearing.  Calls that
+ *              overlap in time on one counter buffer (different streams) race.
+ * and `out` is always required: it receives the final normalised result
+ *   out[s,h,:] for every (s, h), as after vk_paged_gqa_decode followed by
+ *   vk_paged_gqa_reduce (same formula; the summation order differs).
+ * Split: each workgroup writes its partial triple to max_logits/exp_sums/
+ *   tmp_out as in vk_paged_gqa_decode, then counts itself in
+ *   counters[s * num_kv_heads + g]; the last of the ceil(L/P) workgroups of
+ *   (s, g) merges them into out.  A sequence with one partition writes out
+ *   directly and leaves its scratch rows untouched.  L <= 0 writes zeros.
+ * The merge is done by one workgroup per (s, KV head), so the form suits few
+ * partitions per sequence (short and medium contexts, where the second
+ * launch is a large share of the step); for very long contexts the separate
+ * reduce spreads the merge over more workgroups.  Always runs the matrix-core
+ * family (VK_KERNEL_DOT selects the automatic choice here).  Errors and
+ * device-side guards are those of vk_paged_gqa_decode; additionally
+ * VK_ERR_NULL_ARG if out is NULL, or counters is NULL with partition_size > 0.
+ */
+vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                    int32_t partition_size, int32_t max_num_partitions,
+                                    float* out, float* max_logits, float* exp_sums,
+                                    float* tmp_out, uint32_t* counters, void* stream);
 
 /*
  * vk_paged_kv_append — write each sequence's new token into the paged cache

@@ -22,8 +22,8 @@ STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_S
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4 = 3, 4, 5
 
-EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_reduce",
-            "vk_paged_kv_append", "vk_select_decode_kernel", "vk_status_string",
+EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
+            "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel", "vk_status_string",
             "vk_last_hip_error", "vk_last_plan")
 
 
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                       ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_decode.restype = i32
+    L.vk_paged_gqa_decode_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.vk_paged_gqa_decode_fused.restype = i32
     L.vk_paged_gqa_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     L.vk_paged_gqa_reduce.restype = i32
     L.vk_paged_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64,
@@ -165,13 +168,8 @@ def _need(t, dtype, name):
     _ = torch
 
 
-def paged_gqa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-                     partition_size: int, max_num_partitions: int, out=None, max_logits=None,
-                     exp_sums=None, tmp_out=None, stream=None) -> None:
-    """Enqueue the decode kernel.  Shapes are read from the tensors:
-    q [S,Hq,D] fp16, k/v [num_blocks,Hkv,bs,D] fp16, block_tables [S,max_blocks]
-    int32, seq_lens [S] int32; out [S,Hq,D] fp32 (unsplit) or max_logits /
-    exp_sums [S,Hq,NP], tmp_out [S,Hq,NP,D] fp32 (split)."""
+def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                 max_num_partitions, out, max_logits, exp_sums, tmp_out):
     import torch
     for t, dt, n in ((q, torch.float16, "q"), (k_cache, torch.float16, "k_cache"),
                      (v_cache, torch.float16, "v_cache"), (block_tables, torch.int32, "block_tables"),
@@ -193,12 +191,44 @@ def paged_gqa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                           (tmp_out, (S, Hq, max_num_partitions, D), "tmp_out")):
             if t is not None and tuple(t.shape) != shp:
                 raise ValueError(f"{n} must be {shp}")
-    code = lib().vk_paged_gqa_decode(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv,
-        D, bs, block_tables.shape[1], nb, float(scale), int(partition_size),
-        int(max_num_partitions), _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
-        _stream_handle(stream))
-    _check("vk_paged_gqa_decode", code)
+    return (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv,
+            D, bs, block_tables.shape[1], nb, float(scale), int(partition_size),
+            int(max_num_partitions), _ptr(out), _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out))
+
+
+def paged_gqa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                     partition_size: int, max_num_partitions: int, out=None, max_logits=None,
+                     exp_sums=None, tmp_out=None, stream=None) -> None:
+    """Enqueue the decode kernel.  Shapes are read from the tensors:
+    q [S,Hq,D] fp16, k/v [num_blocks,Hkv,bs,D] fp16, block_tables [S,max_blocks]
+    int32, seq_lens [S] int32; out [S,Hq,D] fp32 (unsplit) or max_logits /
+    exp_sums [S,Hq,NP], tmp_out [S,Hq,NP,D] fp32 (split)."""
+    args = _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                        max_num_partitions, out, max_logits, exp_sums, tmp_out)
+    _check("vk_paged_gqa_decode", lib().vk_paged_gqa_decode(*args, _stream_handle(stream)))
+
+
+def paged_gqa_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                           partition_size: int, max_num_partitions: int, out, max_logits=None,
+                           exp_sums=None, tmp_out=None, counters=None, stream=None) -> None:
+    """Enqueue decode + in-place merge as one launch: the final out [S,Hq,D]
+    fp32 for any partition size.  Split calls also need the scratch of
+    paged_gqa_decode and counters [S*Hkv] int32/uint32, zero before the first
+    call (each call leaves it zero)."""
+    import torch
+    if out is None:
+        raise ValueError("out is required")
+    if partition_size:
+        if counters is None or counters.dtype not in (torch.int32, torch.uint32) or \
+                counters.device.type != "cuda":
+            raise TypeError("counters must be a device int32/uint32 tensor")
+        if counters.numel() < q.shape[0] * k_cache.shape[1]:
+            raise ValueError("counters needs num_seqs * num_kv_heads entries")
+    args = _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                        max_num_partitions, out, max_logits, exp_sums, tmp_out)
+    _check("vk_paged_gqa_decode_fused",
+           lib().vk_paged_gqa_decode_fused(*args, _ptr(counters) if partition_size else None,
+                                           _stream_handle(stream)))
 
 
 def paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: int, out,
@@ -244,10 +274,11 @@ def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache,
 
 class DecodeStep:
     """One decode step on device-resident inputs: plan once (host seq_lens),
-    hold the scratch, then `run()` enqueues decode (+ reduce when split)."""
+    hold the scratch, then `run()` enqueues decode (+ reduce when split), or
+    the single-launch form when `fused`."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, seq_lens_host, scale: float,
-                 partition_request: int = -1, cu_count: int = 0, out=None):
+                 partition_request: int = -1, cu_count: int = 0, out=None, fused: bool = False):
         import torch
         S, Hq, D = q.shape
         nb, Hkv, bs, _ = k_cache.shape
@@ -265,11 +296,19 @@ class DecodeStep:
             self.tmp_out = torch.empty((S, Hq, NP, D), dtype=torch.float32, device=dev)
         else:
             self.max_logits = self.exp_sums = self.tmp_out = None
+        self.fused = bool(fused)
+        # arrival counters of the single-launch form: zeroed once, every call
+        # leaves them zero
+        self.counters = (torch.zeros(S * Hkv, dtype=torch.int32, device=dev)
+                         if (self.fused and P) else None)
 
     def run(self, stream=None):
         P, NP = self.plan.partition_size, self.plan.max_num_partitions
         q, k, v, bt, sl = self.args
-        if P:
+        if self.fused:
+            paged_gqa_decode_fused(q, k, v, bt, sl, self.scale, P, NP, self.out, self.max_logits,
+                                   self.exp_sums, self.tmp_out, self.counters, stream)
+        elif P:
             paged_gqa_decode(q, k, v, bt, sl, self.scale, P, NP, None, self.max_logits,
                              self.exp_sums, self.tmp_out, stream)
             paged_gqa_reduce(self.max_logits, self.exp_sums, self.tmp_out, sl, P, self.out,

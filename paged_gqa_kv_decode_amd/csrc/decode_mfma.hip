@@ -36,6 +36,7 @@
 // register (lane k = page k, one coalesced load) and reads the step's 1-4 ids
 // with readlane, so no dependent table load precedes each K/V load (item 2).
 // Tokens past the end are masked by select (zeroed K/V registers, score -inf).
+#include "merge_ops.h"
 #include "mfma_ops.h"
 #include "vk_constants.h"
 #include "vk_kernels.h"
@@ -56,7 +57,7 @@ namespace {
 
 using namespace mfma;
 
-template <int D, int G, int BS, int W, int T>
+template <int D, int G, int BS, int W, int T, bool FUSED>
 struct MfmaKernel {
     static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
     static constexpr int NT = T / 16;     // 16-token QK tiles per step
@@ -314,18 +315,23 @@ struct MfmaKernel {
             poison = true;
         }
         int t_begin = 0, t_end = L;
+        int nparts = 1;   // partitions of this sequence that write a result
         if (P > 0) {
             t_begin = part * P;
             t_end = min(L, t_begin + P);
             if (part == NP - 1 && L > t_begin + P) poison = true;  // beyond the grid
+            nparts = L > 0 ? (int)min(((int64_t)L + P - 1) / P, (int64_t)NP) : 0;
         }
         if (t_end <= t_begin) {
-            if (P == 0) {  // empty sequence, unsplit: zeros
+            if (P == 0 || (FUSED && part == 0)) {  // empty sequence: zeros
                 float* o = a.out + ((int64_t)s * Hq + g * G) * D;
                 for (int k = tid; k < G * D; k += 64 * W) o[k] = 0.f;
             }
             return;  // split: partitions past the end write nothing
         }
+        // Unsplit, or fused with a single partition: the normalised result
+        // goes straight to `out`.
+        const bool direct = (P == 0) || (FUSED && nparts == 1);
 
 
         State st;
@@ -348,7 +354,7 @@ struct MfmaKernel {
             if (i < G) {
                 const int64_t r = row0 + i;
                 float* dst;
-                if (P == 0) {
+                if (direct) {
                     dst = a.out + r * D;
                 } else {
                     const int64_t pr = r * NP + part;
@@ -402,7 +408,7 @@ struct MfmaKernel {
                 }
                 const float o = out_bad ? __builtin_nanf("") : num / den;
                 const int64_t r = row0 + h;
-                if (P == 0) {
+                if (direct) {
                     a.out[r * D + d] = o;
                 } else {
                     const int64_t pr = r * NP + part;
@@ -414,40 +420,93 @@ struct MfmaKernel {
                 }
             }
         }
+        if constexpr (FUSED) {
+            if (!direct) merge_if_last(a, g, s, nparts, row0, tid);
+        }
+    }
+
+    // Single-launch split-KV: the workgroup that writes the last of the
+    // sequence's `n` partials for KV head g merges all of them into `out`
+    // with the reduce kernel's merge (merge_ops.h), one wave per 32 dims of a
+    // head.  Arrival is counted in counters[s * Hkv + g] with a device-scope
+    // atomic increment that wraps to zero at n - 1: the last arrival sees
+    // n - 1 and leaves the counter at zero for the next call.
+    // Ordering across XCDs (each has its own L2): every wave waits for its
+    // partial stores to be acknowledged, the barrier gathers the workgroup,
+    // then one lane releases at device scope (L2 write-back) before its
+    // increment; the last arrival acquires (L2 invalidate) before the
+    // barrier that lets its waves read the other partials.  One release per
+    // workgroup, one acquire per (sequence, KV head).
+    static __device__ void merge_if_last(const DecodeArgs& a, int g, int s, int n, int64_t row0,
+                                         int tid) {
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const unsigned old = atomicInc(a.counters + (int64_t)s * a.num_kv_heads + g, (unsigned)(n - 1));
+            const bool last = old == (unsigned)(n - 1);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        const int NP = a.max_num_partitions;
+        const int wave = tid >> 6, lane = tid & 63;
+        constexpr int kChunks = D / merge::kDims;
+        for (int it = wave; it < G * kChunks; it += W) {
+            const int h = it / kChunks, chunk = it % kChunks;
+            const int64_t r = row0 + h;
+            merge::merge_columns(a.max_logits + r * NP, a.exp_sums + r * NP,
+                                 reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * merge::kDims),
+                                 D / 4, n, lane,
+                                 reinterpret_cast<float4*>(a.out + r * D + chunk * merge::kDims));
+        }
     }
 
     static __device__ void run(const DecodeArgs& a) { item(a, blockIdx.x, blockIdx.y, blockIdx.z); }
 };
 
 // At least two resident waves per SIMD: caps a lane at 256 registers.
-template <int D, int G, int BS, int W>
+template <int D, int G, int BS, int W, bool FUSED>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(VK_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(DecodeArgs a) {
-    MfmaKernel<D, G, BS, W, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128)>::run(a);
+    MfmaKernel<D, G, BS, W, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128), FUSED>::run(a);
 }
 
-template <int D, int G, int W>
+template <int D, int G, int W, bool FUSED>
 hipError_t launch_bs(const DecodeArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
     *ok = true;
     const dim3 block(64 * W);
     switch (bs) {
-        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W>), grid, block, 0, st, a); break;
-        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W>), grid, block, 0, st, a); break;
-        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W, FUSED>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W, FUSED>), grid, block, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W, FUSED>), grid, block, 0, st, a); break;
         default: *ok = false; return hipSuccess;
     }
     return hipGetLastError();
 }
 
-template <int W>
+template <int W, bool FUSED>
 hipError_t launch_w(const DecodeArgs& a, int group, int head_dim, int bs, dim3 grid,
                     hipStream_t st, bool* ok) {
-    if (group == 4 && head_dim == 128) return launch_bs<128, 4, W>(a, bs, grid, st, ok);
-    if (group == 6 && head_dim == 256) return launch_bs<256, 6, W>(a, bs, grid, st, ok);
-    if (group == 8 && head_dim == 128) return launch_bs<128, 8, W>(a, bs, grid, st, ok);
-    if (group == 8 && head_dim == 256) return launch_bs<256, 8, W>(a, bs, grid, st, ok);
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4, W, FUSED>(a, bs, grid, st, ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6, W, FUSED>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8, W, FUSED>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8, W, FUSED>(a, bs, grid, st, ok);
     *ok = false;
     return hipSuccess;
+}
+
+template <bool FUSED>
+hipError_t launch_waves(const DecodeArgs& a, int group, int head_dim, int block_size, int waves,
+                        dim3 grid, hipStream_t stream, bool* geometry_ok) {
+    switch (waves) {
+        case 1: return launch_w<1, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 2: return launch_w<2, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 4: return launch_w<4, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        default: *geometry_ok = false; return hipSuccess;
+    }
 }
 
 }  // namespace
@@ -456,12 +515,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int 
                               int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
                               int* block) {
     *block = 64 * waves;
-    switch (waves) {
-        case 1: return launch_w<1>(a, group, head_dim, block_size, grid, stream, geometry_ok);
-        case 2: return launch_w<2>(a, group, head_dim, block_size, grid, stream, geometry_ok);
-        case 4: return launch_w<4>(a, group, head_dim, block_size, grid, stream, geometry_ok);
-        default: *geometry_ok = false; return hipSuccess;
-    }
+    // Split launches with a counter array merge their partitions in place.
+    if (a.counters != nullptr && a.partition_size > 0)
+        return launch_waves<true>(a, group, head_dim, block_size, waves, grid, stream, geometry_ok);
+    return launch_waves<false>(a, group, head_dim, block_size, waves, grid, stream, geometry_ok);
 }
 
 }  // namespace vk

@@ -155,14 +155,21 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int
     return VK_OK;
 }
 
-vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_tables, const int32_t* seq_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                              int64_t num_blocks, float scale, int32_t partition_size,
-                              int32_t max_num_partitions, float* out, float* max_logits,
-                              float* exp_sums, float* tmp_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the two decode entry points; `fused` selects the single-launch
+// form (split partials merged in place by the last workgroup per KV head).
+vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                      float scale, int32_t partition_size, int32_t max_num_partitions, float* out,
+                      float* max_logits, float* exp_sums, float* tmp_out, uint32_t* counters,
+                      bool fused, void* stream) {
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return VK_ERR_NULL_ARG;
+    if (fused && (!out || (partition_size != 0 && !counters))) return VK_ERR_NULL_ARG;
     if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return VK_ERR_BAD_DIM;
     if (num_seqs > 65535) return VK_ERR_BAD_DIM;  // grid.z limit
     vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
@@ -191,6 +198,7 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     a.max_logits = max_logits;
     a.exp_sums = exp_sums;
     a.tmp_out = tmp_out;
+    a.counters = fused ? counters : nullptr;
     a.num_blocks = num_blocks;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_q_heads = num_q_heads;
@@ -208,6 +216,8 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     bool ok = false;
     int block = 0;
     int32_t kernel = t_kernel_choice;
+    // The in-place merge exists only in the matrix-core family.
+    if (fused && kernel == VK_KERNEL_DOT) kernel = VK_KERNEL_AUTO;
     if (kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA) {
         // Waves per workgroup from the grid size (measured on MI355X, 256
         // CUs, two resident waves per SIMD = 2048 wave slots): small grids
@@ -240,6 +250,37 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     p.block = block;
     t_last_plan = p;
     return VK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, float* max_logits,
+                              float* exp_sums, float* tmp_out, void* stream) {
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
+                       nullptr, false, stream);
+}
+
+vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                    int32_t partition_size, int32_t max_num_partitions,
+                                    float* out, float* max_logits, float* exp_sums,
+                                    float* tmp_out, uint32_t* counters, void* stream) {
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
+                       counters, true, stream);
 }
 
 vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,

@@ -17,6 +17,7 @@ struct DecodeArgs {
     float* max_logits;            // [S, Hq, NP]         (split)
     float* exp_sums;              // [S, Hq, NP]         (split)
     float* tmp_out;               // [S, Hq, NP, D]      (split)
+    uint32_t* counters;           // [S, Hkv] arrival counters (split, single launch); else null
     int64_t num_blocks;
     int32_t max_blocks_per_seq;
     int32_t num_q_heads;

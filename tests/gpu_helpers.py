@@ -29,10 +29,22 @@ def to_device(wl):
     return vb.device_inputs(wl, "cuda")
 
 
+_refs = {}
+
+
+def oracle_ref(orc, name):
+    """Oracle output of a named workload, computed once per process."""
+    if name not in _refs:
+        say(f"  oracle {name} ...")
+        _refs[name] = orc.paged_attention(named(name))
+    return _refs[name]
+
+
 def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=False,
-            prefill_nan=True, cu_count=0):
-    """One decode step through libvkpaged.  Returns (out float64 numpy, plan,
-    partials or None)."""
+            prefill_nan=True, cu_count=0, fused=False):
+    """One decode step through libvkpaged (decode + reduce, or the single-launch
+    form when `fused`).  Returns (out float64 numpy, plan, last launch plan,
+    partials or None).  A fused split call must leave its counters at zero."""
     import torch
     if dev is None:
         dev = to_device(wl)
@@ -42,7 +54,7 @@ def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=Fal
     prev = vb.select_decode_kernel(kernel) if kernel is not None else None
     try:
         step = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, partition_request,
-                             cu_count=cu_count, out=out)
+                             cu_count=cu_count, out=out, fused=fused)
         if step.tmp_out is not None and prefill_nan:
             step.max_logits.fill_(float("nan"))
             step.exp_sums.fill_(float("nan"))
@@ -53,6 +65,8 @@ def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=Fal
     finally:
         if prev is not None:
             vb.select_decode_kernel(prev)
+    if step.counters is not None:
+        assert int(step.counters.abs().sum().item()) == 0, "counters not returned to zero"
     parts = None
     if keep_partials and step.tmp_out is not None:
         parts = (step.max_logits.cpu().numpy().astype(np.float64),

@@ -9,7 +9,7 @@ repeated runs and canaries are bit-exact.
 import numpy as np
 import pytest
 
-from gpu_helpers import assert_parity, named, run_hip, say, to_device
+from gpu_helpers import assert_parity, named, oracle_ref, run_hip, say, to_device
 from paged_gqa_kv_decode_amd import binding as vb
 from paged_gqa_kv_decode_amd.workloads import make_custom, make_onehot_probe
 
@@ -21,7 +21,6 @@ FAMILIES = [vb.KERNEL_DOT, vb.KERNEL_MFMA]
 NAMED = [("tiny_1x64", 0), ("batch8_2k", 512), ("long32_16k", 256), ("long32_16k", 512),
          ("mixed64_32k", 512), ("long4_128k", -1)]
 
-_refs = {}
 _probes = {}
 
 
@@ -32,13 +31,6 @@ def _probe(name, seed):
             _probes.pop(next(iter(_probes)))
         _probes[key] = make_onehot_probe(named(name, canaries=True), seed=seed)
     return _probes[key]
-
-
-def oracle_ref(orc, name):
-    if name not in _refs:
-        say(f"  oracle {name} ...")
-        _refs[name] = orc.paged_attention(named(name))
-    return _refs[name]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
