@@ -198,9 +198,14 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long4_128k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--shape", default=None,
+                    help="time a custom shape instead: S,Hq,Hkv,D,bs,Lmin,Lmax (lengths uniform "
+                         "in [Lmin, Lmax], seeded; pages shuffled in an exact-fit pool)")
     ap.add_argument("--partition", type=int, default=None,
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4"])
+    ap.add_argument("--order", default="auto", choices=["auto", "grid", "longest"],
+                    help="work order of the matrix-core decode (A/B switch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle sample (cpu_baseline)")
@@ -253,13 +258,26 @@ def main():
     from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, make_workload
 
     t0 = time.time()
-    wl = make_workload(args.workload)
+    if args.shape:
+        from paged_gqa_kv_decode_amd.workloads import make_custom
+        S_, Hq_, Hkv_, D_, bs_, lo_, hi_ = (int(x) for x in args.shape.split(","))
+        lens_ = np.random.default_rng(7).integers(lo_, hi_ + 1, S_)
+        wl = make_custom(seq_lens=lens_, num_q_heads=Hq_, num_kv_heads=Hkv_, head_dim=D_,
+                         block_size=bs_, seed=7)
+        wl.partition_sizes = (-1,)
+        args.workload = f"custom_{args.shape}"
+        DESCRIPTIONS[args.workload] = (f"{S_} seqs, L uniform in [{lo_}, {hi_}], "
+                                       f"({Hq_}q, {Hkv_}kv, {D_}), block {bs_}")
+    else:
+        wl = make_workload(args.workload)
     gen_s = time.time() - t0
     P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
     kernel = {"auto": vb.KERNEL_AUTO, "dot": vb.KERNEL_DOT, "mfma": vb.KERNEL_MFMA,
               "mfma1": vb.KERNEL_MFMA_W1, "mfma2": vb.KERNEL_MFMA_W2,
               "mfma4": vb.KERNEL_MFMA_W4}[args.kernel]
     vb.select_decode_kernel(kernel)
+    vb.select_work_order({"auto": vb.ORDER_AUTO, "grid": vb.ORDER_GRID,
+                          "longest": vb.ORDER_LONGEST_FIRST}[args.order])
 
     dev = vb.device_inputs(wl)
     q, k, v, bt, sl = dev
@@ -324,6 +342,7 @@ def main():
         one_step()
     torch.cuda.synchronize()
     kernel_ran = vb.last_plan().kernel
+    order_ran = vb.last_plan().work_order
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -362,6 +381,7 @@ def main():
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "partition_size": P, "max_num_partitions": NP,
                    "decode_kernel": KERNEL_NAMES.get(kernel_ran, str(kernel_ran)),
+                   "work_order": {1: "grid", 2: "longest_first"}.get(order_ran, str(order_ran)),
                    "single_launch": bool(args.fused), "with_append": bool(args.append)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -91,6 +91,17 @@ enum {
     VK_KERNEL_MFMA_W4 = 5   /* matrix cores, 4 wave64s per workgroup (A/B tuning) */
 };
 
+/* Work order of the matrix-core decode; see vk_select_work_order. */
+enum {
+    VK_ORDER_AUTO = 0,           /* longest first when the split grid over <= 64
+                                    sequences takes more than one round of the
+                                    device's resident wave slots and pages hold
+                                    >= 16 tokens; else grid order */
+    VK_ORDER_GRID = 1,           /* (partition, KV head, sequence) in launch order */
+    VK_ORDER_LONGEST_FIRST = 2   /* split, <= 64 sequences: full partitions, then
+                                    ragged ones by decreasing length */
+};
+
 typedef struct vk_plan {
     int32_t  partition_size;     /* 0 = unsplit, else 256 or 512 */
     int32_t  max_num_partitions; /* NP = ceil(max_s L_s / P); 1 when unsplit */
@@ -101,6 +112,7 @@ typedef struct vk_plan {
     uint64_t scratch_bytes;      /* S * Hq * NP * (D + 2) * 4 */
     int32_t  grid[3];            /* decode: launch grid (partitions, Hkv, S) */
     int32_t  block;              /* decode: threads per workgroup */
+    int32_t  work_order;         /* decode: VK_ORDER_GRID or VK_ORDER_LONGEST_FIRST used */
 } vk_plan;
 
 /*
@@ -245,6 +257,16 @@ vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t
  * Returns the previous setting, or -1 for an unknown value (setting kept).
  */
 int32_t vk_select_decode_kernel(int32_t kernel);
+
+/*
+ * vk_select_work_order — A/B switch for the order in which this thread's
+ * later matrix-core decode launches hand out their (partition, KV head,
+ * sequence) items.  Longest first applies only to split launches over at most
+ * 64 sequences (others run in grid order whatever the setting); it changes
+ * which workgroup computes which partial, never a result.  Returns the
+ * previous setting, or -1 for an unknown value (setting kept).
+ */
+int32_t vk_select_work_order(int32_t order);
 
 /* Human-readable name of a status code (static storage). */
 const char* vk_status_string(vk_status s);

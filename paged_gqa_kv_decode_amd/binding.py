@@ -21,10 +21,11 @@ STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_S
                 5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP"}
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4 = 3, 4, 5
+ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
-            "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel", "vk_status_string",
-            "vk_last_hip_error", "vk_last_plan")
+            "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
+            "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan")
 
 
 class VkError(RuntimeError):
@@ -43,7 +44,7 @@ class _Plan(ctypes.Structure):
                 ("work_full_parts", ctypes.c_int64), ("budget", ctypes.c_int64),
                 ("cu_count", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("scratch_bytes", ctypes.c_uint64), ("grid", ctypes.c_int32 * 3),
-                ("block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("work_order", ctypes.c_int32)]
 
 
 @dataclass
@@ -57,11 +58,12 @@ class Plan:
     scratch_bytes: int
     grid: tuple
     block: int
+    work_order: int = 0
 
     @classmethod
     def from_c(cls, p: _Plan) -> "Plan":
         return cls(p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget,
-                   p.cu_count, p.kernel, p.scratch_bytes, tuple(p.grid), p.block)
+                   p.cu_count, p.kernel, p.scratch_bytes, tuple(p.grid), p.block, p.work_order)
 
 
 _lib = None
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_kv_append.restype = i32
     L.vk_select_decode_kernel.argtypes = [i32]
     L.vk_select_decode_kernel.restype = i32
+    L.vk_select_work_order.argtypes = [i32]
+    L.vk_select_work_order.restype = i32
     L.vk_status_string.argtypes = [i32]
     L.vk_status_string.restype = ctypes.c_char_p
     L.vk_last_hip_error.argtypes = []
@@ -119,6 +123,13 @@ def select_decode_kernel(kernel: int) -> int:
     prev = lib().vk_select_decode_kernel(int(kernel))
     if prev < 0:
         raise ValueError(f"unknown decode kernel {kernel}")
+    return prev
+
+
+def select_work_order(order: int) -> int:
+    prev = lib().vk_select_work_order(int(order))
+    if prev < 0:
+        raise ValueError(f"unknown work order {order}")
     return prev
 
 

@@ -51,6 +51,9 @@
 #ifndef VK_MFMA_WAVES_PER_EU
 #define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
 #endif
+#ifndef VK_MFMA_ORDER
+#define VK_MFMA_ORDER 1          // split launches of <= 64 sequences: longest-first work order
+#endif
 
 namespace vk {
 namespace {
@@ -464,7 +467,83 @@ struct MfmaKernel {
         }
     }
 
-    static __device__ void run(const DecodeArgs& a) { item(a, blockIdx.x, blockIdx.y, blockIdx.z); }
+    // Work order of a split launch over at most 64 sequences, used when the
+    // grid takes several rounds of the resident wave slots.  Workgroups
+    // start in linear-id order as slots free up, so the order of the items
+    // decides the tail: every full partition first, then the ragged last
+    // partitions by decreasing length (longest-first list scheduling); the
+    // ids past the last item (partitions past the end of a sequence) exit
+    // after one load.  Every wave derives the same mapping from the sequence
+    // lengths (lane j holds sequence j), without LDS or barriers.  Lengths
+    // are taken as the kernel guards them (<= 0: none; at most the table
+    // capacity and NP * P), so each partition index the guarded item code
+    // accepts is covered exactly once.  The single-launch form adds one
+    // item per (sequence, KV head) of length <= 0, whose output is zeros.
+    static __device__ __forceinline__ bool longest_first(const DecodeArgs& a, int& part, int& g,
+                                                         int& s) {
+        const int lane = threadIdx.x & 63;
+        const int S = a.num_seqs, Hkv = a.num_kv_heads, P = a.partition_size;
+        const int64_t k = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+        const int lim = min(a.max_blocks_per_seq * BS, a.max_num_partitions * P);
+        const int L = lane < S ? a.seq_lens[lane] : 0;
+        const int Le = min(max(L, 0), lim);
+        const int F = Le / P;       // full partitions of sequence `lane`
+        const int r = Le % P;       // tokens of its ragged last partition (0: none)
+        int pf = F;                 // inclusive prefix sum of F over the lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(pf, off);
+            if (lane >= off) pf += t;
+        }
+        const int64_t nfull = (int64_t)__shfl(pf, 63) * Hkv;
+        if (k < nfull) {
+            s = __ffsll((unsigned long long)__ballot((int64_t)pf * Hkv > k)) - 1;
+            const int Fs = __shfl(F, s);
+            const int64_t rem = k - (int64_t)(__shfl(pf, s) - Fs) * Hkv;
+            g = (int)(rem / Fs);
+            part = (int)(rem % Fs);
+            return true;
+        }
+        const bool ragged = lane < S && r > 0;
+        const unsigned long long rmask = __ballot(ragged);
+        const int64_t nrag = (int64_t)__popcll(rmask) * Hkv;
+        const int64_t q = k - nfull;
+        if (q >= nrag) {
+            if constexpr (FUSED) {
+                const unsigned long long zmask = __ballot(lane < S && Le == 0);
+                const int64_t qz = q - nrag;
+                if (qz >= (int64_t)__popcll(zmask) * Hkv) return false;
+                const int want = (int)(qz / Hkv);
+                const int idx = __popcll(zmask & ((1ull << lane) - 1ull));
+                s = __ffsll((unsigned long long)__ballot(((zmask >> lane) & 1ull) && idx == want)) - 1;
+                g = (int)(qz % Hkv);
+                part = 0;
+                return true;
+            }
+            return false;
+        }
+        // Rank of each ragged partition: longer first, ties by sequence.
+        int rank = 0;
+        for (int j = 0; j < S; ++j) {
+            const int rj = __builtin_amdgcn_readlane(r, j);
+            rank += (rj > r) || (rj == r && j < lane);
+        }
+        s = __ffsll((unsigned long long)__ballot(ragged && rank == (int)(q / Hkv))) - 1;
+        g = (int)(q % Hkv);
+        part = __shfl(F, s);
+        return true;
+    }
+
+    static __device__ void run(const DecodeArgs& a) {
+#if VK_MFMA_ORDER
+        if (a.work_order == 1) {
+            int part, g, s;
+            if (longest_first(a, part, g, s)) item(a, part, g, s);
+            return;
+        }
+#endif
+        item(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    }
 };
 
 // At least two resident waves per SIMD: caps a lane at 256 registers.

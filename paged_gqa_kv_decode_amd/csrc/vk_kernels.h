@@ -26,6 +26,7 @@ struct DecodeArgs {
     int32_t partition_size;       // 0 = unsplit
     int32_t max_num_partitions;
     float scale_log2e;            // scale * log2(e), rounded once to fp32
+    int32_t work_order;           // 0: grid order; 1: longest first (split, <= 64 sequences)
 };
 
 struct ReduceArgs {

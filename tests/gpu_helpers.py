@@ -41,7 +41,7 @@ def oracle_ref(orc, name):
 
 
 def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=False,
-            prefill_nan=True, cu_count=0, fused=False):
+            prefill_nan=True, cu_count=0, fused=False, order=None):
     """One decode step through libvkpaged (decode + reduce, or the single-launch
     form when `fused`).  Returns (out float64 numpy, plan, last launch plan,
     partials or None).  A fused split call must leave its counters at zero."""
@@ -52,6 +52,7 @@ def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=Fal
     out = torch.full((wl.num_seqs, wl.num_q_heads, wl.head_dim),
                      float("nan") if prefill_nan else 0.0, dtype=torch.float32, device="cuda")
     prev = vb.select_decode_kernel(kernel) if kernel is not None else None
+    prev_order = vb.select_work_order(order) if order is not None else None
     try:
         step = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, partition_request,
                              cu_count=cu_count, out=out, fused=fused)
@@ -65,6 +66,8 @@ def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=Fal
     finally:
         if prev is not None:
             vb.select_decode_kernel(prev)
+        if prev_order is not None:
+            vb.select_work_order(prev_order)
     if step.counters is not None:
         assert int(step.counters.abs().sum().item()) == 0, "counters not returned to zero"
     parts = None

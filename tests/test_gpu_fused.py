@@ -144,9 +144,10 @@ def test_fused_all_specialisations_ragged(orc, geom, bs, kernel):
         assert_parity(gpu, ref, f"fused {geom} bs{bs} P{P}")
 
 
+@pytest.mark.parametrize("order", [vb.ORDER_GRID, vb.ORDER_LONGEST_FIRST])
 @pytest.mark.parametrize("kernel", [vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
 @pytest.mark.parametrize("head_dim", [128, 256])
-def test_fused_device_side_guards(kernel, head_dim):
+def test_fused_device_side_guards(kernel, head_dim, order):
     """Lengths and page ids the host cannot see: L <= 0 gives zeros; a bad
     page id, a length beyond the page table or beyond NP * P gives NaN for
     that sequence only, in both the merged (several partitions) and the
@@ -171,12 +172,15 @@ def test_fused_device_side_guards(kernel, head_dim):
     es = torch.empty((S, 16, NP), device="cuda")
     to = torch.empty((S, 16, NP, D), device="cuda")
     prev = vb.select_decode_kernel(kernel)
+    prev_order = vb.select_work_order(order)
     try:
         vb.paged_gqa_decode_fused(q, k, v, bt_dev, sl_dev, wl.scale, P, NP, out, ml, es, to,
                                   counters)
         torch.cuda.synchronize()
+        assert vb.last_plan().work_order == order
     finally:
         vb.select_decode_kernel(prev)
+        vb.select_work_order(prev_order)
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o[0])) and np.all(np.isfinite(o[6]))
     assert np.all(o[1] == 0.0), "empty sequence must be zeros"

@@ -232,9 +232,10 @@ def test_all_specialisations_ragged(orc, geom, bs, kernel):
         assert_parity(gpu, ref, f"{geom} bs{bs} P{P}")
 
 
+@pytest.mark.parametrize("order", [vb.ORDER_GRID, vb.ORDER_LONGEST_FIRST])
 @pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
 @pytest.mark.parametrize("head_dim", [128, 256])
-def test_device_side_guards(kernel, head_dim):
+def test_device_side_guards(kernel, head_dim, order):
     """Values the host cannot validate: a length <= 0 gives zeros; a page id
     outside the pool or a length beyond the page table gives NaN for that
     sequence only, without reading out of bounds."""
@@ -248,6 +249,7 @@ def test_device_side_guards(kernel, head_dim):
     bt_h[2, 1] = wl.num_blocks + 5          # out of the pool
     bt_dev = torch.from_numpy(bt_h).cuda()
     prev = vb.select_decode_kernel(kernel)
+    prev_order = vb.select_work_order(order)
     for P in (0, 512):
         D = wl.head_dim
         out = torch.full((4, 16, D), 7.0, device="cuda")
@@ -267,6 +269,7 @@ def test_device_side_guards(kernel, head_dim):
         assert np.all(np.isnan(o[2])), f"P={P}: bad page id must poison its sequence"
         assert np.all(np.isnan(o[3])), f"P={P}: length beyond the page table must poison"
     vb.select_decode_kernel(prev)
+    vb.select_work_order(prev_order)
 
 
 def test_errors_on_real_tensors():
@@ -288,3 +291,32 @@ def test_last_plan_reports_launch():
     assert last.partition_size == 512 and last.max_num_partitions == plan.max_num_partitions
     assert tuple(last.grid) == (plan.max_num_partitions, wl.num_kv_heads, wl.num_seqs)
     assert last.block > 0
+
+
+WORK_LENS = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2100, 4097, 5000]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("kernel", [vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4])
+@pytest.mark.parametrize("geom,bs,S", [((24, 4, 256), 32, 32), ((16, 2, 128), 8, 64),
+                                       ((32, 8, 128), 16, 3)])
+def test_work_orders_bit_identical(orc, geom, bs, S, kernel, fused):
+    """Grid order and longest-first order hand the same (partition, KV head,
+    sequence) items to different workgroups: partials and outputs are
+    bit-identical (NaN-prefilled scratch shows a missed or extra partial),
+    and both match the oracle."""
+    Hq, Hkv, D = geom
+    lens = (WORK_LENS * 4)[:S]
+    wl = make_custom(seq_lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                     seed=Hq + D + bs + S, pool_factor=1.3, canaries=True, sigma_k=2.0)
+    ref = orc.paged_attention(wl)
+    for P in (256, 512):
+        a, _, la, pa = run_hip(wl, P, kernel=kernel, keep_partials=True, fused=fused,
+                               order=vb.ORDER_GRID)
+        b, _, lb, pb = run_hip(wl, P, kernel=kernel, keep_partials=True, fused=fused,
+                               order=vb.ORDER_LONGEST_FIRST)
+        assert la.work_order == vb.ORDER_GRID and lb.work_order == vb.ORDER_LONGEST_FIRST
+        assert np.array_equal(a, b)
+        for x, y in zip(pa, pb):
+            assert np.array_equal(x, y, equal_nan=True)
+        assert_parity(b, ref, f"{geom} S={S} P={P} longest-first")
