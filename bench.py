@@ -49,8 +49,9 @@ KERNEL_SOURCES = {
     3: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
     4: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
     5: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+    6: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
 }
-KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4"}
+KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4", 6: "mfma_w4p2"}
 
 
 def sources_sha(kernel: int) -> str:
@@ -203,7 +204,7 @@ def main():
                          "in [Lmin, Lmax], seeded; pages shuffled in an exact-fit pool)")
     ap.add_argument("--partition", type=int, default=None,
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4", "mfma4p2"])
     ap.add_argument("--order", default="auto", choices=["auto", "grid", "longest"],
                     help="work order of the matrix-core decode (A/B switch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -274,7 +275,7 @@ def main():
     P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
     kernel = {"auto": vb.KERNEL_AUTO, "dot": vb.KERNEL_DOT, "mfma": vb.KERNEL_MFMA,
               "mfma1": vb.KERNEL_MFMA_W1, "mfma2": vb.KERNEL_MFMA_W2,
-              "mfma4": vb.KERNEL_MFMA_W4}[args.kernel]
+              "mfma4": vb.KERNEL_MFMA_W4, "mfma4p2": vb.KERNEL_MFMA_W4P2}[args.kernel]
     vb.select_decode_kernel(kernel)
     vb.select_work_order({"auto": vb.ORDER_AUTO, "grid": vb.ORDER_GRID,
                           "longest": vb.ORDER_LONGEST_FIRST}[args.order])

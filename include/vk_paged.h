@@ -88,7 +88,10 @@ enum {
     VK_KERNEL_MFMA = 2,     /* matrix cores for QK and PV; waves per workgroup chosen */
     VK_KERNEL_MFMA_W1 = 3,  /* matrix cores, 1 wave64 per workgroup (A/B tuning) */
     VK_KERNEL_MFMA_W2 = 4,  /* matrix cores, 2 wave64s per workgroup (A/B tuning) */
-    VK_KERNEL_MFMA_W4 = 5   /* matrix cores, 4 wave64s per workgroup (A/B tuning) */
+    VK_KERNEL_MFMA_W4 = 5,  /* matrix cores, 4 wave64s per workgroup (A/B tuning) */
+    VK_KERNEL_MFMA_W4P2 = 6 /* matrix cores, 4 wave64s per workgroup over two
+                               consecutive partitions, two waves each (split
+                               launches; A/B tuning) */
 };
 
 /* Work order of the matrix-core decode; see vk_select_work_order. */
@@ -110,7 +113,8 @@ typedef struct vk_plan {
     int32_t  cu_count;           /* compute units the budget was sized for */
     int32_t  kernel;             /* decode: VK_KERNEL_DOT or VK_KERNEL_MFMA_W* that ran; planner: 0 */
     uint64_t scratch_bytes;      /* S * Hq * NP * (D + 2) * 4 */
-    int32_t  grid[3];            /* decode: launch grid (partitions, Hkv, S) */
+    int32_t  grid[3];            /* decode: launch grid (partitions, Hkv, S); partitions
+                                    halved (rounded up) for VK_KERNEL_MFMA_W4P2 */
     int32_t  block;              /* decode: threads per workgroup */
     int32_t  work_order;         /* decode: VK_ORDER_GRID or VK_ORDER_LONGEST_FIRST used */
 } vk_plan;

@@ -20,7 +20,7 @@ VK_OK = 0
 STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_SIZE",
                 5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP"}
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
-KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4 = 3, 4, 5
+KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4, KERNEL_MFMA_W4P2 = 3, 4, 5, 6
 ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",

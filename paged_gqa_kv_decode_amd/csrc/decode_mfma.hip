@@ -60,9 +60,13 @@ namespace {
 
 using namespace mfma;
 
-template <int D, int G, int BS, int W, int T, bool FUSED>
+template <int D, int G, int BS, int W, int WP, int T, bool FUSED>
 struct MfmaKernel {
     static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
+    // WP waves share one partition; a workgroup covers PPW = W / WP
+    // consecutive partitions (split launches only, not the single launch).
+    static constexpr int PPW = W / WP;
+    static_assert(W % WP == 0 && (PPW == 1 || !FUSED), "waves per partition");
     static constexpr int NT = T / 16;     // 16-token QK tiles per step
     static constexpr int NJ = T / 4;      // tokens per lane in the PV product
     static constexpr int NKC = D / 32;    // QK k-chunks of 32 dims
@@ -251,7 +255,7 @@ struct MfmaKernel {
     }
 
     static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const uint4 (&qb)[NKC],
-                                                int t_begin, int t_end, int g, int s, int wave,
+                                                int t_begin, int t_end, int g, int s, int wsub,
                                                 int lane, int i, int c, int pg_first, bool& bad) {
         const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
         for (int c0 = t_begin; c0 < t_end; c0 += CH) {
@@ -266,8 +270,8 @@ struct MfmaKernel {
                 }
             }
             // Full steps of this wave, then at most one partial step.
-            const int first = c0 + wave * T;
-            constexpr int stride = W * T;
+            const int first = c0 + wsub * T;
+            constexpr int stride = WP * T;
             const int nfull = (first + T <= c1) ? (c1 - T - first) / stride + 1 : 0;
             for (int k = 0; k < nfull; ++k) {
                 Buf b;
@@ -283,7 +287,9 @@ struct MfmaKernel {
         }
     }
 
-    static __device__ void item(const DecodeArgs& a, const int part, const int g, const int s) {
+    // Workgroup `unit` of (KV head g, sequence s): partitions
+    // [unit * PPW, unit * PPW + PPW), WP waves each.
+    static __device__ void item(const DecodeArgs& a, const int unit, const int g, const int s) {
         __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
         __shared__ float s_m[W][G];
         __shared__ float s_l[W][G];
@@ -291,6 +297,8 @@ struct MfmaKernel {
 
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int i = lane & 15, c = lane >> 4;
+        const int wsub = wave % WP;                     // this wave's index within its partition
+        const int part = unit * PPW + wave / WP;        // this wave's partition
         const int Hq = a.num_q_heads;
         const int P = a.partition_size, NP = a.max_num_partitions;
 
@@ -323,19 +331,22 @@ struct MfmaKernel {
             t_begin = part * P;
             t_end = min(L, t_begin + P);
             if (part == NP - 1 && L > t_begin + P) poison = true;  // beyond the grid
+            if (part >= NP) t_end = t_begin;   // a workgroup's spare partition slot
             nparts = L > 0 ? (int)min(((int64_t)L + P - 1) / P, (int64_t)NP) : 0;
         }
-        if (t_end <= t_begin) {
-            if (P == 0 || (FUSED && part == 0)) {  // empty sequence: zeros
-                float* o = a.out + ((int64_t)s * Hq + g * G) * D;
-                for (int k = tid; k < G * D; k += 64 * W) o[k] = 0.f;
+        const bool active = t_end > t_begin;
+        if constexpr (PPW == 1) {
+            if (!active) {
+                if (P == 0 || (FUSED && part == 0)) {  // empty sequence: zeros
+                    float* o = a.out + ((int64_t)s * Hq + g * G) * D;
+                    for (int k = tid; k < G * D; k += 64 * W) o[k] = 0.f;
+                }
+                return;  // split: partitions past the end write nothing
             }
-            return;  // split: partitions past the end write nothing
         }
         // Unsplit, or fused with a single partition: the normalised result
         // goes straight to `out`.
         const bool direct = (P == 0) || (FUSED && nparts == 1);
-
 
         State st;
 #pragma unroll
@@ -344,7 +355,9 @@ struct MfmaKernel {
         st.l = 0.f;
         bool bad = false;
 
-        scan(a, st, qb, t_begin, t_end, g, s, wave, lane, i, c, pg_first, bad);
+        // (With PPW > 1 the waves of an empty partition skip the scan but
+        // still meet the others at the barrier below.)
+        if (PPW == 1 || active) scan(a, st, qb, t_begin, t_end, g, s, wsub, lane, i, c, pg_first, bad);
 
         // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
         float lsum = st.l + __shfl_xor(st.l, 16);
@@ -391,30 +404,35 @@ struct MfmaKernel {
                     s_l[wave][i] = lsum;
                 }
             }
-            if (lane == 0) s_bad[wave] = wave_bad;
+            if (lane == 0) s_bad[wave] = wave_bad || poison;
             __syncthreads();
-            bool out_bad = poison;
+            for (int idx = tid; idx < PPW * G * D; idx += 64 * W) {
+                const int b = idx / (G * D), h = (idx / D) % G, d = idx % D;
+                const int pb = unit * PPW + b;        // partition of wave group b
+                if constexpr (PPW > 1) {
+                    if (pb >= NP || pb * P >= L) continue;   // empty slot: nothing written
+                }
+                const int w0 = b * WP;
+                bool out_bad = false;
 #pragma unroll
-            for (int w = 0; w < W; ++w) out_bad = out_bad || s_bad[w];
-            for (int idx = tid; idx < G * D; idx += 64 * W) {
-                const int h = idx / D, d = idx % D;
-                float M = s_m[0][h];
+                for (int w = 0; w < WP; ++w) out_bad = out_bad || s_bad[w0 + w];
+                float M = s_m[w0][h];
 #pragma unroll
-                for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+                for (int w = 1; w < WP; ++w) M = fmaxf(M, s_m[w0 + w][h]);
                 float num = 0.f, den = 0.f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    const float mw = s_m[w][h];
+                for (int w = 0; w < WP; ++w) {
+                    const float mw = s_m[w0 + w][h];
                     const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-                    num += sc * s_acc[w][h][d];
-                    den += sc * s_l[w][h];
+                    num += sc * s_acc[w0 + w][h][d];
+                    den += sc * s_l[w0 + w][h];
                 }
                 const float o = out_bad ? __builtin_nanf("") : num / den;
                 const int64_t r = row0 + h;
                 if (direct) {
                     a.out[r * D + d] = o;
                 } else {
-                    const int64_t pr = r * NP + part;
+                    const int64_t pr = r * NP + pb;
                     a.tmp_out[pr * D + d] = o;
                     if (d == 0) {
                         a.max_logits[pr] = M;
@@ -487,8 +505,9 @@ struct MfmaKernel {
         const int lim = min(a.max_blocks_per_seq * BS, a.max_num_partitions * P);
         const int L = lane < S ? a.seq_lens[lane] : 0;
         const int Le = min(max(L, 0), lim);
-        const int F = Le / P;       // full partitions of sequence `lane`
-        const int r = Le % P;       // tokens of its ragged last partition (0: none)
+        const int PU = P * PPW;     // tokens per workgroup unit
+        const int F = Le / PU;      // full units of sequence `lane`
+        const int r = Le % PU;      // tokens of its ragged last unit (0: none)
         int pf = F;                 // inclusive prefix sum of F over the lanes
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -547,32 +566,32 @@ struct MfmaKernel {
 };
 
 // At least two resident waves per SIMD: caps a lane at 256 registers.
-template <int D, int G, int BS, int W, bool FUSED>
+template <int D, int G, int BS, int W, int WP, bool FUSED>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(VK_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(DecodeArgs a) {
-    MfmaKernel<D, G, BS, W, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128), FUSED>::run(a);
+    MfmaKernel<D, G, BS, W, WP, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128), FUSED>::run(a);
 }
 
-template <int D, int G, int W, bool FUSED>
+template <int D, int G, int W, int WP, bool FUSED>
 hipError_t launch_bs(const DecodeArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
     *ok = true;
     const dim3 block(64 * W);
     switch (bs) {
-        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W, FUSED>), grid, block, 0, st, a); break;
-        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W, FUSED>), grid, block, 0, st, a); break;
-        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W, FUSED>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W, WP, FUSED>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W, WP, FUSED>), grid, block, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W, WP, FUSED>), grid, block, 0, st, a); break;
         default: *ok = false; return hipSuccess;
     }
     return hipGetLastError();
 }
 
-template <int W, bool FUSED>
+template <int W, int WP, bool FUSED>
 hipError_t launch_w(const DecodeArgs& a, int group, int head_dim, int bs, dim3 grid,
                     hipStream_t st, bool* ok) {
-    if (group == 4 && head_dim == 128) return launch_bs<128, 4, W, FUSED>(a, bs, grid, st, ok);
-    if (group == 6 && head_dim == 256) return launch_bs<256, 6, W, FUSED>(a, bs, grid, st, ok);
-    if (group == 8 && head_dim == 128) return launch_bs<128, 8, W, FUSED>(a, bs, grid, st, ok);
-    if (group == 8 && head_dim == 256) return launch_bs<256, 8, W, FUSED>(a, bs, grid, st, ok);
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4, W, WP, FUSED>(a, bs, grid, st, ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6, W, WP, FUSED>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8, W, WP, FUSED>(a, bs, grid, st, ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8, W, WP, FUSED>(a, bs, grid, st, ok);
     *ok = false;
     return hipSuccess;
 }
@@ -581,9 +600,9 @@ template <bool FUSED>
 hipError_t launch_waves(const DecodeArgs& a, int group, int head_dim, int block_size, int waves,
                         dim3 grid, hipStream_t stream, bool* geometry_ok) {
     switch (waves) {
-        case 1: return launch_w<1, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
-        case 2: return launch_w<2, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
-        case 4: return launch_w<4, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 1: return launch_w<1, 1, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 2: return launch_w<2, 2, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+        case 4: return launch_w<4, 4, FUSED>(a, group, head_dim, block_size, grid, stream, geometry_ok);
         default: *geometry_ok = false; return hipSuccess;
     }
 }
@@ -591,12 +610,29 @@ hipError_t launch_waves(const DecodeArgs& a, int group, int head_dim, int block_
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
-                              int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
-                              int* block) {
+                              int waves, int parts_per_wg, dim3 grid, hipStream_t stream,
+                              bool* geometry_ok, int* block) {
     *block = 64 * waves;
     // Split launches with a counter array merge their partitions in place.
-    if (a.counters != nullptr && a.partition_size > 0)
+    if (a.counters != nullptr && a.partition_size > 0) {
+        if (parts_per_wg != 1) {
+            *geometry_ok = false;
+            return hipSuccess;
+        }
         return launch_waves<true>(a, group, head_dim, block_size, waves, grid, stream, geometry_ok);
+    }
+    if (parts_per_wg == 2) {
+        // four waves over two consecutive partitions, two waves each (split only)
+        if (waves != 4 || a.partition_size == 0) {
+            *geometry_ok = false;
+            return hipSuccess;
+        }
+        return launch_w<4, 2, false>(a, group, head_dim, block_size, grid, stream, geometry_ok);
+    }
+    if (parts_per_wg != 1) {
+        *geometry_ok = false;
+        return hipSuccess;
+    }
     return launch_waves<false>(a, group, head_dim, block_size, waves, grid, stream, geometry_ok);
 }
 

@@ -98,7 +98,7 @@ vk_status vk_last_plan(vk_plan* out) {
 }
 
 int32_t vk_select_decode_kernel(int32_t kernel) {
-    if (kernel < VK_KERNEL_AUTO || kernel > VK_KERNEL_MFMA_W4) return -1;
+    if (kernel < VK_KERNEL_AUTO || kernel > VK_KERNEL_MFMA_W4P2) return -1;
     const int32_t prev = t_kernel_choice;
     t_kernel_choice = kernel;
     return prev;
@@ -236,17 +236,20 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
 
     const int group = num_q_heads / num_kv_heads;
-    const dim3 grid(partition_size == 0 ? 1u : (unsigned)max_num_partitions, (unsigned)num_kv_heads,
-                    (unsigned)num_seqs);
+    dim3 grid(partition_size == 0 ? 1u : (unsigned)max_num_partitions, (unsigned)num_kv_heads,
+              (unsigned)num_seqs);
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool ok = false;
     int block = 0;
     int32_t kernel = t_kernel_choice;
-    // The in-place merge exists only in the matrix-core family.
+    // The in-place merge exists only in the matrix-core family, one
+    // partition per workgroup; two partitions per workgroup need a split.
     if (fused && kernel == VK_KERNEL_DOT) kernel = VK_KERNEL_AUTO;
+    if (kernel == VK_KERNEL_MFMA_W4P2 && (fused || partition_size == 0)) kernel = VK_KERNEL_MFMA_W4;
     const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
     const int64_t slots = kernel == VK_KERNEL_DOT ? 0 : wave_slots();
-    if (kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA) {
+    const bool auto_waves = kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA;
+    if (auto_waves) {
         // Waves per workgroup from the grid size (measured on MI355X, 256
         // CUs = 2048 wave slots): small grids (few sequences or unsplit)
         // spread a workgroup's tokens over 4 waves; a grid that fills the
@@ -259,7 +262,8 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     if (kernel == VK_KERNEL_DOT) {
         e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
     } else {
-        const int waves = kernel == VK_KERNEL_MFMA_W1 ? 1 : kernel == VK_KERNEL_MFMA_W2 ? 2 : 4;
+        int waves = kernel == VK_KERNEL_MFMA_W1 ? 1 : kernel == VK_KERNEL_MFMA_W2 ? 2 : 4;
+        int parts_per_wg = kernel == VK_KERNEL_MFMA_W4P2 ? 2 : 1;
         // Longest-first work order when the split grid takes more than one
         // round of the wave slots, so the order decides the tail.  Measured on
         // MI355X at P = 512: 9-20% faster for 16-64 sequences of 2k-32k
@@ -269,7 +273,15 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         if (lf_ok && (t_order_choice == VK_ORDER_LONGEST_FIRST ||
                       (t_order_choice == VK_ORDER_AUTO && wgs * waves > slots && block_size >= 16)))
             a.work_order = 1;
-        e = vk::launch_decode_mfma(a, group, head_dim, block_size, waves, grid, st, &ok, &block);
+        // In longest-first order, waves of 8 steps (P / 128 waves per
+        // partition) balanced best: 4 waves at P = 512, 2 at P = 256.
+        if (auto_waves && a.work_order == 1) {
+            waves = partition_size / 128;
+            kernel = waves == 4 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W2;
+        }
+        if (parts_per_wg == 2) grid.x = (grid.x + 1) / 2;
+        e = vk::launch_decode_mfma(a, group, head_dim, block_size, waves, parts_per_wg, grid, st,
+                                   &ok, &block);
     }
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);

@@ -59,10 +59,11 @@ struct AppendArgs {
 // false when no specialisation exists for the shape (host code checks first).
 hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,
                              dim3 grid, hipStream_t stream, bool* geometry_ok, int* block);
-// waves: 1, 2 or 4 wave64s per workgroup.
+// waves: 1, 2 or 4 wave64s per workgroup; parts_per_wg: partitions per
+// workgroup (1, or 2 with 4 waves in a split launch: grid.x = ceil(NP / 2)).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
-                              int waves, dim3 grid, hipStream_t stream, bool* geometry_ok,
-                              int* block);
+                              int waves, int parts_per_wg, dim3 grid, hipStream_t stream,
+                              bool* geometry_ok, int* block);
 hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok);

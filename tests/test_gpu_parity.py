@@ -15,7 +15,8 @@ from paged_gqa_kv_decode_amd.workloads import make_custom, make_onehot_probe
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4]
+KERNELS = [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4,
+           vb.KERNEL_MFMA_W4P2]
 FAMILIES = [vb.KERNEL_DOT, vb.KERNEL_MFMA]
 
 NAMED = [("tiny_1x64", 0), ("batch8_2k", 512), ("long32_16k", 256), ("long32_16k", 512),
@@ -42,11 +43,15 @@ def test_named_workload_parity(orc, name, P, kernel):
     gpu, plan, last, _ = run_hip(wl, P, kernel=kernel)
     if P == -1:
         assert plan.partition_size == 512, "planner should pick 512 for 4 x 131072 tokens"
-    assert last.kernel == kernel
+    if kernel == vb.KERNEL_MFMA_W4P2 and plan.partition_size == 0:
+        assert last.kernel == vb.KERNEL_MFMA_W4    # two partitions per workgroup need a split
+    else:
+        assert last.kernel == kernel
     assert_parity(gpu, ref, f"{name} P={plan.partition_size}")
 
 
-@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4,
+                                    vb.KERNEL_MFMA_W4P2])
 @pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512), ("long32_16k", 256)])
 def test_partials_match_oracle(orc, name, P, kernel):
     say(f"[partials] {name} P={P} kernel={kernel}")
@@ -233,7 +238,8 @@ def test_all_specialisations_ragged(orc, geom, bs, kernel):
 
 
 @pytest.mark.parametrize("order", [vb.ORDER_GRID, vb.ORDER_LONGEST_FIRST])
-@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4])
+@pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4,
+                                    vb.KERNEL_MFMA_W4P2])
 @pytest.mark.parametrize("head_dim", [128, 256])
 def test_device_side_guards(kernel, head_dim, order):
     """Values the host cannot validate: a length <= 0 gives zeros; a page id
@@ -297,7 +303,8 @@ WORK_LENS = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2100
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("kernel", [vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4])
+@pytest.mark.parametrize("kernel", [vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W2, vb.KERNEL_MFMA_W4,
+                                    vb.KERNEL_MFMA_W4P2])
 @pytest.mark.parametrize("geom,bs,S", [((24, 4, 256), 32, 32), ((16, 2, 128), 8, 64),
                                        ((32, 8, 128), 16, 3)])
 def test_work_orders_bit_identical(orc, geom, bs, S, kernel, fused):
