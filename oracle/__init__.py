@@ -7,6 +7,8 @@ nothing from the GPU library.
   paged_attention(wl)      float64 [S, Hq, D]   (oracle.c)
   partials(wl, P, NP)      float64 m, l [S, Hq, NP], o [S, Hq, NP, D]
   merge(m, l, o, ...)      float64 [S, Hq, D]
+  paged_varlen_arrays(...) float64 [total_q, Hq, D]: several causal query
+                           tokens per sequence (oracle.c)
   plan(...)                the partition planner rule (planner.py)
 
 Inputs are the numpy arrays of a `Workload` (fp16 pools, int32 tables).
@@ -78,6 +80,9 @@ class Oracle:
         lib.oracle_partials.restype = i32
         lib.oracle_merge.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
         lib.oracle_merge.restype = None
+        lib.oracle_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_longlong, ctypes.c_double, P, i32]
+        lib.oracle_paged_varlen.restype = i32
         self.lib = lib
         self.path = path
 
@@ -101,6 +106,25 @@ class Oracle:
                                              _ptr(out), nthreads or default_threads())
         if st != 0:
             raise ValueError(f"oracle_paged_attention failed: {st}")
+        return out
+
+    def paged_varlen_arrays(self, q, k_cache, v_cache, block_tables, seq_lens, cu_q, scale,
+                            nthreads: int | None = None) -> np.ndarray:
+        """Causal attention of packed query rows q [total_q, Hq, D] (sequence s
+        owns rows cu_q[s] .. cu_q[s+1]-1, the last qlen_s of its L_s tokens)."""
+        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens)
+        cu = _c(cu_q, np.int32)
+        T, Hq, D = q.shape
+        nb, Hkv, bs, D2 = k.shape
+        S = sl.shape[0]
+        assert D2 == D and v.shape == k.shape and bt.shape[0] == S and cu.shape == (S + 1,)
+        assert int(cu[0]) == 0 and int(cu[-1]) == T and np.all(np.diff(cu) >= 0)
+        out = np.empty((T, Hq, D), dtype=np.float64)
+        st = self.lib.oracle_paged_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl),
+                                          _ptr(cu), S, Hq, Hkv, D, bs, bt.shape[1], nb,
+                                          float(scale), _ptr(out), nthreads or default_threads())
+        if st != 0:
+            raise ValueError(f"oracle_paged_varlen failed: {st}")
         return out
 
     def partials_arrays(self, q, k_cache, v_cache, block_tables, seq_lens, scale, P: int,
@@ -172,6 +196,10 @@ def partials(wl, P: int, NP: int | None = None, nthreads: int | None = None):
 
 def partials_arrays(*a, **kw):
     return default().partials_arrays(*a, **kw)
+
+
+def paged_varlen_arrays(*a, **kw) -> np.ndarray:
+    return default().paged_varlen_arrays(*a, **kw)
 
 
 def merge(m, l, o, seq_lens, P: int) -> np.ndarray:

@@ -30,6 +30,15 @@
  *    normalised by its own l_i.
  *  - Merge of partials: M = max m_i, w_i = l_i 2^(m_i - M),
  *    out = sum_i w_i o_i / sum_i w_i.
+ *  - Several query tokens per sequence (the vllm-metal page, section "什么是
+ *    Paged Attention", names a unified paged variable-length kernel for
+ *    prefill and speculative decoding; the pages give no formula, so the
+ *    plain causal reading is taken): sequence s contributes qlen_s =
+ *    cu_q[s+1] - cu_q[s] query rows, packed at rows cu_q[s] .. cu_q[s+1]-1;
+ *    its cache holds all L_s tokens, the new ones last, so query j sits at
+ *    position L_s - qlen_s + j and attends to the tokens t < L_s - qlen_s +
+ *    j + 1 (itself and everything before it).  A row with no such token is
+ *    zeros.
  *
  * fp16 values widen to double exactly (decoded from their bits below).
  * Build with -O2 -ffp-contract=off and no fast-math.
@@ -63,6 +72,7 @@ double oracle_half_to_double(uint16_t h)
 typedef struct {
     const uint16_t *q, *k, *v;
     const int32_t *block_tables, *seq_lens;
+    const int32_t *cu_q;            /* variable-length queries only: [S + 1] */
     int S, Hq, Hkv, D, bs, max_blocks;
     long long num_blocks;
     double scale;
@@ -80,13 +90,24 @@ static const uint16_t *row_ptr(const uint16_t *pool, long long block, int g, int
     return pool + (((block * Hkv + g) * (long long)bs + j) * (long long)D);
 }
 
-/* Scores z_t for t in [t0, t1) of row (s, h).  Returns 0, or -1 when a page
- * id is outside the pool. */
-static int scores(const job_t *J, int s, int h, int t0, int t1, double *z)
+/* Query vector of packed query row r, head h. */
+static const uint16_t *q_row(const job_t *J, long long r, int h)
+{
+    return J->q + (r * J->Hq + h) * J->D;
+}
+
+/* KV head read by query head h. */
+static int kv_head(const job_t *J, int h)
 {
     int G = J->Hq / J->Hkv;
     int g = h / G;
-    const uint16_t *qrow = J->q + ((long long)s * J->Hq + h) * J->D;
+    return g;
+}
+
+/* Scores z_t for t in [t0, t1) of query vector qrow against sequence s's keys
+ * of KV head g.  Returns 0, or -1 when a page id is outside the pool. */
+static int scores(const job_t *J, const uint16_t *qrow, int s, int g, int t0, int t1, double *z)
+{
     for (int t = t0; t < t1; ++t) {
         long long b = J->block_tables[(long long)s * J->max_blocks + t / J->bs];
         if (b < 0 || b >= J->num_blocks) return -1;
@@ -102,11 +123,9 @@ static int scores(const job_t *J, int s, int h, int t0, int t1, double *z)
 /* Softmax-weighted average of V over tokens [t0, t1) with scores z, relative
  * to the maximum score zmax.  Writes sum_t e_t v_t / sum_t e_t into res and
  * returns the exp-sum sum_t e_t (e_t = exp(z_t - zmax)). */
-static double weighted_v(const job_t *J, int s, int h, int t0, int t1, const double *z,
+static double weighted_v(const job_t *J, int s, int g, int t0, int t1, const double *z,
                          double zmax, double *acc, double *res)
 {
-    int G = J->Hq / J->Hkv;
-    int g = h / G;
     double sum = 0.0;
     for (int d = 0; d < J->D; ++d) acc[d] = 0.0;
     for (int t = t0; t < t1; ++t) {
@@ -137,10 +156,10 @@ static void *attention_worker(void *arg)
             for (int d = 0; d < J->D; ++d) dst[d] = 0.0;
             continue;
         }
-        if (scores(J, s, h, 0, L, z) != 0) { J->status = -1; break; }
+        if (scores(J, q_row(J, s, h), s, kv_head(J, h), 0, L, z) != 0) { J->status = -1; break; }
         double zmax = -INFINITY;            /* pass 1: the maximum score */
         for (int t = 0; t < L; ++t) if (z[t] > zmax) zmax = z[t];
-        weighted_v(J, s, h, 0, L, z, zmax, acc, dst);   /* pass 2 */
+        weighted_v(J, s, kv_head(J, h), 0, L, z, zmax, acc, dst);   /* pass 2 */
     }
     free(z);
     free(acc);
@@ -162,12 +181,54 @@ static void *partials_worker(void *arg)
         for (int i = 0; i < nparts && i < J->NP; ++i) {
             int t0 = i * J->P;
             int t1 = t0 + J->P < L ? t0 + J->P : L;
-            if (scores(J, s, h, t0, t1, z) != 0) { J->status = -1; goto done; }
+            if (scores(J, q_row(J, s, h), s, kv_head(J, h), t0, t1, z) != 0) { J->status = -1; goto done; }
             double zmax = -INFINITY;
             for (int t = t0; t < t1; ++t) if (z[t - t0] > zmax) zmax = z[t - t0];
             long long pi = r * J->NP + i;
-            J->l[pi] = weighted_v(J, s, h, t0, t1, z, zmax, acc, J->o + pi * J->D);
+            J->l[pi] = weighted_v(J, s, kv_head(J, h), t0, t1, z, zmax, acc, J->o + pi * J->D);
             J->m[pi] = ORACLE_LOG2E * zmax;
+        }
+    }
+done:
+    free(z);
+    free(acc);
+    return NULL;
+}
+
+/* Variable-length queries: rows are (packed query row, head); query row
+ * cu_q[s] + j of sequence s attends to the tokens before position
+ * L_s - qlen_s + j + 1. */
+static void *varlen_worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    int maxL = 0;
+    for (int s = 0; s < J->S; ++s) if (J->seq_lens[s] > maxL) maxL = J->seq_lens[s];
+    double *z = (double *)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)J->D);
+    if (!z || !acc) { J->status = -2; free(z); free(acc); return NULL; }
+    long long k = 0;                        /* running (row, head) index */
+    for (int s = 0; s < J->S; ++s) {
+        int L = J->seq_lens[s];
+        int qlen = J->cu_q[s + 1] - J->cu_q[s];
+        for (int j = 0; j < qlen; ++j) {
+            long long row = J->cu_q[s] + j;
+            int lim = L - qlen + j + 1;     /* tokens visible to this query */
+            if (lim > L) lim = L;
+            for (int h = 0; h < J->Hq; ++h, ++k) {
+                if (k % J->nthreads != J->tid) continue;
+                double *dst = J->out + (row * J->Hq + h) * J->D;
+                if (lim <= 0) {
+                    for (int d = 0; d < J->D; ++d) dst[d] = 0.0;
+                    continue;
+                }
+                if (scores(J, q_row(J, row, h), s, kv_head(J, h), 0, lim, z) != 0) {
+                    J->status = -1;
+                    goto done;
+                }
+                double zmax = -INFINITY;
+                for (int t = 0; t < lim; ++t) if (z[t] > zmax) zmax = z[t];
+                weighted_v(J, s, kv_head(J, h), 0, lim, z, zmax, acc, dst);
+            }
         }
     }
 done:
@@ -233,6 +294,24 @@ int oracle_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *
     J.num_blocks = num_blocks; J.scale = scale; J.P = P; J.NP = NP;
     J.m = m; J.l = l; J.o = o;
     return run_jobs(&J, nthreads, partials_worker);
+}
+
+/* out[total_q][Hq][D] for variable-length queries: sequence s has the query
+ * rows cu_q[s] .. cu_q[s+1]-1 (packed [total_q][Hq][D] fp16) and its cache
+ * holds L = seq_lens[s] tokens including them; row j attends causally (see
+ * the header).  Same return codes as oracle_paged_attention. */
+int oracle_paged_varlen(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                        const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_q,
+                        int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                        long long num_blocks, double scale, double *out, int nthreads)
+{
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q; J.k = k_cache; J.v = v_cache;
+    J.block_tables = block_tables; J.seq_lens = seq_lens; J.cu_q = cu_q;
+    J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
+    J.num_blocks = num_blocks; J.scale = scale; J.out = out;
+    return run_jobs(&J, nthreads, varlen_worker);
 }
 
 /* Merge per-partition triples of every (s, h) into out[S][Hq][D]. */

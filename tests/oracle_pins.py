@@ -321,6 +321,86 @@ def pin_golden(orc):
         _close(out, want, 1e-13, f"golden {name}")
 
 
+# ----------------------------------------------------------------------------
+# Several query tokens per sequence (causal, packed rows).
+# ----------------------------------------------------------------------------
+def varlen_case(seed, lens, qlens, Hq, Hkv, D, bs):
+    c = dense_case(seed, lens, Hq, Hkv, D, bs)
+    rng = np.random.default_rng(seed + 1000)
+    T = int(sum(qlens))
+    c["qv"] = rng.standard_normal((T, Hq, D), dtype=np.float32).astype(np.float16)
+    c["cu"] = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    c["qlens"] = list(qlens)
+    return c
+
+
+def run_varlen(orc, c):
+    return orc.paged_varlen_arrays(c["qv"], c["k_cache"], c["v_cache"], c["block_tables"],
+                                   c["seq_lens"], c["cu"], c["scale"])
+
+
+def sdpa_varlen(c):
+    """torch float64 SDPA per sequence with an explicit boolean mask: query j
+    of a sequence of L tokens whose last qlen are the queries sees the tokens
+    t <= L - qlen + j.  Rows that see no token are zeros."""
+    Hq, D = c["qv"].shape[1], c["qv"].shape[2]
+    G = Hq // c["Hkv"]
+    out = np.zeros((c["qv"].shape[0], Hq, D))
+    for s, (L, ql) in enumerate(zip(c["seq_lens"], c["qlens"])):
+        L, ql = int(L), int(ql)
+        if ql == 0:
+            continue
+        rows = c["qv"][c["cu"][s]:c["cu"][s + 1]].astype(np.float64)      # [ql, Hq, D]
+        qs = torch.from_numpy(rows.transpose(1, 0, 2).copy())              # [Hq, ql, D]
+        ks = torch.from_numpy(c["dk"][s].astype(np.float64)).repeat_interleave(G, 0)
+        vs = torch.from_numpy(c["dv"][s].astype(np.float64)).repeat_interleave(G, 0)
+        mask = torch.zeros((ql, L), dtype=torch.bool)
+        for j in range(ql):
+            mask[j, :max(0, L - ql + j + 1)] = True
+        o = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask,
+                                                             scale=c["scale"])
+        o = o.numpy().transpose(1, 0, 2)
+        for j in range(ql):
+            if L - ql + j + 1 > 0:
+                out[c["cu"][s] + j] = o[j]
+    return out
+
+
+VARLEN_CASES = [([40, 7, 100, 3], [5, 7, 1, 5], 8, 2, 16, 4),
+                ([33, 64, 1], [33, 16, 1], 24, 4, 8, 8)]
+
+
+def pin_varlen_sdpa(orc):
+    for i, (lens, qlens, Hq, Hkv, D, bs) in enumerate(VARLEN_CASES):
+        c = varlen_case(200 + i, lens, qlens, Hq, Hkv, D, bs)
+        got = run_varlen(orc, c)
+        _close(got, sdpa_varlen(c), 1e-12, f"varlen sdpa case {i}")
+
+
+def pin_varlen_rows_are_truncated_decodes(orc):
+    """Query row j of sequence s is a one-token decode over the first
+    L - qlen + j + 1 tokens of the same pages: same value to the last bit."""
+    c = varlen_case(211, [50, 9, 30], [6, 9, 2], 8, 2, 16, 4)
+    got = run_varlen(orc, c)
+    for s, (L, ql) in enumerate(zip(c["seq_lens"], c["qlens"])):
+        for j in range(ql):
+            lim = int(L) - ql + j + 1
+            row = c["cu"][s] + j
+            ref = orc.paged_attention_arrays(c["qv"][row:row + 1], c["k_cache"], c["v_cache"],
+                                             c["block_tables"][s:s + 1],
+                                             np.array([lim], dtype=np.int32), c["scale"])
+            assert np.array_equal(got[row], ref[0]), f"row {row} != decode over {lim} tokens"
+
+
+def pin_varlen_one_token_is_decode(orc):
+    c = varlen_case(221, [17, 1, 64], [1, 1, 1], 16, 2, 32, 8)
+    got = run_varlen(orc, c)
+    ref = orc.paged_attention_arrays(c["qv"], c["k_cache"], c["v_cache"], c["block_tables"],
+                                     c["seq_lens"], c["scale"])
+    assert np.array_equal(got, ref), "qlen = 1 must be the decode oracle"
+
+
 ALL_PINS = [pin_half_decode, pin_sdpa, pin_closed_forms, pin_large_scores, pin_permutation,
             pin_split_merge, pin_partials_closed, pin_merge_closed, pin_shift_invariance,
-            pin_gqa_to_mha, pin_onehot, pin_golden]
+            pin_gqa_to_mha, pin_onehot, pin_golden, pin_varlen_sdpa,
+            pin_varlen_rows_are_truncated_decodes, pin_varlen_one_token_is_decode]

@@ -14,7 +14,8 @@ MUTANTS = [
     ("page_index_shift", "[(long long)s * J->max_blocks + t / J->bs]",
      "[(long long)s * J->max_blocks + (t + 1) / J->bs]"),
     ("pool_head_swapped", "(((block * Hkv + g) *", "(((block * Hkv + (Hkv - 1 - g)) *"),
-    ("drops_last_token", "scores(J, s, h, 0, L, z)", "scores(J, s, h, 0, L - 1, z)"),
+    ("drops_last_token", "scores(J, q_row(J, s, h), s, kv_head(J, h), 0, L, z)",
+     "scores(J, q_row(J, s, h), s, kv_head(J, h), 0, L - 1, z)"),
     ("exp_sign", "exp(z[t - t0] - zmax)", "exp(zmax - z[t - t0])"),
     ("no_max_subtraction", "exp(z[t - t0] - zmax)", "exp(z[t - t0])"),
     ("scale_dropped", "z[t - t0] = J->scale * dot;", "z[t - t0] = dot;"),
@@ -26,6 +27,9 @@ MUTANTS = [
     ("merge_drops_l", "double w = l[r * NP + i] *", "double w = 1.0 *"),
     ("partition_tail_dropped", "int t1 = t0 + J->P < L ? t0 + J->P : L;",
      "int t1 = t0 + J->P < L ? t0 + J->P : L - 1;"),
+    ("varlen_causal_off_by_one", "int lim = L - qlen + j + 1;", "int lim = L - qlen + j;"),
+    ("varlen_not_causal", "int lim = L - qlen + j + 1;", "int lim = L;"),
+    ("varlen_row_offset", "long long row = J->cu_q[s] + j;", "long long row = J->cu_q[s] + qlen - 1 - j;"),
     ("dot_skips_last_dim", "for (int d = 0; d < J->D; ++d)\n            dot +=",
      "for (int d = 0; d < J->D - 1; ++d)\n            dot +="),
 ]
