@@ -43,7 +43,12 @@ DESCRIPTIONS = {
     "mixed64_32k": "64 seqs, mixed L (25% L=1, 25% 1-3 token tails, rest up to 32768), "
                    "(16q, 2kv, 128), block 8, P=512",
     "long4_128k": "4 seqs x 131072 tokens, (16q, 2kv, 256), block 32, pool 2x, planner",
+    "verify32_q4": "speculative-decode verification: 32 seqs, L uniform in [4096, 16384], "
+                   "4 query tokens each, (32q, 8kv, 128), block 16, planner",
+    "prefill4_chunk1k": "chunked prefill: 4 seqs, a 1024-token chunk on a context uniform in "
+                        "[1024, 8192], (24q, 4kv, 256), block 32, planner",
 }
+VARLEN = ("verify32_q4", "prefill4_chunk1k")
 KERNEL_SOURCES = {
     1: ["paged_gqa_kv_decode_amd/csrc/decode_dot.hip"],
     3: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
@@ -193,6 +198,142 @@ def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
             "seconds": round(total, 3)}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+
+
+def cpu_baseline_varlen(wl, min_seconds: float, max_seconds: float, flops_unit: bool):
+    """The float64 oracle on whole sequences of a multi-token workload, in
+    order and cycling, until at least `min_seconds` (bounded by `max_seconds`)."""
+    import numpy as np
+    import oracle
+    from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, varlen_pairs
+    nthreads = oracle.default_threads()
+    cu, ql = wl.meta["cu_q"], wl.meta["q_lens"]
+    done, total, runs, work = 0, 0.0, 0, 0.0
+    per = None
+    while total < min_seconds:
+        s = runs % wl.num_seqs
+        w = (4.0 * wl.head_dim * wl.num_q_heads * varlen_pairs(wl.seq_lens[s:s + 1], ql[s:s + 1])
+             if flops_unit else kv_read_bytes(wl.seq_lens[s:s + 1], wl.num_kv_heads, wl.head_dim))
+        if per is not None and total + per * w > max_seconds:
+            break
+        t = time.perf_counter()
+        oracle.paged_varlen_arrays(wl.q[cu[s]:cu[s + 1]], wl.k_cache, wl.v_cache,
+                                   wl.block_tables[s:s + 1], wl.seq_lens[s:s + 1],
+                                   np.array([0, ql[s]], dtype=np.int32), wl.scale,
+                                   nthreads=nthreads)
+        total += time.perf_counter() - t
+        runs += 1
+        done += int(ql[s])
+        work += w
+        per = total / work
+    value = work / total / (1e12 if flops_unit else 1e9)
+    return {"value": round(value, 6), "unit": "TFLOP/s" if flops_unit else "GB/s (KV-read)",
+            "cores": nthreads, "kind": "oracle",
+            "sample": f"{runs} single-sequence oracle calls cycling over the {wl.num_seqs} "
+                      f"sequences ({done} query rows, all {wl.num_q_heads} q heads), "
+                      f"{total:.2f} s wall",
+            "seconds": round(total, 3)}
+
+
+def bench_varlen(args, wl, gen_s):
+    """Several query tokens per sequence: plan (host) + the multi-token kernel
+    (+ its reduce when split) per step, pools rotated as for the decode."""
+    import numpy as np
+    import torch
+    from paged_gqa_kv_decode_amd import binding as vb
+    from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, varlen_pairs
+    P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
+    ql = wl.meta["q_lens"]
+    q = torch.from_numpy(wl.q).cuda()
+    k = torch.from_numpy(wl.k_cache).cuda()
+    v = torch.from_numpy(wl.v_cache).cuda()
+    bt = torch.from_numpy(wl.block_tables).cuda()
+    sl = torch.from_numpy(wl.seq_lens).cuda()
+    cu = torch.from_numpy(wl.meta["cu_q"]).cuda()
+    kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim)
+    flops = 4.0 * wl.head_dim * wl.num_q_heads * varlen_pairs(wl.seq_lens, ql)
+    ncopies = max(2, min(args.max_copies, -(-(4 * MALL_BYTES) // kv_bytes)))
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(ncopies - 1)]
+    stream = torch.cuda.current_stream()
+    step0 = vb.VarlenStep(q, k, v, bt, sl, cu, wl.seq_lens, ql, wl.scale, P_req)
+    P, NP, mq = step0.plan.partition_size, step0.plan.max_num_partitions, step0.max_q_len
+    counter = [0]
+
+    def one_step(ev=None):
+        kk, vv = pools[counter[0] % ncopies]
+        counter[0] += 1
+        plan = vb.plan_varlen(wl.seq_lens, ql, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                              wl.block_size, wl.max_blocks_per_seq, P_req)
+        assert plan.partition_size == P and plan.max_num_partitions == NP
+        if ev is not None:
+            ev[0].record(stream)
+        if P:
+            vb.paged_gqa_varlen(q, kk, vv, bt, sl, cu, mq, wl.scale, P, NP, None,
+                                step0.max_logits, step0.exp_sums, step0.tmp_out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            vb.paged_gqa_varlen_reduce(step0.max_logits, step0.exp_sums, step0.tmp_out, sl, cu,
+                                       mq, P, step0.out, stream)
+        else:
+            vb.paged_gqa_varlen(q, kk, vv, bt, sl, cu, mq, wl.scale, 0, 1, step0.out,
+                                stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t = time.perf_counter()
+    for i in range(args.steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ms = wall * 1e3 / args.steps
+    dec_s = float(dec_ms.mean()) * 1e-3
+    ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    compute_bound = flops / kv_bytes > ridge
+    if compute_bound:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": round(flops / dec_s / 1e12, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(flops / dec_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        value, unit = kv_bytes / (ms * 1e-3) / 1e9, "GB/s"
+        roof = {"bound": "hbm", "achieved": round(kv_bytes / dec_s / 1e9, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kv_bytes / dec_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+    result = {
+        "metric": "multi-token paged attention µs/step (" +
+                  ("causal attention TFLOP/s" if compute_bound else "KV-read HBM GB/s") + ")",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0, 1) fp16 K/V/q, shuffled pages)",
+        "config": {"workload": wl.name, "description": DESCRIPTIONS[wl.name],
+                   "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
+                   "total_q": int(ql.sum()), "max_q_len": mq, "partition_size": P,
+                   "max_num_partitions": NP, "decode_kernel": "varlen_w1"},
+        "roofline": roof,
+        "kernel_us": {"varlen_mean": round(float(dec_ms.mean()) * 1e3, 2),
+                      "varlen_median": round(float(np.median(dec_ms)) * 1e3, 2),
+                      "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)},
+        "kv_read_bytes": kv_bytes, "causal_flops": flops, "kv_pool_copies": ncopies,
+        "input_gen_s": round(gen_s, 1),
+    }
+    result["cpu_baseline"] = (None if args.no_cpu_baseline else
+                              cpu_baseline_varlen(wl, args.cpu_seconds, 3 * args.cpu_seconds,
+                                                  compute_bound))
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +410,10 @@ def main():
         args.workload = f"custom_{args.shape}"
         DESCRIPTIONS[args.workload] = (f"{S_} seqs, L uniform in [{lo_}, {hi_}], "
                                        f"({Hq_}q, {Hkv_}kv, {D_}), block {bs_}")
+    elif args.workload in VARLEN:
+        from paged_gqa_kv_decode_amd.workloads import make_varlen
+        wl = make_varlen(args.workload)
+        return bench_varlen(args, wl, time.time() - t0)
     else:
         wl = make_workload(args.workload)
     gen_s = time.time() - t0

@@ -227,6 +227,75 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
                                     float* tmp_out, uint32_t* counters, void* stream);
 
 /*
+ * vk_plan_varlen — plan a vk_paged_gqa_varlen call (host only; no HIP call
+ * when cu_count > 0).  seq_lens_host[s] (>= 1, within the page table) counts
+ * all of sequence s's cached tokens including its q_lens_host[s] new query
+ * tokens (0 <= q_len <= seq_len).  A column tile holds 16 / G query tokens of
+ * one KV head's G heads; with partition_request == -1 the call is unsplit
+ * when the tiles alone give one wave per wave slot (Hkv * sum ceil(q_len /
+ * (16/G)) >= 8 * cu_count), otherwise split at 512 when
+ * Hkv * sum ceil(q_len / (16/G)) * floor(L / 512) >= 33 * cu_count, else
+ * 256.  NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
+ * against the cap.  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
+ * q_len outside [0, seq_len]; VK_ERR_BAD_DIM if a q_len exceeds 65535.
+ */
+vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_host,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t partition_request, int32_t cu_count, uint64_t scratch_cap_bytes,
+                         vk_plan* plan_out);
+
+/*
+ * vk_paged_gqa_varlen — several query tokens per sequence, causal, over the
+ * paged cache: speculative-decode verification and chunked prefill (the
+ * vllm-metal kernels page, section "什么是 Paged Attention": a unified paged
+ * variable-length kernel serves prefill and speculative decoding).
+ *
+ *   q              fp16 [total_q, Hq, D], the query rows of all sequences
+ *                  packed in sequence order
+ *   cu_seqlens_q   int32 [num_seqs + 1], device: sequence s owns rows
+ *                  cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (non-decreasing,
+ *                  first 0, last total_q)
+ *   seq_lens       int32 [num_seqs], device: cached tokens of s, its new
+ *                  query tokens included (they are the last q_len of them,
+ *                  written beforehand, e.g. with vk_paged_kv_append)
+ *   max_q_len      host: the largest q_len (sets the grid; rows of a longer
+ *                  sequence would not be computed)
+ *   out            fp32 [total_q, Hq, D] (unsplit)
+ *   max_logits, exp_sums  fp32 [total_q, Hq, NP]; tmp_out fp32
+ *                  [total_q, Hq, NP, D] (split), as for vk_paged_gqa_decode
+ * Query j of sequence s attends to tokens t < L_s - q_len_s + j + 1 with the
+ * decode's scores and log2-space softmax; a row that sees no token is zeros.
+ * Split: partition i of row j is written for i < ceil((L - q_len + j + 1) / P)
+ * and merged by vk_paged_gqa_varlen_reduce on the same stream.  Geometries,
+ * block sizes, errors and device-side guards as for vk_paged_gqa_decode (a
+ * sequence longer than the page table gives NaN rows and reads nothing);
+ * VK_ERR_BAD_DIM for total_q or max_q_len outside [1, 65535] or max_q_len >
+ * total_q.
+ */
+vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                              int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, float* max_logits,
+                              float* exp_sums, float* tmp_out, void* stream);
+
+/*
+ * vk_paged_gqa_varlen_reduce — the merge of vk_paged_gqa_reduce for
+ * variable-length rows: row cu_seqlens_q[s] + j merges its
+ * n = min(ceil((L - q_len + j + 1) / P), NP) partitions into out
+ * [total_q, Hq, D]; a row that sees no token is zeros.
+ */
+vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_sums,
+                                     const float* tmp_out, const int32_t* seq_lens,
+                                     const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                     int32_t max_q_len, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t partition_size, int32_t max_num_partitions,
+                                     float* out, void* stream);
+
+/*
  * vk_paged_kv_append — write each sequence's new token into the paged cache
  * (vllm-metal kernels page, section "什么是 Paged Attention": the token at
  * position pos of sequence s lives in physical page block_tables[s][pos/bs],

@@ -25,7 +25,8 @@ ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
-            "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan")
+            "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
+            "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce")
 
 
 class VkError(RuntimeError):
@@ -88,6 +89,15 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_decode_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_decode_fused.restype = i32
+    L.vk_plan_varlen.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, u64,
+                                 ctypes.POINTER(_Plan)]
+    L.vk_plan_varlen.restype = i32
+    L.vk_paged_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      i32, i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
+    L.vk_paged_gqa_varlen.restype = i32
+    L.vk_paged_gqa_varlen_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                             vp, vp]
+    L.vk_paged_gqa_varlen_reduce.restype = i32
     L.vk_paged_gqa_reduce.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     L.vk_paged_gqa_reduce.restype = i32
     L.vk_paged_kv_append.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64,
@@ -259,6 +269,119 @@ def paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: in
                                      _ptr(seq_lens), S, Hq, D, int(partition_size), NP,
                                      _ptr(out), _stream_handle(stream))
     _check("vk_paged_gqa_reduce", code)
+
+
+def plan_varlen(seq_lens_host, q_lens_host, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, max_blocks_per_seq: int, partition_request: int = -1,
+                cu_count: int = 0, scratch_cap_bytes: int = 0) -> Plan:
+    sl = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    ql = np.ascontiguousarray(np.asarray(q_lens_host, dtype=np.int32))
+    if sl.shape != ql.shape:
+        raise ValueError("seq_lens and q_lens must have one entry per sequence")
+    p = _Plan()
+    code = lib().vk_plan_varlen(sl.ctypes.data if sl.size else None,
+                                ql.ctypes.data if ql.size else None, int(sl.size), num_q_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                partition_request, cu_count, scratch_cap_bytes, ctypes.byref(p))
+    _check("vk_plan_varlen", code)
+    return Plan.from_c(p)
+
+
+def paged_gqa_varlen(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, max_q_len: int,
+                     scale: float, partition_size: int, max_num_partitions: int, out=None,
+                     max_logits=None, exp_sums=None, tmp_out=None, stream=None) -> None:
+    """Enqueue the multi-token (causal, packed rows) kernel: q [total_q,Hq,D]
+    fp16, cu_seqlens_q [S+1] int32; out [total_q,Hq,D] fp32 (unsplit) or the
+    partials [total_q,Hq,NP(,D)] (split)."""
+    import torch
+    for t, dt, n in ((q, torch.float16, "q"), (k_cache, torch.float16, "k_cache"),
+                     (v_cache, torch.float16, "v_cache"), (block_tables, torch.int32, "block_tables"),
+                     (seq_lens, torch.int32, "seq_lens"), (cu_seqlens_q, torch.int32, "cu_seqlens_q"),
+                     (out, torch.float32, "out"), (max_logits, torch.float32, "max_logits"),
+                     (exp_sums, torch.float32, "exp_sums"), (tmp_out, torch.float32, "tmp_out")):
+        _need(t, dt, n)
+    T, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    S = seq_lens.shape[0]
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache / q shapes disagree")
+    if block_tables.shape[0] != S or tuple(cu_seqlens_q.shape) != (S + 1,):
+        raise ValueError("block_tables / cu_seqlens_q must match seq_lens")
+    if out is not None and tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must be [total_q, Hq, D]")
+    if partition_size:
+        for t, shp, n in ((max_logits, (T, Hq, max_num_partitions), "max_logits"),
+                          (exp_sums, (T, Hq, max_num_partitions), "exp_sums"),
+                          (tmp_out, (T, Hq, max_num_partitions, D), "tmp_out")):
+            if t is not None and tuple(t.shape) != shp:
+                raise ValueError(f"{n} must be {shp}")
+    code = lib().vk_paged_gqa_varlen(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(cu_seqlens_q), S, T, int(max_q_len), Hq, Hkv, D, bs, block_tables.shape[1], nb,
+        float(scale), int(partition_size), int(max_num_partitions), _ptr(out), _ptr(max_logits),
+        _ptr(exp_sums), _ptr(tmp_out), _stream_handle(stream))
+    _check("vk_paged_gqa_varlen", code)
+
+
+def paged_gqa_varlen_reduce(max_logits, exp_sums, tmp_out, seq_lens, cu_seqlens_q,
+                            max_q_len: int, partition_size: int, out, stream=None) -> None:
+    """Enqueue the merge of the multi-token partials into out [total_q,Hq,D]."""
+    import torch
+    for t, dt, n in ((max_logits, torch.float32, "max_logits"), (exp_sums, torch.float32, "exp_sums"),
+                     (tmp_out, torch.float32, "tmp_out"), (seq_lens, torch.int32, "seq_lens"),
+                     (cu_seqlens_q, torch.int32, "cu_seqlens_q"), (out, torch.float32, "out")):
+        _need(t, dt, n)
+    T, Hq, NP, D = tmp_out.shape
+    S = seq_lens.shape[0]
+    if tuple(max_logits.shape) != (T, Hq, NP) or tuple(exp_sums.shape) != (T, Hq, NP):
+        raise ValueError("partials shapes disagree")
+    if tuple(out.shape) != (T, Hq, D) or tuple(cu_seqlens_q.shape) != (S + 1,):
+        raise ValueError("out / cu_seqlens_q shapes disagree")
+    code = lib().vk_paged_gqa_varlen_reduce(_ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out),
+                                            _ptr(seq_lens), _ptr(cu_seqlens_q), S, int(max_q_len),
+                                            Hq, D, int(partition_size), NP, _ptr(out),
+                                            _stream_handle(stream))
+    _check("vk_paged_gqa_varlen_reduce", code)
+
+
+class VarlenStep:
+    """One multi-token step on device-resident inputs: plan once from the host
+    lengths, hold the scratch, `run()` enqueues the kernel (+ reduce if split)."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, seq_lens_host,
+                 q_lens_host, scale: float, partition_request: int = -1, cu_count: int = 0,
+                 out=None):
+        import torch
+        T, Hq, D = q.shape
+        nb, Hkv, bs, _ = k_cache.shape
+        self.plan = plan_varlen(seq_lens_host, q_lens_host, Hq, Hkv, D, bs, block_tables.shape[1],
+                                partition_request, cu_count)
+        self.max_q_len = int(max(1, int(np.max(q_lens_host))))
+        self.args = (q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q)
+        self.scale = float(scale)
+        dev = q.device
+        self.out = out if out is not None else torch.empty((T, Hq, D), dtype=torch.float32,
+                                                           device=dev)
+        P, NP = self.plan.partition_size, self.plan.max_num_partitions
+        if P:
+            self.max_logits = torch.empty((T, Hq, NP), dtype=torch.float32, device=dev)
+            self.exp_sums = torch.empty((T, Hq, NP), dtype=torch.float32, device=dev)
+            self.tmp_out = torch.empty((T, Hq, NP, D), dtype=torch.float32, device=dev)
+        else:
+            self.max_logits = self.exp_sums = self.tmp_out = None
+
+    def run(self, stream=None):
+        P, NP = self.plan.partition_size, self.plan.max_num_partitions
+        q, k, v, bt, sl, cu = self.args
+        if P:
+            paged_gqa_varlen(q, k, v, bt, sl, cu, self.max_q_len, self.scale, P, NP, None,
+                             self.max_logits, self.exp_sums, self.tmp_out, stream)
+            paged_gqa_varlen_reduce(self.max_logits, self.exp_sums, self.tmp_out, sl, cu,
+                                    self.max_q_len, P, self.out, stream)
+        else:
+            paged_gqa_varlen(q, k, v, bt, sl, cu, self.max_q_len, self.scale, 0, 1, self.out,
+                             stream=stream)
+        return self.out
 
 
 def paged_kv_append(k_new, v_new, block_tables, positions, k_cache, v_cache,

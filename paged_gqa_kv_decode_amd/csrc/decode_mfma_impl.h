@@ -1,0 +1,576 @@
+// The matrix-core decode's workgroup code (MfmaKernel) and its tuning knobs,
+// shared by the decode kernels (decode_mfma.hip) and the multi-token query
+// kernels (decode_varlen.hip), which reuse its K/V step loads and PV product.
+//
+// Paged GQA decode attention on the gfx950 matrix cores (VK_KERNEL_MFMA).
+//
+// Why matrix cores: with G query heads per KV head the path does G flops per
+// KV byte (4, 6 or 8).  With packed fp32 off, the VALU ridge is ~9.8 flop/B,
+// so a VALU kernel spends most of its issue slots on arithmetic.  Both
+// contractions of a KV-group step are small dense products:
+//   S[t, h]  = sum_d K[t, d] Q[h, d]      (16 tokens x 16 heads x D)
+//   O^T[d,h] += sum_t V^T[d, t] P^T[t, h]   (16 dims  x 16 heads x T tokens)
+// and one v_mfma_f32_16x16x32_f16 (16x16x16 for T = 16) does each block,
+// leaving the VALU only the softmax.  The G <= 8 heads fill half (or less) of
+// the 16 columns; the matrix cores are far from busy either way.
+//
+// Workgroup = W wave64s per (partition, KV head, sequence) (vllm-metal
+// kernels page, cf-1.com/news/5525226, section "Metal 并行模型": all query
+// heads of the group share one pass over the group's K/V pages).  Each wave
+// takes every W-th step of T tokens (T = 32 for D = 128; T = 16 for D = 256,
+// which keeps a lane under 256 registers).  Per step and lane l (i = l % 16,
+// c = l / 16), shown for T = 32:
+//  * K: two 16-token tiles; lane l loads token i (and 16 + i), dims
+//    [32 kk + 8 c, +8) for kk < D/32: 16-byte loads that are exactly the MFMA
+//    A operand.  The B operand is Q^T: head i, the same dims (zero for
+//    i >= G), held in registers for the whole partition.
+//  * The QK output tile gives lane l head i and tokens 4c + r (r < 4); the two
+//    tiles give 8 tokens per lane.  That is exactly the B operand (P^T) of the
+//    PV product when k-slot j of lane group c is token (j < 4 ? 4c + j :
+//    16 + 4c + j - 4), so P needs no data movement, only fp16 packing.
+//  * V: lane l loads its 8 tokens' dims [128 dh + 8 i, +8) (whole 256-byte
+//    half-rows per 16 lanes) and transposes the 8x8 fp16 block in registers
+//    with v_perm_b32 into the PV A operands: tile (dh, e) holds
+//    d = 128 dh + 8 i + e for row i.
+//  * Online softmax in log2 space (section "GQA 解码内核的四个提速技巧",
+//    item 1): per head, max over the 32 tokens (in-lane, then across the 4
+//    lane groups), one rescale of the accumulators per step, exp2 of
+//    x - max, per-lane partial exp-sums (summed once at the end).
+// Page ids: each wave holds up to 64 page ids of the current chunk in one
+// register (lane k = page k, one coalesced load) and reads the step's 1-4 ids
+// with readlane, so no dependent table load precedes each K/V load (item 2).
+// Tokens past the end are masked by select (zeroed K/V registers, score -inf).
+
+#pragma once
+
+#include "merge_ops.h"
+#include "mfma_ops.h"
+#include "vk_constants.h"
+#include "vk_kernels.h"
+
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef VK_MFMA_T128
+#define VK_MFMA_T128 16          // tokens per wave step, D = 128
+#endif
+#ifndef VK_MFMA_T256
+#define VK_MFMA_T256 16          // tokens per wave step, D = 256
+#endif
+#ifndef VK_MFMA_WAVES_PER_EU
+#define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
+#endif
+#ifndef VK_MFMA_ORDER
+#define VK_MFMA_ORDER 1          // split launches of <= 64 sequences: longest-first work order
+#endif
+
+namespace vk {
+namespace {
+
+using namespace mfma;
+
+template <int D, int G, int BS, int W, int WP, int T, bool FUSED>
+struct MfmaKernel {
+    static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
+    // WP waves share one partition; a workgroup covers PPW = W / WP
+    // consecutive partitions (split launches only, not the single launch).
+    static constexpr int PPW = W / WP;
+    static_assert(W % WP == 0 && (PPW == 1 || !FUSED), "waves per partition");
+    static constexpr int NT = T / 16;     // 16-token QK tiles per step
+    static constexpr int NJ = T / 4;      // tokens per lane in the PV product
+    static constexpr int NKC = D / 32;    // QK k-chunks of 32 dims
+    static constexpr int NDH = D / 128;   // 128-dim halves of a V row
+    static constexpr int NPT = D / 16;    // PV output tiles (16 dims each)
+    static constexpr int CHP = 64;        // page ids per chunk (one per lane)
+    static constexpr int CH = CHP * BS;   // tokens per chunk
+
+    struct State {
+        floatx4 acc[NPT];
+        float m, l;
+    };
+
+    // Page id of token `tok` (0..31 within the step) from the step's ids.
+    static __device__ __forceinline__ int page_of(int tok, const int (&pid)[T / BS < 1 ? 1 : T / BS]) {
+        if constexpr (BS >= T) {
+            return pid[0];
+        } else {
+            int p = pid[0];
+#pragma unroll
+            for (int k = 1; k < T / BS; ++k) p = (tok >= k * BS) ? pid[k] : p;
+            return p;
+        }
+    }
+
+    // K/V registers of one step.
+    struct Buf {
+        uint4 kr[NT][NKC];
+        uint4 vr[NDH][NJ];
+    };
+
+    // Page ids of the step at chunk offset `off`, read from the chunk's page
+    // list (lane k = page k) with readlane: wave-uniform, no memory access.
+    struct StepPages {
+        int pid[T / BS < 1 ? 1 : T / BS];
+        int off_slot;   // step start within its page (BS > T only)
+    };
+    static __device__ __forceinline__ StepPages step_pages(int pg, int off) {
+        StepPages sp;
+        const int k0 = off / BS;
+#pragma unroll
+        for (int k = 0; k < (T / BS < 1 ? 1 : T / BS); ++k)
+            sp.pid[k] = __builtin_amdgcn_readlane(pg, k0 + k);
+        sp.off_slot = off % BS;
+        return sp;
+    }
+
+    // Issue the K loads of a step (`remain` valid tokens when not FULL).
+    template <bool FULL>
+    static __device__ __forceinline__ void issue_k(const DecodeArgs& a, Buf& b, const StepPages& sp,
+                                                   int g, int remain, int i, int c) {
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const uint16_t* kbase = a.k + (int64_t)g * BS * D;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int tok = 16 * tt + i;
+            const bool ok = FULL || tok < remain;
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk)
+                b.kr[tt][kk] = ok ? load_stream(kp + 4 * kk + c) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // Issue the V loads of a step: this lane's NJ tokens, dims [128 dh + 8 i, +8).
+    template <bool FULL>
+    static __device__ __forceinline__ void issue_v(const DecodeArgs& a, Buf& b, const StepPages& sp,
+                                                   int g, int remain, int i, int c) {
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const uint16_t* vbase = a.v + (int64_t)g * BS * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int tok = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
+            const bool ok = FULL || tok < remain;
+            const uint4* vp = reinterpret_cast<const uint4*>(
+                vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh)
+                b.vr[dh][j] = ok ? load_stream(vp + 16 * dh + i) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    template <bool FULL>
+    static __device__ __forceinline__ void issue(const DecodeArgs& a, Buf& b, int pg, int g,
+                                                 int off, int remain, int i, int c) {
+        const StepPages sp = step_pages(pg, off);
+        issue_k<FULL>(a, b, sp, g, remain, i, c);
+        issue_v<FULL>(a, b, sp, g, remain, i, c);
+    }
+
+    // QK and the online-softmax update of one step; returns the fp16 weights
+    // packed as the PV B operand (x, y used for 16-token steps).
+    template <bool FULL>
+    static __device__ __forceinline__ uint4 qk_softmax(const DecodeArgs& a, State& st, const Buf& b,
+                                                       const uint4 (&qb)[NKC], int remain, int c) {
+        const auto& kr = b.kr;
+        // ---- S = K Q^T on the matrix cores ----
+        floatx4 sc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            sc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) sc[tt] = mfma32(kr[tt][kk], qb[kk], sc[tt]);
+        }
+
+        // ---- online softmax (log2 units) for head i, tokens of this lane ----
+        float x[NJ];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = mul_rounded(sc[tt][r], a.scale_log2e);
+                if (!FULL && (16 * tt + 4 * c + r) >= remain) v = -INFINITY;
+                x[4 * tt + r] = v;
+            }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2_fast(st.m - mref);
+        float p[NJ];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            p[j] = exp2_fast(x[j] - mref);
+            ps += p[j];
+        }
+        st.l = st.l * alpha + ps;
+        st.m = mnew;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
+        uint4 pb;
+        pb.x = pack_half2(p[0], p[1]);
+        pb.y = pack_half2(p[2], p[3]);
+        if constexpr (T == 32) {
+            pb.z = pack_half2(p[4], p[5]);
+            pb.w = pack_half2(p[6], p[7]);
+        } else {
+            pb.z = pb.w = 0;
+        }
+        return pb;
+    }
+
+    // ---- O^T += V^T P^T on the matrix cores ----
+    static __device__ __forceinline__ void pv(State& st, const Buf& b, const uint4& pb) {
+        const auto& vr = b.vr;
+        if constexpr (T == 32) {
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) {
+                st.acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
+                st.acc[dh * 8 + 1] = mfma32(vt_operand<1>(vr[dh]), pb, st.acc[dh * 8 + 1]);
+                st.acc[dh * 8 + 2] = mfma32(vt_operand<2>(vr[dh]), pb, st.acc[dh * 8 + 2]);
+                st.acc[dh * 8 + 3] = mfma32(vt_operand<3>(vr[dh]), pb, st.acc[dh * 8 + 3]);
+                st.acc[dh * 8 + 4] = mfma32(vt_operand<4>(vr[dh]), pb, st.acc[dh * 8 + 4]);
+                st.acc[dh * 8 + 5] = mfma32(vt_operand<5>(vr[dh]), pb, st.acc[dh * 8 + 5]);
+                st.acc[dh * 8 + 6] = mfma32(vt_operand<6>(vr[dh]), pb, st.acc[dh * 8 + 6]);
+                st.acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
+            }
+        } else {
+            const uint2 pb2 = make_uint2(pb.x, pb.y);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) {
+                st.acc[dh * 8 + 0] = mfma16(vt_operand4<0>(vr[dh]), pb2, st.acc[dh * 8 + 0]);
+                st.acc[dh * 8 + 1] = mfma16(vt_operand4<1>(vr[dh]), pb2, st.acc[dh * 8 + 1]);
+                st.acc[dh * 8 + 2] = mfma16(vt_operand4<2>(vr[dh]), pb2, st.acc[dh * 8 + 2]);
+                st.acc[dh * 8 + 3] = mfma16(vt_operand4<3>(vr[dh]), pb2, st.acc[dh * 8 + 3]);
+                st.acc[dh * 8 + 4] = mfma16(vt_operand4<4>(vr[dh]), pb2, st.acc[dh * 8 + 4]);
+                st.acc[dh * 8 + 5] = mfma16(vt_operand4<5>(vr[dh]), pb2, st.acc[dh * 8 + 5]);
+                st.acc[dh * 8 + 6] = mfma16(vt_operand4<6>(vr[dh]), pb2, st.acc[dh * 8 + 6]);
+                st.acc[dh * 8 + 7] = mfma16(vt_operand4<7>(vr[dh]), pb2, st.acc[dh * 8 + 7]);
+            }
+        }
+    }
+
+    template <bool FULL>
+    static __device__ __forceinline__ void compute(const DecodeArgs& a, State& st, const Buf& b,
+                                                   const uint4 (&qb)[NKC], int remain, int c) {
+        const uint4 pb = qk_softmax<FULL>(a, st, b, qb, remain, c);
+        pv(st, b, pb);
+    }
+
+    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const uint4 (&qb)[NKC],
+                                                int t_begin, int t_end, int g, int s, int wsub,
+                                                int lane, int i, int c, int pg_first, bool& bad) {
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+            const int c1 = min(t_end, c0 + CH);
+            const int np = (c1 - c0 + BS - 1) / BS;
+            int pg = 0;
+            if (lane < np) {
+                pg = (c0 == t_begin) ? pg_first : bt[c0 / BS + lane];
+                if (pg < 0 || (int64_t)pg >= a.num_blocks) {
+                    pg = 0;
+                    bad = true;
+                }
+            }
+            // Full steps of this wave, then at most one partial step.
+            const int first = c0 + wsub * T;
+            constexpr int stride = WP * T;
+            const int nfull = (first + T <= c1) ? (c1 - T - first) / stride + 1 : 0;
+            for (int k = 0; k < nfull; ++k) {
+                Buf b;
+                issue<true>(a, b, pg, g, first + k * stride - c0, T, i, c);
+                compute<true>(a, st, b, qb, T, c);
+            }
+            const int tl = first + nfull * stride;
+            if (tl < c1) {
+                Buf bl;
+                issue<false>(a, bl, pg, g, tl - c0, c1 - tl, i, c);
+                compute<false>(a, st, bl, qb, c1 - tl, c);
+            }
+        }
+    }
+
+    // Workgroup `unit` of (KV head g, sequence s): partitions
+    // [unit * PPW, unit * PPW + PPW), WP waves each.
+    static __device__ void item(const DecodeArgs& a, const int unit, const int g, const int s) {
+        __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
+        __shared__ float s_m[W][G];
+        __shared__ float s_l[W][G];
+        __shared__ int s_bad[W];
+
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int i = lane & 15, c = lane >> 4;
+        const int wsub = wave % WP;                     // this wave's index within its partition
+        const int part = unit * PPW + wave / WP;        // this wave's partition
+        const int Hq = a.num_q_heads;
+        const int P = a.partition_size, NP = a.max_num_partitions;
+
+        // Issue the independent loads together: the sequence length, the
+        // first chunk's page ids (its start does not depend on the length;
+        // the index is clamped into the table row and the ids are used only
+        // below ceil(L/bs)) and the query.  The first K/V loads then wait for
+        // one round trip, not for the length and then the table.
+        const int t_first = P > 0 ? part * P : 0;
+        const int32_t pg_first =
+            a.block_tables[(int64_t)s * a.max_blocks_per_seq +
+                           min(t_first / BS + lane, a.max_blocks_per_seq - 1)];
+        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
+        uint4 qb[NKC];
+        {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
+        int L = a.seq_lens[s];
+        bool poison = false;
+        const int cap = a.max_blocks_per_seq * BS;
+        if (L > cap) {
+            L = cap;
+            poison = true;
+        }
+        int t_begin = 0, t_end = L;
+        int nparts = 1;   // partitions of this sequence that write a result
+        if (P > 0) {
+            t_begin = part * P;
+            t_end = min(L, t_begin + P);
+            if (part == NP - 1 && L > t_begin + P) poison = true;  // beyond the grid
+            if (part >= NP) t_end = t_begin;   // a workgroup's spare partition slot
+            nparts = L > 0 ? (int)min(((int64_t)L + P - 1) / P, (int64_t)NP) : 0;
+        }
+        const bool active = t_end > t_begin;
+        if constexpr (PPW == 1) {
+            if (!active) {
+                if (P == 0 || (FUSED && part == 0)) {  // empty sequence: zeros
+                    float* o = a.out + ((int64_t)s * Hq + g * G) * D;
+                    for (int k = tid; k < G * D; k += 64 * W) o[k] = 0.f;
+                }
+                return;  // split: partitions past the end write nothing
+            }
+        }
+        // Unsplit, or fused with a single partition: the normalised result
+        // goes straight to `out`.
+        const bool direct = (P == 0) || (FUSED && nparts == 1);
+
+        State st;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.f;
+        bool bad = false;
+
+        // (With PPW > 1 the waves of an empty partition skip the scan but
+        // still meet the others at the barrier below.)
+        if (PPW == 1 || active) scan(a, st, qb, t_begin, t_end, g, s, wsub, lane, i, c, pg_first, bad);
+
+        // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
+        float lsum = st.l + __shfl_xor(st.l, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const bool wave_bad = __ballot(bad) != 0;
+
+        const int64_t row0 = (int64_t)s * Hq + g * G;   // first query head of the group
+        if constexpr (W == 1) {
+            const bool out_bad = poison || wave_bad;
+            if (i < G) {
+                const int64_t r = row0 + i;
+                float* dst;
+                if (direct) {
+                    dst = a.out + r * D;
+                } else {
+                    const int64_t pr = r * NP + part;
+                    dst = a.tmp_out + pr * D;
+                    if (c == 0) {
+                        a.max_logits[pr] = st.m;
+                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                    }
+                }
+#pragma unroll
+                for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int d = 128 * dh + 8 * (4 * c + rr) + e;
+                            dst[d] = out_bad ? __builtin_nanf("") : st.acc[dh * 8 + e][rr] / lsum;
+                        }
+            }
+        } else {
+            if (i < G) {
+#pragma unroll
+                for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            s_acc[wave][i][128 * dh + 8 * (4 * c + rr) + e] = st.acc[dh * 8 + e][rr];
+                if (c == 0) {
+                    s_m[wave][i] = st.m;
+                    s_l[wave][i] = lsum;
+                }
+            }
+            if (lane == 0) s_bad[wave] = wave_bad || poison;
+            __syncthreads();
+            for (int idx = tid; idx < PPW * G * D; idx += 64 * W) {
+                const int b = idx / (G * D), h = (idx / D) % G, d = idx % D;
+                const int pb = unit * PPW + b;        // partition of wave group b
+                if constexpr (PPW > 1) {
+                    if (pb >= NP || pb * P >= L) continue;   // empty slot: nothing written
+                }
+                const int w0 = b * WP;
+                bool out_bad = false;
+#pragma unroll
+                for (int w = 0; w < WP; ++w) out_bad = out_bad || s_bad[w0 + w];
+                float M = s_m[w0][h];
+#pragma unroll
+                for (int w = 1; w < WP; ++w) M = fmaxf(M, s_m[w0 + w][h]);
+                float num = 0.f, den = 0.f;
+#pragma unroll
+                for (int w = 0; w < WP; ++w) {
+                    const float mw = s_m[w0 + w][h];
+                    const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+                    num += sc * s_acc[w0 + w][h][d];
+                    den += sc * s_l[w0 + w][h];
+                }
+                const float o = out_bad ? __builtin_nanf("") : num / den;
+                const int64_t r = row0 + h;
+                if (direct) {
+                    a.out[r * D + d] = o;
+                } else {
+                    const int64_t pr = r * NP + pb;
+                    a.tmp_out[pr * D + d] = o;
+                    if (d == 0) {
+                        a.max_logits[pr] = M;
+                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : den;
+                    }
+                }
+            }
+        }
+        if constexpr (FUSED) {
+            if (!direct) merge_if_last(a, g, s, nparts, row0, tid);
+        }
+    }
+
+    // Single-launch split-KV: the workgroup that writes the last of the
+    // sequence's `n` partials for KV head g merges all of them into `out`
+    // with the reduce kernel's merge (merge_ops.h), one wave per 32 dims of a
+    // head.  Arrival is counted in counters[s * Hkv + g] with a device-scope
+    // atomic increment that wraps to zero at n - 1: the last arrival sees
+    // n - 1 and leaves the counter at zero for the next call.
+    // Ordering across XCDs (each has its own L2): every wave waits for its
+    // partial stores to be acknowledged, the barrier gathers the workgroup,
+    // then one lane releases at device scope (L2 write-back) before its
+    // increment; the last arrival acquires (L2 invalidate) before the
+    // barrier that lets its waves read the other partials.  One release per
+    // workgroup, one acquire per (sequence, KV head).
+    static __device__ void merge_if_last(const DecodeArgs& a, int g, int s, int n, int64_t row0,
+                                         int tid) {
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const unsigned old = atomicInc(a.counters + (int64_t)s * a.num_kv_heads + g, (unsigned)(n - 1));
+            const bool last = old == (unsigned)(n - 1);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        const int NP = a.max_num_partitions;
+        const int wave = tid >> 6, lane = tid & 63;
+        constexpr int kChunks = D / merge::kDims;
+        for (int it = wave; it < G * kChunks; it += W) {
+            const int h = it / kChunks, chunk = it % kChunks;
+            const int64_t r = row0 + h;
+            merge::merge_columns(a.max_logits + r * NP, a.exp_sums + r * NP,
+                                 reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * merge::kDims),
+                                 D / 4, n, lane,
+                                 reinterpret_cast<float4*>(a.out + r * D + chunk * merge::kDims));
+        }
+    }
+
+    // Work order of a split launch over at most 64 sequences, used when the
+    // grid takes several rounds of the resident wave slots.  Workgroups
+    // start in linear-id order as slots free up, so the order of the items
+    // decides the tail: every full partition first, then the ragged last
+    // partitions by decreasing length (longest-first list scheduling); the
+    // ids past the last item (partitions past the end of a sequence) exit
+    // after one load.  Every wave derives the same mapping from the sequence
+    // lengths (lane j holds sequence j), without LDS or barriers.  Lengths
+    // are taken as the kernel guards them (<= 0: none; at most the table
+    // capacity and NP * P), so each partition index the guarded item code
+    // accepts is covered exactly once.  The single-launch form adds one
+    // item per (sequence, KV head) of length <= 0, whose output is zeros.
+    static __device__ __forceinline__ bool longest_first(const DecodeArgs& a, int& part, int& g,
+                                                         int& s) {
+        const int lane = threadIdx.x & 63;
+        const int S = a.num_seqs, Hkv = a.num_kv_heads, P = a.partition_size;
+        const int64_t k = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+        const int lim = min(a.max_blocks_per_seq * BS, a.max_num_partitions * P);
+        const int L = lane < S ? a.seq_lens[lane] : 0;
+        const int Le = min(max(L, 0), lim);
+        const int PU = P * PPW;     // tokens per workgroup unit
+        const int F = Le / PU;      // full units of sequence `lane`
+        const int r = Le % PU;      // tokens of its ragged last unit (0: none)
+        int pf = F;                 // inclusive prefix sum of F over the lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(pf, off);
+            if (lane >= off) pf += t;
+        }
+        const int64_t nfull = (int64_t)__shfl(pf, 63) * Hkv;
+        if (k < nfull) {
+            s = __ffsll((unsigned long long)__ballot((int64_t)pf * Hkv > k)) - 1;
+            const int Fs = __shfl(F, s);
+            const int64_t rem = k - (int64_t)(__shfl(pf, s) - Fs) * Hkv;
+            g = (int)(rem / Fs);
+            part = (int)(rem % Fs);
+            return true;
+        }
+        const bool ragged = lane < S && r > 0;
+        const unsigned long long rmask = __ballot(ragged);
+        const int64_t nrag = (int64_t)__popcll(rmask) * Hkv;
+        const int64_t q = k - nfull;
+        if (q >= nrag) {
+            if constexpr (FUSED) {
+                const unsigned long long zmask = __ballot(lane < S && Le == 0);
+                const int64_t qz = q - nrag;
+                if (qz >= (int64_t)__popcll(zmask) * Hkv) return false;
+                const int want = (int)(qz / Hkv);
+                const int idx = __popcll(zmask & ((1ull << lane) - 1ull));
+                s = __ffsll((unsigned long long)__ballot(((zmask >> lane) & 1ull) && idx == want)) - 1;
+                g = (int)(qz % Hkv);
+                part = 0;
+                return true;
+            }
+            return false;
+        }
+        // Rank of each ragged partition: longer first, ties by sequence.
+        int rank = 0;
+        for (int j = 0; j < S; ++j) {
+            const int rj = __builtin_amdgcn_readlane(r, j);
+            rank += (rj > r) || (rj == r && j < lane);
+        }
+        s = __ffsll((unsigned long long)__ballot(ragged && rank == (int)(q / Hkv))) - 1;
+        g = (int)(q % Hkv);
+        part = __shfl(F, s);
+        return true;
+    }
+
+    static __device__ void run(const DecodeArgs& a) {
+#if VK_MFMA_ORDER
+        if (a.work_order == 1) {
+            int part, g, s;
+            if (longest_first(a, part, g, s)) item(a, part, g, s);
+            return;
+        }
+#endif
+        item(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    }
+};
+
+}  // namespace
+}  // namespace vk

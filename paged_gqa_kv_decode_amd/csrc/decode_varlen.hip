@@ -1,0 +1,220 @@
+// Several query tokens per sequence over the paged KV cache, causal, on the
+// gfx950 matrix cores: speculative-decode verification (a few draft tokens)
+// and chunked prefill (a chunk of new tokens) in one kernel (the vllm-metal
+// kernels page, cf-1.com/news/5525226, section "什么是 Paged Attention",
+// names a unified paged variable-length kernel for both).  Sequence s owns
+// the packed query rows cu_q[s] .. cu_q[s+1]-1; its cache already holds all
+// L tokens, the new ones last, so query j (position L - qlen + j) sees the
+// tokens t < L - qlen + j + 1.
+//
+// The decode kernel's matrix-core step is reused unchanged (MfmaKernel in
+// decode_mfma_impl.h: 16-token steps, K as the A operand, V transposed in
+// registers).  What changes is the meaning of the 16 MFMA columns: in the
+// decode they are the G heads of a KV group; here they are (query token,
+// head) pairs, 16 / G tokens x G heads per tile, so every K/V load of a step
+// serves that many queries.  Each column carries its own causal limit; the
+// scores past it are masked by select.  One wave per workgroup = one column
+// tile of one (sequence, KV head) over one partition of the keys (split-KV,
+// merged by the variable-length reduce) or over all of them (unsplit).
+#include "decode_mfma_impl.h"
+
+namespace vk {
+namespace {
+
+template <int D, int G, int BS>
+struct VarlenKernel {
+    using M = MfmaKernel<D, G, BS, 1, 1, 16, false>;
+    using Buf = typename M::Buf;
+    using State = typename M::State;
+    static constexpr int TPT = 16 / G;    // query tokens per column tile
+    static constexpr int NC = TPT * G;    // columns in use
+    static constexpr int NKC = M::NKC, NDH = M::NDH, NPT = M::NPT, CH = M::CH;
+
+    // QK of one 16-key step and the online-softmax update per column; `rem`
+    // is how many of the step's keys this lane's column may see (<= 0: none).
+    static __device__ __forceinline__ uint4 qk_softmax(const DecodeArgs& a, State& st, const Buf& b,
+                                                       const uint4 (&qb)[NKC], int rem, int c) {
+        floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKC; ++kk) sc = mfma32(b.kr[0][kk], qb[kk], sc);
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = mul_rounded(sc[r], a.scale_log2e);
+            x[r] = (4 * c + r) < rem ? v : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2_fast(st.m - mref);
+        float p[4];
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = exp2_fast(x[r] - mref);
+            ps += p[r];
+        }
+        st.l = st.l * alpha + ps;
+        st.m = mnew;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
+        uint4 pb;
+        pb.x = pack_half2(p[0], p[1]);
+        pb.y = pack_half2(p[2], p[3]);
+        pb.z = pb.w = 0;
+        return pb;
+    }
+
+    static __device__ void run(const VarlenArgs& va) {
+        const DecodeArgs& a = va.d;
+        const int lane = threadIdx.x, i = lane & 15, c = lane >> 4;
+        const int tile = (int)(blockIdx.x % (unsigned)va.tiles);
+        const int part = (int)(blockIdx.x / (unsigned)va.tiles);
+        const int g = blockIdx.y, s = blockIdx.z;
+        const int q0 = va.cu_q[s], qlen = va.cu_q[s + 1] - q0;
+        if (qlen <= 0 || tile * TPT >= qlen) return;
+        const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
+
+        // A length beyond the page table poisons the whole sequence: its rows
+        // that see keys become NaN and nothing of it is read.
+        const int L = a.seq_lens[s];
+        const bool poison = L > a.max_blocks_per_seq * BS;
+        // Column i: query token jt of the sequence, head h.
+        const int jt = tile * TPT + i / G;
+        const int h = g * G + i % G;
+        const bool valid = i < NC && jt < qlen;
+        const int lim = valid ? L - qlen + jt + 1 : 0;           // keys this column sees
+        int kv_end = lim;                                        // the wave's key range
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) kv_end = max(kv_end, __shfl_xor(kv_end, off));
+        int t_begin = 0, t_end = kv_end;
+        bool col_poison = false;
+        if (P > 0) {
+            t_begin = part * P;
+            t_end = min(kv_end, t_begin + P);
+            if (part == NP - 1 && lim > t_begin + P) col_poison = true;   // beyond the grid
+        }
+        const int64_t row = ((int64_t)q0 + jt) * Hq + h;
+        if (t_end <= t_begin || poison) {
+            if (valid && P == 0) {            // no visible key: zeros; poisoned: NaN
+                const float z = (poison && lim > 0) ? __builtin_nanf("") : 0.f;
+                float* o = a.out + row * D;
+                for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(z, z, z, z);
+            } else if (valid && poison && lim > t_begin) {   // the partials the reduce will read
+                const int64_t pr = row * NP + part;
+                if (c == 0) a.max_logits[pr] = a.exp_sums[pr] = __builtin_nanf("");
+                const float z = __builtin_nanf("");
+                float* o = a.tmp_out + pr * D;
+                for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(z, z, z, z);
+            }
+            return;
+        }
+        // The first chunk's page ids (clamped into the table row), then the
+        // query columns: one round trip before the first K/V loads.
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        const int32_t pg_first = bt[min(t_begin / BS + lane, a.max_blocks_per_seq - 1)];
+        uint4 qb[NKC];
+        {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + (valid ? row : 0) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) qb[kk] = valid ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+        }
+        const int e_lim = min(lim, t_end);   // this column's last visible key + 1 here
+
+        State st;
+#pragma unroll
+        for (int t = 0; t < NPT; ++t) st.acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.f;
+        bool bad = false;
+        for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+            const int c1 = min(t_end, c0 + CH);
+            const int np = (c1 - c0 + BS - 1) / BS;
+            int pg = 0;
+            if (lane < np) {
+                pg = (c0 == t_begin) ? pg_first : bt[c0 / BS + lane];
+                if (pg < 0 || (int64_t)pg >= a.num_blocks) {
+                    pg = 0;
+                    bad = true;
+                }
+            }
+            int t0 = c0;
+            for (; t0 + 16 <= c1; t0 += 16) {
+                Buf b;
+                M::template issue<true>(a, b, pg, g, t0 - c0, 16, i, c);
+                M::pv(st, b, qk_softmax(a, st, b, qb, e_lim - t0, c));
+            }
+            if (t0 < c1) {
+                Buf b;
+                M::template issue<false>(a, b, pg, g, t0 - c0, c1 - t0, i, c);
+                M::pv(st, b, qk_softmax(a, st, b, qb, min(e_lim, c1) - t0, c));
+            }
+        }
+        float lsum = st.l + __shfl_xor(st.l, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const bool out_bad = col_poison || __ballot(bad) != 0;
+        if (!valid) return;
+        if (P == 0 && lim <= 0) {   // a query that sees no key: zeros
+            float* o = a.out + row * D;
+            for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+            return;
+        }
+        if (lim <= t_begin) return;   // this column does not see this partition
+        float* dst;
+        if (P == 0) {
+            dst = a.out + row * D;
+        } else {
+            const int64_t pr = row * NP + part;
+            dst = a.tmp_out + pr * D;
+            if (c == 0) {
+                a.max_logits[pr] = st.m;
+                a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+            }
+        }
+#pragma unroll
+        for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int d = 128 * dh + 8 * (4 * c + rr) + e;
+                    dst[d] = out_bad ? __builtin_nanf("") : st.acc[dh * 8 + e][rr] / lsum;
+                }
+    }
+};
+
+template <int D, int G, int BS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(VK_MFMA_WAVES_PER_EU)))
+void decode_varlen_kernel(VarlenArgs a) {
+    VarlenKernel<D, G, BS>::run(a);
+}
+
+template <int D, int G>
+hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    *ok = true;
+    switch (bs) {
+        case 8: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 8>), grid, dim3(64), 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 16>), grid, dim3(64), 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 32>), grid, dim3(64), 0, st, a); break;
+        default: *ok = false; return hipSuccess;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int varlen_tokens_per_tile(int group) { return group > 0 && group <= 16 ? 16 / group : 0; }
+
+hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, int block_size,
+                                dim3 grid, hipStream_t stream, bool* geometry_ok) {
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, block_size, grid, stream, geometry_ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, block_size, grid, stream, geometry_ok);
+    *geometry_ok = false;
+    return hipSuccess;
+}
+
+}  // namespace vk

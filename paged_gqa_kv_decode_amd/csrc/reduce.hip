@@ -29,7 +29,49 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
                          D / 4, n, lane, dst);
 }
 
+// Variable-length rows: grid ((D / 32) * Hq, max_q_len, S); query j of
+// sequence s (row cu_q[s] + j) merges the partitions its causal range
+// [0, L - qlen + j + 1) covers; a row that sees no key is zeros.
+template <int D>
+__global__ __launch_bounds__(64) void reduce_varlen_kernel(ReduceArgs a, const int32_t* __restrict__ cu_q) {
+    constexpr int kChunks = D / merge::kDims;
+    const int chunk = blockIdx.x % kChunks, h = blockIdx.x / kChunks;
+    const int j = blockIdx.y, s = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int q0 = cu_q[s], qlen = cu_q[s + 1] - q0;
+    if (j >= qlen) return;
+    const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
+    const int64_t r = ((int64_t)q0 + j) * Hq + h;
+    const int lim = a.seq_lens[s] - qlen + j + 1;
+    float4* dst = reinterpret_cast<float4*>(a.out + r * D + chunk * merge::kDims);
+    if (lim <= 0) {
+        if (lane < merge::kCols) dst[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    const int n = (int)min(((int64_t)lim + P - 1) / P, (int64_t)NP);
+    merge::merge_columns(a.max_logits + r * NP, a.exp_sums + r * NP,
+                         reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * merge::kDims),
+                         D / 4, n, lane, dst);
+}
+
 }  // namespace
+
+hipError_t launch_reduce_varlen(const ReduceArgs& a, const int32_t* cu_q, int head_dim,
+                                int max_q_len, int num_seqs, hipStream_t stream,
+                                bool* geometry_ok) {
+    *geometry_ok = true;
+    const dim3 g((unsigned)(head_dim / merge::kDims * a.num_q_heads), (unsigned)max_q_len,
+                 (unsigned)num_seqs);
+    if (head_dim == 128) {
+        hipLaunchKernelGGL(reduce_varlen_kernel<128>, g, dim3(64), 0, stream, a, cu_q);
+    } else if (head_dim == 256) {
+        hipLaunchKernelGGL(reduce_varlen_kernel<256>, g, dim3(64), 0, stream, a, cu_q);
+    } else {
+        *geometry_ok = false;
+        return hipSuccess;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok) {

@@ -333,6 +333,187 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
                        counters, true, stream);
 }
 
+vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_host,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                         int32_t partition_request, int32_t cu_count, uint64_t scratch_cap_bytes,
+                         vk_plan* plan_out) {
+    if (!seq_lens_host || !q_lens_host || !plan_out) return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0) return VK_ERR_BAD_DIM;
+    vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
+    if (gs != VK_OK) return gs;
+    if (!block_size_ok(block_size)) return VK_ERR_BLOCK_SIZE;
+    if (partition_request != -1 && partition_request != 0 &&
+        partition_request != VK_PARTITION_SMALL && partition_request != VK_PARTITION_LARGE)
+        return VK_ERR_PARTITION;
+    if (cu_count < 0) return VK_ERR_BAD_DIM;
+    const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
+    if (cap_tokens > INT32_MAX) return VK_ERR_BAD_DIM;
+    const int tpt = vk::varlen_tokens_per_tile(num_q_heads / num_kv_heads);
+    int64_t max_len = 0, total_q = 0, tiles = 0, full512 = 0, full256 = 0, max_q = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t L = seq_lens_host[s], ql = q_lens_host[s];
+        if (L < 1 || L > cap_tokens) return VK_ERR_SEQ_LEN;
+        if (ql < 0 || ql > L) return VK_ERR_SEQ_LEN;
+        if (L > max_len) max_len = L;
+        if (ql > max_q) max_q = ql;
+        total_q += ql;
+        const int64_t t = (ql + tpt - 1) / tpt;
+        tiles += t;
+        full512 += t * (L / VK_PARTITION_LARGE);
+        full256 += t * (L / VK_PARTITION_SMALL);
+    }
+    if (max_q > 65535 || total_q > INT32_MAX) return VK_ERR_BAD_DIM;
+    if (cu_count == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e);
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        cu_count = n;
+    }
+    const uint64_t cap = scratch_cap_bytes > 0 ? scratch_cap_bytes : VK_DEFAULT_SCRATCH_CAP;
+    vk_plan p = {};
+    p.cu_count = cu_count;
+    p.budget = (int64_t)VK_DEFAULT_BUDGET_PER_CU * cu_count;
+    int32_t P = partition_request;
+    if (P == -1) {
+        // One wave per (column tile, KV head) when unsplit: enough of them to
+        // fill the wave slots once (8 per CU) needs no split; otherwise the
+        // decode's rule over (tile, full partition) units.
+        if ((int64_t)num_kv_heads * tiles >= 8 * (int64_t)cu_count)
+            P = 0;
+        else
+            P = ((int64_t)num_kv_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
+    }
+    p.partition_size = P;
+    if (P == 0) {
+        p.max_num_partitions = 1;
+        p.work_full_parts = (int64_t)num_kv_heads * tiles;
+    } else {
+        p.max_num_partitions = (int32_t)((max_len + P - 1) / P);
+        p.work_full_parts = (int64_t)num_kv_heads * (P == VK_PARTITION_LARGE ? full512 : full256);
+        p.scratch_bytes = (uint64_t)total_q * (uint64_t)num_q_heads *
+                          (uint64_t)p.max_num_partitions * (uint64_t)(head_dim + 2) * 4u;
+        if (p.scratch_bytes > cap) return VK_ERR_SCRATCH_CAP;
+    }
+    *plan_out = p;
+    t_last_plan = p;
+    return VK_OK;
+}
+
+vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                              int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, float* max_logits,
+                              float* exp_sums, float* tmp_out, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q)
+        return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+        total_q <= 0 || max_q_len <= 0 || max_q_len > 65535 || max_q_len > total_q)
+        return VK_ERR_BAD_DIM;
+    vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
+    if (gs != VK_OK) return gs;
+    if (!block_size_ok(block_size)) return VK_ERR_BLOCK_SIZE;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return VK_ERR_BAD_DIM;
+    if (!std::isfinite(scale)) return VK_ERR_BAD_DIM;
+    if (partition_size == 0) {
+        if (!out) return VK_ERR_NULL_ARG;
+        if (max_num_partitions != 1) return VK_ERR_PARTITION;
+    } else if (partition_size == VK_PARTITION_SMALL || partition_size == VK_PARTITION_LARGE) {
+        if (!max_logits || !exp_sums || !tmp_out) return VK_ERR_NULL_ARG;
+        if (max_num_partitions < 1) return VK_ERR_PARTITION;
+        if ((int64_t)max_num_partitions * partition_size > (int64_t)INT32_MAX) return VK_ERR_PARTITION;
+    } else {
+        return VK_ERR_PARTITION;
+    }
+    const int group = num_q_heads / num_kv_heads;
+    const int tpt = vk::varlen_tokens_per_tile(group);
+    const int64_t tiles = (max_q_len + tpt - 1) / tpt;
+    const int64_t gx = tiles * (partition_size == 0 ? 1 : max_num_partitions);
+    if (gx > INT32_MAX) return VK_ERR_BAD_DIM;
+
+    vk::VarlenArgs va = {};
+    vk::DecodeArgs& a = va.d;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.counters = nullptr;
+    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.num_seqs = num_seqs;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
+    a.work_order = 0;
+    va.cu_q = cu_seqlens_q;
+    va.tiles = (int32_t)tiles;
+    const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);
+    bool ok = false;
+    hipError_t e = vk::launch_decode_varlen(va, group, head_dim, block_size, grid,
+                                            static_cast<hipStream_t>(stream), &ok);
+    if (!ok) return VK_ERR_GEOMETRY;
+    if (e != hipSuccess) return hip_fail(e);
+    vk_plan p = {};
+    p.partition_size = partition_size;
+    p.max_num_partitions = max_num_partitions;
+    p.kernel = VK_KERNEL_MFMA_W1;
+    p.scratch_bytes = partition_size == 0 ? 0
+                      : (uint64_t)total_q * num_q_heads * (uint64_t)max_num_partitions *
+                            (uint64_t)(head_dim + 2) * 4u;
+    p.grid[0] = (int32_t)grid.x;
+    p.grid[1] = (int32_t)grid.y;
+    p.grid[2] = (int32_t)grid.z;
+    p.block = 64;
+    p.work_order = VK_ORDER_GRID;
+    t_last_plan = p;
+    return VK_OK;
+}
+
+vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_sums,
+                                     const float* tmp_out, const int32_t* seq_lens,
+                                     const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                     int32_t max_q_len, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t partition_size, int32_t max_num_partitions,
+                                     float* out, void* stream) {
+    if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !cu_seqlens_q || !out)
+        return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_seqs > 65535 || num_q_heads <= 0 || num_q_heads > 256 ||
+        max_q_len <= 0 || max_q_len > 65535)
+        return VK_ERR_BAD_DIM;
+    if (head_dim != 128 && head_dim != 256) return VK_ERR_GEOMETRY;
+    if (partition_size != VK_PARTITION_SMALL && partition_size != VK_PARTITION_LARGE)
+        return VK_ERR_PARTITION;
+    if (max_num_partitions < 1) return VK_ERR_PARTITION;
+    vk::ReduceArgs a;
+    a.max_logits = max_logits;
+    a.exp_sums = exp_sums;
+    a.tmp_out = tmp_out;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.num_q_heads = num_q_heads;
+    a.partition_size = partition_size;
+    a.max_num_partitions = max_num_partitions;
+    bool ok = false;
+    hipError_t e = vk::launch_reduce_varlen(a, cu_seqlens_q, head_dim, max_q_len, num_seqs,
+                                            static_cast<hipStream_t>(stream), &ok);
+    if (!ok) return VK_ERR_GEOMETRY;
+    if (e != hipSuccess) return hip_fail(e);
+    return VK_OK;
+}
+
 vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t* block_tables,
                              const int32_t* positions, int32_t num_seqs, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,

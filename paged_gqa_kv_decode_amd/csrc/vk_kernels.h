@@ -29,6 +29,15 @@ struct DecodeArgs {
     int32_t work_order;           // 0: grid order; 1: longest first (split, <= 64 sequences)
 };
 
+// Several query tokens per sequence (causal): `d` as for the decode, with
+// d.q the packed query rows [total_q, Hq, D], d.out [total_q, Hq, D] and the
+// partials [total_q, Hq, NP(, D)]; sequence s owns rows cu_q[s] .. cu_q[s+1]-1.
+struct VarlenArgs {
+    DecodeArgs d;
+    const int32_t* cu_q;          // [S + 1]
+    int32_t tiles;                // column tiles per (sequence, KV head): grid.x = tiles * NP
+};
+
 struct ReduceArgs {
     const float* max_logits;
     const float* exp_sums;
@@ -64,8 +73,17 @@ hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int b
 hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
                               int waves, int parts_per_wg, dim3 grid, hipStream_t stream,
                               bool* geometry_ok, int* block);
+// One wave per workgroup; grid (tiles * max(NP, 1), Hkv, S).  tokens_per_tile
+// receives 16 / G (query tokens per 16-column tile) for the caller's grid.
+hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, int block_size,
+                                dim3 grid, hipStream_t stream, bool* geometry_ok);
+int varlen_tokens_per_tile(int group);
 hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok);
+// Variable-length rows: grid (Hq, max_q_len, S) before the split into 32-dim chunks.
+hipError_t launch_reduce_varlen(const ReduceArgs& a, const int32_t* cu_q, int head_dim,
+                                int max_q_len, int num_seqs, hipStream_t stream,
+                                bool* geometry_ok);
 
 }  // namespace vk

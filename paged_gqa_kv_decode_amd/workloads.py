@@ -37,6 +37,10 @@ __all__ = [
     "make_custom",
     "make_onehot_probe",
     "kv_read_bytes",
+    "VARLEN_WORKLOADS",
+    "make_varlen",
+    "make_varlen_custom",
+    "varlen_pairs",
 ]
 
 
@@ -297,3 +301,66 @@ def make_onehot_probe(base: Workload, seed: int, amplitude: float | None = None)
                   q=q, k_cache=k, v_cache=v, scale=base.scale,
                   partition_sizes=base.partition_sizes)
     return wl, targets
+
+
+# ----------------------------------------------------------------------------
+# Several query tokens per sequence (speculative-decode verification, chunked
+# prefill).  The cache holds L tokens per sequence, the last q_len of them the
+# new ones; q is packed [total_q, Hq, D] with cu_q [S + 1] row offsets.
+# ----------------------------------------------------------------------------
+VARLEN_WORKLOADS = {
+    # 32 seqs, (32q, 8kv, 128), bs 16, L uniform in [4096, 16384], 4 query
+    # tokens each (3 drafted + 1).
+    "verify32_q4": dict(index=6, S=32, Hq=32, Hkv=8, D=128, bs=16, L=(4096, 16384), q=(4, 4)),
+    # 4 seqs, (24q, 4kv, 256), bs 32, a 1024-token chunk on a context uniform
+    # in [1024, 8192] (L = context + 1024).
+    "prefill4_chunk1k": dict(index=7, S=4, Hq=24, Hkv=4, D=256, bs=32, ctx=(1024, 8192), q=(1024, 1024)),
+}
+
+
+def varlen_pairs(seq_lens, q_lens) -> int:
+    """(query, key) pairs of a causal varlen batch: sum over rows of the keys
+    each query sees."""
+    n = 0
+    for L, ql in zip(seq_lens, q_lens):
+        L, ql = int(L), int(ql)
+        for j in range(ql):
+            n += max(0, L - ql + j + 1)
+    return n
+
+
+def make_varlen_custom(*, seq_lens, q_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       block_size: int, seed: int, pool_factor: float = 1.0,
+                       sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0,
+                       canaries: bool = False, extra_blocks_per_seq: int = 0,
+                       name: str = "varlen") -> Workload:
+    """A seeded cache as make_custom builds it, with packed query rows: q is
+    [sum q_lens, Hq, D]; meta holds cu_q (int32 [S + 1]) and q_lens."""
+    wl = make_custom(seq_lens=seq_lens, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                     head_dim=head_dim, block_size=block_size, seed=seed,
+                     pool_factor=pool_factor, sigma_q=sigma_q, sigma_k=sigma_k, sigma_v=sigma_v,
+                     canaries=canaries, extra_blocks_per_seq=extra_blocks_per_seq, name=name)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    r_q = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(5)[4]))
+    total = int(q_lens.sum())
+    wl.q = _draw_fp16(r_q, (total, num_q_heads, head_dim), sigma_q)
+    wl.meta["cu_q"] = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    wl.meta["q_lens"] = q_lens
+    return wl
+
+
+def make_varlen(name: str, *, canaries: bool = False) -> Workload:
+    """Build one named variable-length workload deterministically."""
+    spec = VARLEN_WORKLOADS[name]
+    i, S = spec["index"], spec["S"]
+    r_len = _rngs(i)[0]
+    q_lens = r_len.integers(spec["q"][0], spec["q"][1], size=S, endpoint=True)
+    if "L" in spec:
+        lens = r_len.integers(spec["L"][0], spec["L"][1], size=S, endpoint=True)
+    else:
+        lens = r_len.integers(spec["ctx"][0], spec["ctx"][1], size=S, endpoint=True) + q_lens
+    wl = make_varlen_custom(seq_lens=lens, q_lens=q_lens, num_q_heads=spec["Hq"],
+                            num_kv_heads=spec["Hkv"], head_dim=spec["D"], block_size=spec["bs"],
+                            seed=1000 + i, canaries=canaries, name=name)
+    wl.partition_sizes = (-1,)
+    return wl

@@ -171,3 +171,55 @@ def test_reduce_validation():
 def test_planner_device_query_without_gpu_is_hip_error():
     code = _c_plan([100], 32, 8, 128, 16, 8, -1, 0)
     assert code == "HIP"
+
+
+# ----------------------------------------------------------------------------
+# vk_plan_varlen: hand-computed decisions (host only; cu_count given).
+# ----------------------------------------------------------------------------
+def _pv(lens, qlens, geom, bs=16, P=-1, cu=256, cap=0, mb=None):
+    Hq, Hkv, D = geom
+    mb = mb or max(-(-L // bs) for L in lens)
+    return vb.plan_varlen(lens, qlens, Hq, Hkv, D, bs, mb, P, cu, cap)
+
+
+def test_plan_varlen_split_small_work():
+    # G = 4: 4 query tokens per tile; tiles 1 + 1, units 8 * 2 = 16 < 8 * 4.
+    # Full-512 work 8 * (1 + 1) = 16 < 33 * 4 -> 256; NP = ceil(1000 / 256) = 4.
+    p = _pv([1000, 600], [4, 1], (32, 8, 128), cu=4)
+    assert (p.partition_size, p.max_num_partitions) == (256, 4)
+    assert p.scratch_bytes == 5 * 32 * 4 * 130 * 4
+    assert p.budget == 33 * 4
+
+
+def test_plan_varlen_unsplit_when_tiles_fill_the_slots():
+    # G = 8: 2 tokens per tile; tiles 4 + 4 + 2 = 10, units 2 * 10 = 20 >= 8 * 1.
+    p = _pv([100, 100, 100], [8, 8, 4], (16, 2, 128), cu=1)
+    assert (p.partition_size, p.max_num_partitions, p.scratch_bytes) == (0, 1, 0)
+    assert p.work_full_parts == 20
+
+
+def test_plan_varlen_large_partition_at_the_budget():
+    # G = 8, tiles 1 + 1 -> units 4 < 8.  Full-512 units: 2 * (16 + 8) = 48 >= 33.
+    p = _pv([8192, 4096], [2, 2], (16, 2, 256), bs=32, cu=1)
+    assert (p.partition_size, p.max_num_partitions) == (512, 16)
+    # 2 * (8 + 4) = 24 < 33 -> 256
+    p = _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, cu=1)
+    assert (p.partition_size, p.max_num_partitions) == (256, 16)
+    # forced sizes and unsplit
+    assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=512, cu=1).max_num_partitions == 8
+    assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=0, cu=1).partition_size == 0
+
+
+@pytest.mark.parametrize("lens,qlens,name", [([100, 50], [101, 1], "SEQ_LEN"),
+                                             ([100, 50], [-1, 1], "SEQ_LEN"),
+                                             ([0, 50], [0, 1], "SEQ_LEN")])
+def test_plan_varlen_rejects(lens, qlens, name):
+    with pytest.raises(vb.VkError) as e:
+        _pv(lens, qlens, (32, 8, 128), cu=4)
+    assert e.value.name == name
+
+
+def test_plan_varlen_scratch_cap():
+    with pytest.raises(vb.VkError) as e:
+        _pv([4096], [4], (32, 8, 128), P=256, cu=4, cap=1000)
+    assert e.value.name == "SCRATCH_CAP"
