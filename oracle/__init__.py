@@ -80,6 +80,15 @@ class Oracle:
         lib.oracle_partials.restype = i32
         lib.oracle_merge.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
         lib.oracle_merge.restype = None
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_paged_attention_dt.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                  ctypes.c_longlong, ctypes.c_double, i32, P, i32]
+        lib.oracle_paged_attention_dt.restype = i32
+        lib.oracle_partials_dt.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                           ctypes.c_longlong, ctypes.c_double, i32, i32, i32, P,
+                                           P, P, i32]
+        lib.oracle_partials_dt.restype = i32
         lib.oracle_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                             ctypes.c_longlong, ctypes.c_double, P, i32]
         lib.oracle_paged_varlen.restype = i32
@@ -89,21 +98,31 @@ class Oracle:
     def half_to_double(self, bits: int) -> float:
         return self.lib.oracle_half_to_double(int(bits) & 0xFFFF)
 
-    @staticmethod
-    def _args(q, k_cache, v_cache, block_tables, seq_lens):
-        return (_c(q, np.float16), _c(k_cache, np.float16), _c(v_cache, np.float16),
+    def bf16_to_double(self, bits: int) -> float:
+        return self.lib.oracle_bf16_to_double(int(bits) & 0xFFFF)
+
+    # element type of q / K / V: numpy storage and the oracle's code
+    DTYPES = {"f16": (np.float16, 0), "bf16": (np.uint16, 1), "f32": (np.float32, 2)}
+
+    @classmethod
+    def _args(cls, q, k_cache, v_cache, block_tables, seq_lens, dtype="f16"):
+        st = cls.DTYPES[dtype][0]
+        return (_c(q, st), _c(k_cache, st), _c(v_cache, st),
                 _c(block_tables, np.int32), _c(seq_lens, np.int32))
 
     def paged_attention_arrays(self, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                               nthreads: int | None = None) -> np.ndarray:
-        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens)
+                               nthreads: int | None = None, dtype: str = "f16") -> np.ndarray:
+        """dtype of q, K, V: "f16" (float16 arrays), "bf16" (uint16 bit
+        patterns) or "f32" (float32 arrays)."""
+        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens, dtype)
         S, Hq, D = q.shape
         nb, Hkv, bs, D2 = k.shape
         assert D2 == D and v.shape == k.shape and bt.shape[0] == S and sl.shape == (S,)
         out = np.empty((S, Hq, D), dtype=np.float64)
-        st = self.lib.oracle_paged_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl), S,
-                                             Hq, Hkv, D, bs, bt.shape[1], nb, float(scale),
-                                             _ptr(out), nthreads or default_threads())
+        st = self.lib.oracle_paged_attention_dt(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl), S,
+                                                Hq, Hkv, D, bs, bt.shape[1], nb, float(scale),
+                                                self.DTYPES[dtype][1], _ptr(out),
+                                                nthreads or default_threads())
         if st != 0:
             raise ValueError(f"oracle_paged_attention failed: {st}")
         return out
@@ -128,8 +147,8 @@ class Oracle:
         return out
 
     def partials_arrays(self, q, k_cache, v_cache, block_tables, seq_lens, scale, P: int,
-                        NP: int | None = None, nthreads: int | None = None):
-        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens)
+                        NP: int | None = None, nthreads: int | None = None, dtype: str = "f16"):
+        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens, dtype)
         S, Hq, D = q.shape
         nb, Hkv, bs, _ = k.shape
         if NP is None:
@@ -137,10 +156,10 @@ class Oracle:
         m = np.full((S, Hq, NP), np.nan)
         l = np.full((S, Hq, NP), np.nan)
         o = np.full((S, Hq, NP, D), np.nan)
-        st = self.lib.oracle_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl), S, Hq,
-                                      Hkv, D, bs, bt.shape[1], nb, float(scale), int(P),
-                                      int(NP), _ptr(m), _ptr(l), _ptr(o),
-                                      nthreads or default_threads())
+        st = self.lib.oracle_partials_dt(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl), S, Hq,
+                                         Hkv, D, bs, bt.shape[1], nb, float(scale), int(P),
+                                         int(NP), self.DTYPES[dtype][1], _ptr(m), _ptr(l),
+                                         _ptr(o), nthreads or default_threads())
         if st != 0:
             raise ValueError(f"oracle_partials failed: {st}")
         return m, l, o
@@ -159,11 +178,13 @@ class Oracle:
     # Workload conveniences
     def paged_attention(self, wl, nthreads: int | None = None) -> np.ndarray:
         return self.paged_attention_arrays(wl.q, wl.k_cache, wl.v_cache, wl.block_tables,
-                                           wl.seq_lens, wl.scale, nthreads)
+                                           wl.seq_lens, wl.scale, nthreads,
+                                           wl.meta.get("dtype", "f16"))
 
     def partials(self, wl, P: int, NP: int | None = None, nthreads: int | None = None):
         return self.partials_arrays(wl.q, wl.k_cache, wl.v_cache, wl.block_tables,
-                                    wl.seq_lens, wl.scale, P, NP, nthreads)
+                                    wl.seq_lens, wl.scale, P, NP, nthreads,
+                                    wl.meta.get("dtype", "f16"))
 
 
 _default = None

@@ -40,7 +40,11 @@
  *    j + 1 (itself and everything before it).  A row with no such token is
  *    zeros.
  *
- * fp16 values widen to double exactly (decoded from their bits below).
+ * fp16 values widen to double exactly (decoded from their bits below); so do
+ * the other element types of the *_dt entry points (the voxtral.c page,
+ * dpshk.com/news/5521762, keeps an fp32 KV cache as the fallback of its fp16
+ * one): bf16 (the upper half of an IEEE binary32) and fp32.  q, K and V share
+ * one element type.
  * Build with -O2 -ffp-contract=off and no fast-math.
  */
 #include <math.h>
@@ -69,8 +73,18 @@ double oracle_half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
+/* bfloat16 -> double, exactly: the 16 bits are the upper half of a binary32. */
+double oracle_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
 typedef struct {
-    const uint16_t *q, *k, *v;
+    const void *q, *k, *v;
+    int dtype;                      /* element type of q, k, v: 0 fp16, 1 bf16, 2 fp32 */
     const int32_t *block_tables, *seq_lens;
     const int32_t *cu_q;            /* variable-length queries only: [S + 1] */
     int S, Hq, Hkv, D, bs, max_blocks;
@@ -83,17 +97,24 @@ typedef struct {
     int status;
 } job_t;
 
-/* Address of element (block, kv head g, slot j, dim 0) in the pool. */
-static const uint16_t *row_ptr(const uint16_t *pool, long long block, int g, int j,
-                               int Hkv, int bs, int D)
+/* Element idx of an array of the job's element type, widened to double. */
+static double elem(const job_t *J, const void *base, long long idx)
 {
-    return pool + (((block * Hkv + g) * (long long)bs + j) * (long long)D);
+    if (J->dtype == 1) return oracle_bf16_to_double(((const uint16_t *)base)[idx]);
+    if (J->dtype == 2) return (double)((const float *)base)[idx];
+    return oracle_half_to_double(((const uint16_t *)base)[idx]);
 }
 
-/* Query vector of packed query row r, head h. */
-static const uint16_t *q_row(const job_t *J, long long r, int h)
+/* Element offset of (block, kv head g, slot j, dim 0) in a pool. */
+static long long row_ptr(long long block, int g, int j, int Hkv, int bs, int D)
 {
-    return J->q + (r * J->Hq + h) * J->D;
+    return (((block * Hkv + g) * (long long)bs + j) * (long long)D);
+}
+
+/* Element offset of the query vector of packed query row r, head h. */
+static long long q_row(const job_t *J, long long r, int h)
+{
+    return (r * J->Hq + h) * J->D;
 }
 
 /* KV head read by query head h. */
@@ -106,15 +127,15 @@ static int kv_head(const job_t *J, int h)
 
 /* Scores z_t for t in [t0, t1) of query vector qrow against sequence s's keys
  * of KV head g.  Returns 0, or -1 when a page id is outside the pool. */
-static int scores(const job_t *J, const uint16_t *qrow, int s, int g, int t0, int t1, double *z)
+static int scores(const job_t *J, long long qrow, int s, int g, int t0, int t1, double *z)
 {
     for (int t = t0; t < t1; ++t) {
         long long b = J->block_tables[(long long)s * J->max_blocks + t / J->bs];
         if (b < 0 || b >= J->num_blocks) return -1;
-        const uint16_t *krow = row_ptr(J->k, b, g, t % J->bs, J->Hkv, J->bs, J->D);
+        long long krow = row_ptr(b, g, t % J->bs, J->Hkv, J->bs, J->D);
         double dot = 0.0;
         for (int d = 0; d < J->D; ++d)
-            dot += oracle_half_to_double(qrow[d]) * oracle_half_to_double(krow[d]);
+            dot += elem(J, J->q, qrow + d) * elem(J, J->k, krow + d);
         z[t - t0] = J->scale * dot;
     }
     return 0;
@@ -130,10 +151,10 @@ static double weighted_v(const job_t *J, int s, int g, int t0, int t1, const dou
     for (int d = 0; d < J->D; ++d) acc[d] = 0.0;
     for (int t = t0; t < t1; ++t) {
         long long b = J->block_tables[(long long)s * J->max_blocks + t / J->bs];
-        const uint16_t *vrow = row_ptr(J->v, b, g, t % J->bs, J->Hkv, J->bs, J->D);
+        long long vrow = row_ptr(b, g, t % J->bs, J->Hkv, J->bs, J->D);
         double e = exp(z[t - t0] - zmax);
         sum += e;
-        for (int d = 0; d < J->D; ++d) acc[d] += e * oracle_half_to_double(vrow[d]);
+        for (int d = 0; d < J->D; ++d) acc[d] += e * elem(J, J->v, vrow + d);
     }
     for (int d = 0; d < J->D; ++d) res[d] = acc[d] / sum;
     return sum;
@@ -263,13 +284,16 @@ static int run_jobs(job_t *base, int nthreads, void *(*fn)(void *))
 /* out[S][Hq][D] = softmax attention of every query head over its sequence's
  * paged K/V.  Returns 0, -1 if a page id falls outside [0, num_blocks), -2 on
  * allocation failure. */
-int oracle_paged_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                           const int32_t *block_tables, const int32_t *seq_lens,
-                           int S, int Hq, int Hkv, int D, int bs, int max_blocks,
-                           long long num_blocks, double scale, double *out, int nthreads)
+int oracle_paged_attention_dt(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens,
+                              int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                              long long num_blocks, double scale, int dtype, double *out,
+                              int nthreads)
 {
+    if (dtype < 0 || dtype > 2) return -4;
     job_t J;
     memset(&J, 0, sizeof(J));
+    J.dtype = dtype;
     J.q = q; J.k = k_cache; J.v = v_cache;
     J.block_tables = block_tables; J.seq_lens = seq_lens;
     J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
@@ -277,23 +301,43 @@ int oracle_paged_attention(const uint16_t *q, const uint16_t *k_cache, const uin
     return run_jobs(&J, nthreads, attention_worker);
 }
 
+int oracle_paged_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *block_tables, const int32_t *seq_lens,
+                           int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                           long long num_blocks, double scale, double *out, int nthreads)
+{
+    return oracle_paged_attention_dt(q, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, D,
+                                     bs, max_blocks, num_blocks, scale, 0, out, nthreads);
+}
+
 /* Per-partition triples for partitions i < ceil(L/P) (and i < NP); entries of
  * partitions past a sequence's end are left as they were. */
-int oracle_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                    const int32_t *block_tables, const int32_t *seq_lens,
-                    int S, int Hq, int Hkv, int D, int bs, int max_blocks,
-                    long long num_blocks, double scale, int P, int NP,
-                    double *m, double *l, double *o, int nthreads)
+int oracle_partials_dt(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *seq_lens,
+                       int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                       long long num_blocks, double scale, int P, int NP, int dtype,
+                       double *m, double *l, double *o, int nthreads)
 {
-    if (P <= 0 || NP <= 0) return -4;
+    if (P <= 0 || NP <= 0 || dtype < 0 || dtype > 2) return -4;
     job_t J;
     memset(&J, 0, sizeof(J));
+    J.dtype = dtype;
     J.q = q; J.k = k_cache; J.v = v_cache;
     J.block_tables = block_tables; J.seq_lens = seq_lens;
     J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
     J.num_blocks = num_blocks; J.scale = scale; J.P = P; J.NP = NP;
     J.m = m; J.l = l; J.o = o;
     return run_jobs(&J, nthreads, partials_worker);
+}
+
+int oracle_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                    const int32_t *block_tables, const int32_t *seq_lens,
+                    int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                    long long num_blocks, double scale, int P, int NP,
+                    double *m, double *l, double *o, int nthreads)
+{
+    return oracle_partials_dt(q, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, D, bs,
+                              max_blocks, num_blocks, scale, P, NP, 0, m, l, o, nthreads);
 }
 
 /* out[total_q][Hq][D] for variable-length queries: sequence s has the query

@@ -147,10 +147,38 @@ def _place_pages(pages_per_seq, pool_blocks: int, rng, max_blocks: int,
     return bt
 
 
-def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int) -> int:
-    """Algorithmic K+V bytes of one decode step: each fp16 element of every
-    valid token's K and V row is read once, for every KV head."""
-    return int(4 * num_kv_heads * head_dim * int(np.asarray(seq_lens, dtype=np.int64).sum()))
+def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """Algorithmic K+V bytes of one decode step: each element (fp16 unless
+    elem_bytes says otherwise) of every valid token's K and V row is read
+    once, for every KV head."""
+    return int(2 * elem_bytes * num_kv_heads * head_dim *
+               int(np.asarray(seq_lens, dtype=np.int64).sum()))
+
+
+# Element types of q, K and V: numpy storage (bf16 as its uint16 bit pattern)
+# and the value that stands for NaN in canaries.
+ELEM_TYPES = {"f16": (np.float16, np.float16(np.nan)),
+              "bf16": (np.uint16, np.uint16(0x7FC0)),
+              "f32": (np.float32, np.float32(np.nan))}
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + r) >> 16).astype(np.uint16)
+
+
+def _draw(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
+    """standard_normal(float32) * sigma in the element type (fp16 / bf16 round
+    to nearest even; fp32 as drawn)."""
+    if dtype == "f16":
+        return _draw_fp16(rng, shape, sigma)
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    x = x.reshape(shape)
+    return _to_bf16_bits(x) if dtype == "bf16" else x
 
 
 def _fill_canaries(wl: Workload) -> None:
@@ -158,6 +186,7 @@ def _fill_canaries(wl: Workload) -> None:
     each sequence's last page."""
     used = np.zeros(wl.num_blocks, dtype=bool)
     bs = wl.block_size
+    nan = ELEM_TYPES[wl.meta.get("dtype", "f16")][1]
     for s in range(wl.num_seqs):
         L = int(wl.seq_lens[s])
         n = -(-L // bs)
@@ -166,10 +195,10 @@ def _fill_canaries(wl: Workload) -> None:
         tail = L - (n - 1) * bs
         if tail < bs:
             last = ids[n - 1]
-            wl.k_cache[last, :, tail:, :] = np.float16(np.nan)
-            wl.v_cache[last, :, tail:, :] = np.float16(np.nan)
-    wl.k_cache[~used] = np.float16(np.nan)
-    wl.v_cache[~used] = np.float16(np.nan)
+            wl.k_cache[last, :, tail:, :] = nan
+            wl.v_cache[last, :, tail:, :] = nan
+    wl.k_cache[~used] = nan
+    wl.v_cache[~used] = nan
     wl.meta["unused_blocks"] = int((~used).sum())
 
 
@@ -221,10 +250,12 @@ def make_custom(*, seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
                 block_size: int, seed: int, pool_factor: float = 1.0,
                 sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0,
                 scale: float | None = None, canaries: bool = False, pad_value: int = -1,
-                extra_blocks_per_seq: int = 0, name: str = "custom") -> Workload:
+                extra_blocks_per_seq: int = 0, name: str = "custom",
+                dtype: str = "f16") -> Workload:
     """A seeded workload of any shape (for tests): pages shuffled in a pool of
     ceil(pool_factor * needed) blocks; `extra_blocks_per_seq` widens the page
-    table beyond the longest sequence."""
+    table beyond the longest sequence.  dtype: element type of q, K and V
+    ("f16", "bf16" as uint16 bit patterns, "f32"); meta["dtype"] records it."""
     r_place, r_q, r_k, r_v = [np.random.Generator(np.random.PCG64(s))
                               for s in np.random.SeedSequence(seed).spawn(4)]
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
@@ -235,14 +266,15 @@ def make_custom(*, seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
     pool = max(1, int(math.ceil(pool_factor * need)))
     max_blocks = max(1, max(pages) + extra_blocks_per_seq)
     bt = _place_pages(pages, pool, r_place, max_blocks, pad_value, take_prefix=True)
-    q = _draw_fp16(r_q, (S, num_q_heads, head_dim), sigma_q)
-    k = _draw_fp16(r_k, (pool, num_kv_heads, bs, head_dim), sigma_k)
-    v = _draw_fp16(r_v, (pool, num_kv_heads, bs, head_dim), sigma_v)
+    q = _draw(r_q, (S, num_q_heads, head_dim), sigma_q, dtype)
+    k = _draw(r_k, (pool, num_kv_heads, bs, head_dim), sigma_k, dtype)
+    v = _draw(r_v, (pool, num_kv_heads, bs, head_dim), sigma_v, dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     wl = Workload(name=name, num_seqs=S, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                   head_dim=head_dim, block_size=bs, seq_lens=seq_lens, block_tables=bt,
                   num_blocks=pool, q=q, k_cache=k, v_cache=v, scale=float(np.float32(scale)))
+    wl.meta["dtype"] = dtype
     if canaries:
         _fill_canaries(wl)
     return wl

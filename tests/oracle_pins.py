@@ -400,7 +400,74 @@ def pin_varlen_one_token_is_decode(orc):
     assert np.array_equal(got, ref), "qlen = 1 must be the decode oracle"
 
 
+# ----------------------------------------------------------------------------
+# Other element types of q, K and V (bf16 bit patterns, fp32).
+# ----------------------------------------------------------------------------
+def pin_bf16_decode(orc):
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):          # signalling NaN patterns
+        ref = (bits << 16).view(np.float32).astype(np.float64)
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits[::97]] +
+                   [orc.bf16_to_double(int(b)) for b in (0x0000, 0x8000, 0x0001, 0x7F80, 0xFF80,
+                                                        0x7F7F, 0x3F80, 0x7FC0)])
+    want = np.concatenate([ref[::97], ref[[0x0000, 0x8000, 0x0001, 0x7F80, 0xFF80, 0x7F7F,
+                                           0x3F80, 0x7FC0]]])
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert np.all(same), "bf16 decode"
+
+
+def _dtype_case(seed, lens, Hq, Hkv, D, bs, dtype):
+    """Dense values in the element type; torch builds the float64 copies the
+    reference uses from the stored bits itself."""
+    c = dense_case(seed, lens, Hq, Hkv, D, bs)
+    rng = np.random.default_rng(seed + 7)
+
+    def draw(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if dtype == "f32":
+            return x, torch.from_numpy(x.copy()).double()
+        u = x.view(np.uint32)
+        b = (((u + (((u >> 16) & 1) + np.uint32(0x7FFF))) >> 16)).astype(np.uint16)
+        t = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).double()
+        return b, t
+
+    S = len(lens)
+    q, tq = draw((S, Hq, D))
+    dk, tk, dv, tv = [], [], [], []
+    for L in lens:
+        a, ta = draw((Hkv, L, D))
+        b_, tb = draw((Hkv, L, D))
+        dk.append(a); tk.append(ta); dv.append(b_); tv.append(tb)
+    st = np.float32 if dtype == "f32" else np.uint16
+    kc = np.zeros(c["k_cache"].shape, dtype=st)
+    vc = np.zeros(c["v_cache"].shape, dtype=st)
+    for s, L in enumerate(lens):
+        for p in range(-(-L // bs)):
+            blk = c["block_tables"][s, p]
+            n = min(bs, L - p * bs)
+            kc[blk, :, :n, :] = dk[s][:, p * bs:p * bs + n, :]
+            vc[blk, :, :n, :] = dv[s][:, p * bs:p * bs + n, :]
+    G = Hq // Hkv
+    ref = np.empty((S, Hq, D))
+    for s in range(S):
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq[s][:, None, :], tk[s].repeat_interleave(G, 0), tv[s].repeat_interleave(G, 0),
+            scale=c["scale"])
+        ref[s] = o[:, 0, :].numpy()
+    return q, kc, vc, c["block_tables"], c["seq_lens"], c["scale"], ref
+
+
+def pin_other_element_types(orc):
+    for dtype in ("bf16", "f32"):
+        q, kc, vc, bt, sl, scale, ref = _dtype_case(301, [37, 1, 70], 16, 2, 32, 8, dtype)
+        got = orc.paged_attention_arrays(q, kc, vc, bt, sl, scale, dtype=dtype)
+        _close(got, ref, 1e-12, f"sdpa {dtype}")
+        m, l, o = orc.partials_arrays(q, kc, vc, bt, sl, scale, 16, dtype=dtype)
+        _close(orc.merge(m, l, o, sl, 16), ref, 1e-12, f"split/merge {dtype}")
+
+
 ALL_PINS = [pin_half_decode, pin_sdpa, pin_closed_forms, pin_large_scores, pin_permutation,
             pin_split_merge, pin_partials_closed, pin_merge_closed, pin_shift_invariance,
             pin_gqa_to_mha, pin_onehot, pin_golden, pin_varlen_sdpa,
-            pin_varlen_rows_are_truncated_decodes, pin_varlen_one_token_is_decode]
+            pin_varlen_rows_are_truncated_decodes, pin_varlen_one_token_is_decode,
+            pin_bf16_decode, pin_other_element_types]

@@ -30,6 +30,9 @@ MUTANTS = [
     ("varlen_causal_off_by_one", "int lim = L - qlen + j + 1;", "int lim = L - qlen + j;"),
     ("varlen_not_causal", "int lim = L - qlen + j + 1;", "int lim = L;"),
     ("varlen_row_offset", "long long row = J->cu_q[s] + j;", "long long row = J->cu_q[s] + qlen - 1 - j;"),
+    ("bf16_wrong_half", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;"),
+    ("f32_read_as_half", "if (J->dtype == 2) return (double)((const float *)base)[idx];",
+     "if (J->dtype == 2) return oracle_half_to_double(((const uint16_t *)base)[idx]);"),
     ("dot_skips_last_dim", "for (int d = 0; d < J->D; ++d)\n            dot +=",
      "for (int d = 0; d < J->D - 1; ++d)\n            dot +="),
 ]
