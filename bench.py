@@ -49,12 +49,11 @@ DESCRIPTIONS = {
                         "[1024, 8192], (24q, 4kv, 256), block 32, planner",
 }
 VARLEN = ("verify32_q4", "prefill4_chunk1k")
+_MFMA_SOURCES = ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip",
+                 "paged_gqa_kv_decode_amd/csrc/decode_mfma_impl.h"]
 KERNEL_SOURCES = {
     1: ["paged_gqa_kv_decode_amd/csrc/decode_dot.hip"],
-    3: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
-    4: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
-    5: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
-    6: ["paged_gqa_kv_decode_amd/csrc/decode_mfma.hip"],
+    3: _MFMA_SOURCES, 4: _MFMA_SOURCES, 5: _MFMA_SOURCES, 6: _MFMA_SOURCES,
 }
 KERNEL_NAMES = {1: "dot", 3: "mfma_w1", 4: "mfma_w2", 5: "mfma_w4", 6: "mfma_w4p2"}
 
@@ -183,12 +182,13 @@ def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
         t = time.perf_counter()
         oracle.paged_attention_arrays(wl.q[s:s + 1], wl.k_cache, wl.v_cache,
                                       wl.block_tables[s:s + 1], wl.seq_lens[s:s + 1], wl.scale,
-                                      nthreads=nthreads)
+                                      nthreads=nthreads, dtype=wl.meta.get("dtype", "f16"))
         dt = time.perf_counter() - t
         total += dt
         runs += 1
         done_tokens += L
-        done_bytes += kv_read_bytes(wl.seq_lens[s:s + 1], wl.num_kv_heads, wl.head_dim)
+        done_bytes += kv_read_bytes(wl.seq_lens[s:s + 1], wl.num_kv_heads, wl.head_dim,
+                                    4 if wl.meta.get("dtype") == "f32" else 2)
         per_token = total / max(done_tokens, 1)
     return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s (KV-read)",
             "cores": nthreads, "kind": "oracle",
@@ -340,6 +340,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long4_128k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--dtype", default="f16", choices=["f16", "bf16", "f32"],
+                    help="element type of q / K / V (with --shape)")
     ap.add_argument("--shape", default=None,
                     help="time a custom shape instead: S,Hq,Hkv,D,bs,Lmin,Lmax (lengths uniform "
                          "in [Lmin, Lmax], seeded; pages shuffled in an exact-fit pool)")
@@ -405,11 +407,11 @@ def main():
         S_, Hq_, Hkv_, D_, bs_, lo_, hi_ = (int(x) for x in args.shape.split(","))
         lens_ = np.random.default_rng(7).integers(lo_, hi_ + 1, S_)
         wl = make_custom(seq_lens=lens_, num_q_heads=Hq_, num_kv_heads=Hkv_, head_dim=D_,
-                         block_size=bs_, seed=7)
+                         block_size=bs_, seed=7, dtype=args.dtype)
         wl.partition_sizes = (-1,)
         args.workload = f"custom_{args.shape}"
         DESCRIPTIONS[args.workload] = (f"{S_} seqs, L uniform in [{lo_}, {hi_}], "
-                                       f"({Hq_}q, {Hkv_}kv, {D_}), block {bs_}")
+                                       f"({Hq_}q, {Hkv_}kv, {D_}), block {bs_}, {args.dtype}")
     elif args.workload in VARLEN:
         from paged_gqa_kv_decode_amd.workloads import make_varlen
         wl = make_varlen(args.workload)
@@ -427,7 +429,10 @@ def main():
 
     dev = vb.device_inputs(wl)
     q, k, v, bt, sl = dev
-    kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim)
+    dtype_code = {"f16": vb.DTYPE_F16, "bf16": vb.DTYPE_BF16,
+                  "f32": vb.DTYPE_F32}[wl.meta.get("dtype", "f16")]
+    kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim,
+                             4 if dtype_code == vb.DTYPE_F32 else 2)
     # Successive steps rotate over identical copies of the K/V pools so that at
     # least 4x the 256 MB Infinity Cache is read between two reads of the same
     # page: every step streams its KV from HBM, as a layer's decode does when
@@ -441,7 +446,7 @@ def main():
     # Scratch sized once from a first plan; every step plans again (host) and
     # reuses it (the plan depends only on the host seq_lens).
     step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out,
-                          fused=args.fused)
+                          fused=args.fused, dtype=dtype_code)
     P, NP = step0.plan.partition_size, step0.plan.max_num_partitions
 
     counter = [0]
@@ -470,6 +475,15 @@ def main():
                                       step0.exp_sums, step0.tmp_out, step0.counters, stream)
             if ev is not None:
                 ev[1].record(stream)
+        elif dtype_code != vb.DTYPE_F16:
+            vb.paged_gqa_decode_dt(dtype_code, q, k, v, bt, sl, wl.scale, P, NP,
+                                   None if P else out, step0.max_logits, step0.exp_sums,
+                                   step0.tmp_out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            if P:
+                vb.paged_gqa_reduce(step0.max_logits, step0.exp_sums, step0.tmp_out, sl, P, out,
+                                    stream)
         elif P:
             vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, P, NP, None, step0.max_logits,
                                 step0.exp_sums, step0.tmp_out, stream)
@@ -519,8 +533,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded N(0, sigma) fp16 K/V/q, shuffled pages)",
+        "dtype": wl.meta.get("dtype", "f16"),
+        "data": f"synthetic (seeded N(0, sigma) {wl.meta.get('dtype', 'f16')} K/V/q, shuffled pages)",
         "config": {"workload": args.workload, "description": DESCRIPTIONS[args.workload],
                    "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,

@@ -20,10 +20,13 @@
 #define VK_DEFAULT_BUDGET_PER_CU 33
 #define VK_DEFAULT_SCRATCH_CAP (512ull * 1024ull * 1024ull)
 
-/* Admitted geometries (Hq, Hkv, D).  Four geometries x three page sizes give
- * twelve kernel specialisations. */
-#define VK_NUM_GEOMETRIES 4
-#define VK_GEOMETRY_LIST {{32, 8, 128}, {24, 4, 256}, {16, 2, 128}, {16, 2, 256}}
+/* Admitted geometries (Hq, Hkv, D): the four grouped-query triples of the
+ * dispatch layer, then multi-head (Hkv = Hq) and multi-query (Hkv = 1)
+ * triples (the vllm-metal page's prefill path names MHA, GQA and MQA).
+ * Eight geometries x three page sizes give 24 kernel specialisations. */
+#define VK_NUM_GEOMETRIES 8
+#define VK_GEOMETRY_LIST {{32, 8, 128}, {24, 4, 256}, {16, 2, 128}, {16, 2, 256}, \
+                          {16, 16, 128}, {8, 8, 256}, {16, 1, 128}, {16, 1, 256}}
 #define VK_NUM_BLOCK_SIZES 3
 #define VK_BLOCK_SIZE_LIST {8, 16, 32}
 

@@ -78,7 +78,15 @@ enum {
     VK_ERR_PARTITION = 5,   /* partition size or count not allowed */
     VK_ERR_SEQ_LEN = 6,     /* a host seq_len is < 1 or beyond the page table */
     VK_ERR_SCRATCH_CAP = 7, /* split-KV scratch would exceed the cap */
-    VK_ERR_HIP = 8          /* a HIP runtime call or launch failed */
+    VK_ERR_HIP = 8,         /* a HIP runtime call or launch failed */
+    VK_ERR_DTYPE = 9        /* element type not supported by this entry point */
+};
+
+/* Element type of q, K and V (vk_paged_gqa_decode_dt). */
+enum {
+    VK_DTYPE_F16 = 0,
+    VK_DTYPE_BF16 = 1,
+    VK_DTYPE_F32 = 2
 };
 
 /* Decode kernel families; see vk_select_decode_kernel. */
@@ -171,6 +179,29 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
                               int32_t partition_size, int32_t max_num_partitions,
                               float* out, float* max_logits, float* exp_sums, float* tmp_out,
                               void* stream);
+
+/*
+ * vk_paged_gqa_decode_dt — vk_paged_gqa_decode for another element type of
+ * q, k_cache and v_cache (one type for all three; the partials and `out` stay
+ * fp32 and are merged by the same vk_paged_gqa_reduce).  The voxtral.c page,
+ * dpshk.com/news/5521762, keeps fp32 as the fallback of its fp16 KV cache.
+ *   VK_DTYPE_F16   the fp16 path of vk_paged_gqa_decode
+ *   VK_DTYPE_BF16  bfloat16: the matrix-core family, scores exact products
+ *                  accumulated in fp32 as for fp16; each softmax weight enters
+ *                  the PV product as a bf16 value plus its bf16 residual
+ *   VK_DTYPE_F32   fp32: the fp32 matrix-core products (v_mfma 16x16x4 f32)
+ * Layouts as for fp16 with the element size of the type.  VK_ERR_DTYPE for
+ * any other value.  Non-fp16 types always run the matrix-core family with
+ * one partition per workgroup (a VALU or two-partition selection is ignored).
+ */
+vk_status vk_paged_gqa_decode_dt(int32_t dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                 int32_t partition_size, int32_t max_num_partitions, float* out,
+                                 float* max_logits, float* exp_sums, float* tmp_out,
+                                 void* stream);
 
 /*
  * vk_paged_gqa_reduce — merge the split-KV partials (vllm-metal kernels page,

@@ -22,7 +22,9 @@ Readings where the page is silent (each stated in the design notes):
 """
 from __future__ import annotations
 
-ADMITTED_GEOMETRIES = {(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256)}
+ADMITTED_GEOMETRIES = {(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256),
+                       # multi-head and multi-query triples
+                       (16, 16, 128), (8, 8, 256), (16, 1, 128), (16, 1, 256)}
 BLOCK_SIZES = (8, 16, 32)
 PARTITION_SIZES = (256, 512)
 DEFAULT_BUDGET_PER_CU = 33

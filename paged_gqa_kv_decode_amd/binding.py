@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libvkpaged.so")
 
 VK_OK = 0
 STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_SIZE",
-                5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP"}
+                5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP", 9: "DTYPE"}
+DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4, KERNEL_MFMA_W4P2 = 3, 4, 5, 6
 ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
@@ -26,7 +27,8 @@ ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
             "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
-            "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce")
+            "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce",
+            "vk_paged_gqa_decode_dt")
 
 
 class VkError(RuntimeError):
@@ -86,6 +88,9 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                       ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_decode.restype = i32
+    L.vk_paged_gqa_decode_dt.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
+    L.vk_paged_gqa_decode_dt.restype = i32
     L.vk_paged_gqa_decode_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_decode_fused.restype = i32
@@ -189,11 +194,17 @@ def _need(t, dtype, name):
     _ = torch
 
 
-def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
-                 max_num_partitions, out, max_logits, exp_sums, tmp_out):
+def _torch_elem(dtype: int):
     import torch
-    for t, dt, n in ((q, torch.float16, "q"), (k_cache, torch.float16, "k_cache"),
-                     (v_cache, torch.float16, "v_cache"), (block_tables, torch.int32, "block_tables"),
+    return {DTYPE_F16: torch.float16, DTYPE_BF16: torch.bfloat16, DTYPE_F32: torch.float32}[dtype]
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                 max_num_partitions, out, max_logits, exp_sums, tmp_out, dtype=DTYPE_F16):
+    import torch
+    et = _torch_elem(dtype)
+    for t, dt, n in ((q, et, "q"), (k_cache, et, "k_cache"),
+                     (v_cache, et, "v_cache"), (block_tables, torch.int32, "block_tables"),
                      (seq_lens, torch.int32, "seq_lens"), (out, torch.float32, "out"),
                      (max_logits, torch.float32, "max_logits"), (exp_sums, torch.float32, "exp_sums"),
                      (tmp_out, torch.float32, "tmp_out")):
@@ -227,6 +238,17 @@ def paged_gqa_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
     args = _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
                         max_num_partitions, out, max_logits, exp_sums, tmp_out)
     _check("vk_paged_gqa_decode", lib().vk_paged_gqa_decode(*args, _stream_handle(stream)))
+
+
+def paged_gqa_decode_dt(dtype: int, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                        partition_size: int, max_num_partitions: int, out=None, max_logits=None,
+                        exp_sums=None, tmp_out=None, stream=None) -> None:
+    """paged_gqa_decode for q / K / V of element type `dtype` (DTYPE_F16,
+    DTYPE_BF16 with torch.bfloat16 tensors, DTYPE_F32 with float32)."""
+    args = _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                        max_num_partitions, out, max_logits, exp_sums, tmp_out, dtype)
+    _check("vk_paged_gqa_decode_dt",
+           lib().vk_paged_gqa_decode_dt(int(dtype), *args, _stream_handle(stream)))
 
 
 def paged_gqa_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
@@ -412,7 +434,8 @@ class DecodeStep:
     the single-launch form when `fused`."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, seq_lens, seq_lens_host, scale: float,
-                 partition_request: int = -1, cu_count: int = 0, out=None, fused: bool = False):
+                 partition_request: int = -1, cu_count: int = 0, out=None, fused: bool = False,
+                 dtype: int = DTYPE_F16):
         import torch
         S, Hq, D = q.shape
         nb, Hkv, bs, _ = k_cache.shape
@@ -431,6 +454,7 @@ class DecodeStep:
         else:
             self.max_logits = self.exp_sums = self.tmp_out = None
         self.fused = bool(fused)
+        self.dtype = int(dtype)
         # arrival counters of the single-launch form: zeroed once, every call
         # leaves them zero
         self.counters = (torch.zeros(S * Hkv, dtype=torch.int32, device=dev)
@@ -442,6 +466,13 @@ class DecodeStep:
         if self.fused:
             paged_gqa_decode_fused(q, k, v, bt, sl, self.scale, P, NP, self.out, self.max_logits,
                                    self.exp_sums, self.tmp_out, self.counters, stream)
+        elif self.dtype != DTYPE_F16:
+            paged_gqa_decode_dt(self.dtype, q, k, v, bt, sl, self.scale, P, NP,
+                                None if P else self.out, self.max_logits, self.exp_sums,
+                                self.tmp_out, stream)
+            if P:
+                paged_gqa_reduce(self.max_logits, self.exp_sums, self.tmp_out, sl, P, self.out,
+                                 stream)
         elif P:
             paged_gqa_decode(q, k, v, bt, sl, self.scale, P, NP, None, self.max_logits,
                              self.exp_sums, self.tmp_out, stream)
@@ -453,9 +484,16 @@ class DecodeStep:
 
 
 def device_inputs(wl, device="cuda"):
-    """Copy a Workload's host arrays to device tensors (q, k, v, bt, sl)."""
+    """Copy a Workload's host arrays to device tensors (q, k, v, bt, sl);
+    bf16 workloads (uint16 bit patterns) become torch.bfloat16 tensors."""
     import torch
     dev = torch.device(device)
-    return (torch.from_numpy(wl.q).to(dev), torch.from_numpy(wl.k_cache).to(dev),
-            torch.from_numpy(wl.v_cache).to(dev), torch.from_numpy(wl.block_tables).to(dev),
-            torch.from_numpy(wl.seq_lens).to(dev))
+
+    def elem(a):
+        t = torch.from_numpy(a)
+        if wl.meta.get("dtype", "f16") == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    return (elem(wl.q), elem(wl.k_cache), elem(wl.v_cache),
+            torch.from_numpy(wl.block_tables).to(dev), torch.from_numpy(wl.seq_lens).to(dev))

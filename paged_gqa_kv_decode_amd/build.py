@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libvkpaged.so")
 BENCH_LIB = os.path.join(PKG, "libvkbench.so")   # measurement-only kernels
 ARCH = "gfx950"
 
-SOURCES = ["vk_host.cpp", "decode_dot.hip", "decode_mfma.hip", "decode_varlen.hip", "reduce.hip",
+SOURCES = ["vk_host.cpp", "decode_dot.hip", "decode_mfma.hip", "decode_mfma_mhq.hip",
+           "decode_mfma_bf16.hip", "decode_mfma_f32.hip", "decode_varlen.hip", "reduce.hip",
            "kv_append.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 

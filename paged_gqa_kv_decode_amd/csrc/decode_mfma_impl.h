@@ -67,9 +67,19 @@ namespace {
 
 using namespace mfma;
 
-template <int D, int G, int BS, int W, int WP, int T, bool FUSED>
+// DT: element type of q, K and V (0 fp16, 1 bf16, 2 fp32).
+//
+// fp32 (DT = 2) runs the same steps on v_mfma_f32_16x16x4_f32: in QK product
+// kk the k-slot of lane group c is dim c * D/4 + kk, so lane (token i, c)
+// reads D/4 contiguous floats of its K row and the Q^T operand the same dims
+// of head i; the QK output (lane: head i, tokens 4c + r) is again the PV B
+// operand, one fp32 weight per product r, against V[token 4c + r][dim] read
+// one float per lane (16 lanes = 64 contiguous bytes).  Accumulator tile t
+// then holds dims 16t + 4c + r.
+template <int D, int G, int BS, int W, int WP, int T, bool FUSED, int DT = 0>
 struct MfmaKernel {
     static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
+    static_assert(DT == 0 || T == 16, "bf16 and fp32 run 16-token steps");
     // WP waves share one partition; a workgroup covers PPW = W / WP
     // consecutive partitions (split launches only, not the single launch).
     static constexpr int PPW = W / WP;
@@ -100,9 +110,22 @@ struct MfmaKernel {
     }
 
     // K/V registers of one step.
+    static constexpr int KQ = DT == 2 ? D / 16 : NKC;   // uint4 of K per token tile, and of Q
+    static constexpr int NF = DT == 2 ? D / 16 : 1;     // fp32: V floats per token per lane
+    using QReg = uint4[KQ];
+
+    // Dim of accumulator tile t, row rr, for lane group c.
+    static __device__ __forceinline__ int acc_dim(int t, int c, int rr) {
+        if constexpr (DT == 2)
+            return 16 * t + 4 * c + rr;
+        else
+            return 128 * (t / 8) + 8 * (4 * c + rr) + t % 8;
+    }
+
     struct Buf {
-        uint4 kr[NT][NKC];
+        uint4 kr[NT][KQ];
         uint4 vr[NDH][NJ];
+        float vf[4][NF];
     };
 
     // Page ids of the step at chunk offset `off`, read from the chunk's page
@@ -125,7 +148,19 @@ struct MfmaKernel {
     template <bool FULL>
     static __device__ __forceinline__ void issue_k(const DecodeArgs& a, Buf& b, const StepPages& sp,
                                                    int g, int remain, int i, int c) {
-        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // elements
+        if constexpr (DT == 2) {
+            const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)g * BS * D;
+            const int tok = i;
+            const bool ok = FULL || tok < remain;
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int u = 0; u < KQ; ++u)
+                b.kr[0][u] = ok ? load_stream(kp + c * KQ + u) : make_uint4(0, 0, 0, 0);
+            return;
+        }
         const uint16_t* kbase = a.k + (int64_t)g * BS * D;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -144,7 +179,21 @@ struct MfmaKernel {
     template <bool FULL>
     static __device__ __forceinline__ void issue_v(const DecodeArgs& a, Buf& b, const StepPages& sp,
                                                    int g, int remain, int i, int c) {
-        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // halfs
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // elements
+        if constexpr (DT == 2) {
+            const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)g * BS * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 4 * c + r;
+                const bool ok = FULL || tok < remain;
+                const float* vp = vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                                  (int64_t)((sp.off_slot + tok) % BS) * D;
+#pragma unroll
+                for (int t = 0; t < NF; ++t)
+                    b.vf[r][t] = ok ? __builtin_nontemporal_load(vp + 16 * t + i) : 0.f;
+            }
+            return;
+        }
         const uint16_t* vbase = a.v + (int64_t)g * BS * D;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -171,15 +220,25 @@ struct MfmaKernel {
     // packed as the PV B operand (x, y used for 16-token steps).
     template <bool FULL>
     static __device__ __forceinline__ uint4 qk_softmax(const DecodeArgs& a, State& st, const Buf& b,
-                                                       const uint4 (&qb)[NKC], int remain, int c) {
+                                                       const QReg& qb, int remain, int c) {
         const auto& kr = b.kr;
         // ---- S = K Q^T on the matrix cores ----
         floatx4 sc[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             sc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (DT == 2) {
 #pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) sc[tt] = mfma32(kr[tt][kk], qb[kk], sc[tt]);
+                for (int u = 0; u < KQ; ++u) {
+                    sc[tt] = mfma4_f32(kr[tt][u].x, qb[u].x, sc[tt]);
+                    sc[tt] = mfma4_f32(kr[tt][u].y, qb[u].y, sc[tt]);
+                    sc[tt] = mfma4_f32(kr[tt][u].z, qb[u].z, sc[tt]);
+                    sc[tt] = mfma4_f32(kr[tt][u].w, qb[u].w, sc[tt]);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NKC; ++kk) sc[tt] = qk_mma(kr[tt][kk], qb[kk], sc[tt]);
+            }
         }
 
         // ---- online softmax (log2 units) for head i, tokens of this lane ----
@@ -212,19 +271,70 @@ struct MfmaKernel {
 #pragma unroll
         for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
         uint4 pb;
-        pb.x = pack_half2(p[0], p[1]);
-        pb.y = pack_half2(p[2], p[3]);
         if constexpr (T == 32) {
+            pb.x = pack_half2(p[0], p[1]);
+            pb.y = pack_half2(p[2], p[3]);
             pb.z = pack_half2(p[4], p[5]);
             pb.w = pack_half2(p[6], p[7]);
         } else {
+            pb = pack_weights(p[0], p[1], p[2], p[3]);
+        }
+        return pb;
+    }
+
+    // S = K Q^T product of one 32-dim chunk in the element type.
+    static __device__ __forceinline__ floatx4 qk_mma(const uint4& a, const uint4& b, const floatx4& c) {
+        if constexpr (DT == 1)
+            return mfma32_bf16(a, b, c);
+        else
+            return mfma32(a, b, c);
+    }
+
+    // Four weights of a 16-token step as the PV B operand: fp16 in .x/.y; for
+    // bf16 the rounded pairs in .x/.y and their residuals in .z/.w.
+    static __device__ __forceinline__ uint4 pack_weights(float p0, float p1, float p2, float p3) {
+        uint4 pb;
+        if constexpr (DT == 2) {   // fp32 weights as they are
+            pb = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        } else if constexpr (DT == 1) {
+            pack_bf16_split(p0, p1, pb.x, pb.z);
+            pack_bf16_split(p2, p3, pb.y, pb.w);
+        } else {
+            pb.x = pack_half2(p0, p1);
+            pb.y = pack_half2(p2, p3);
             pb.z = pb.w = 0;
         }
         return pb;
     }
 
+    // One 16-dim PV output tile of a 16-token step (dims e of the lane
+    // group's 4 tokens); bf16 adds the residual weights' product.
+    template <int E>
+    static __device__ __forceinline__ void pv16(floatx4& acc, const uint4 (&v)[4], const uint4& pb) {
+        const uint2 a = vt_operand4<E>(v);
+        if constexpr (DT == 1) {
+            acc = mfma16_bf16(a, make_uint2(pb.x, pb.y), acc);
+            acc = mfma16_bf16(a, make_uint2(pb.z, pb.w), acc);
+        } else {
+            acc = mfma16(a, make_uint2(pb.x, pb.y), acc);
+        }
+    }
+
     // ---- O^T += V^T P^T on the matrix cores ----
     static __device__ __forceinline__ void pv(State& st, const Buf& b, const uint4& pb) {
+        if constexpr (DT == 2) {
+            const float p0 = __builtin_bit_cast(float, pb.x), p1 = __builtin_bit_cast(float, pb.y);
+            const float p2 = __builtin_bit_cast(float, pb.z), p3 = __builtin_bit_cast(float, pb.w);
+#pragma unroll
+            for (int t = 0; t < NPT; ++t) {
+                st.acc[t] = mfma4_f32(b.vf[0][t], p0, st.acc[t]);
+                st.acc[t] = mfma4_f32(b.vf[1][t], p1, st.acc[t]);
+                st.acc[t] = mfma4_f32(b.vf[2][t], p2, st.acc[t]);
+                st.acc[t] = mfma4_f32(b.vf[3][t], p3, st.acc[t]);
+            }
+            return;
+        }
         const auto& vr = b.vr;
         if constexpr (T == 32) {
 #pragma unroll
@@ -239,29 +349,28 @@ struct MfmaKernel {
                 st.acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
             }
         } else {
-            const uint2 pb2 = make_uint2(pb.x, pb.y);
 #pragma unroll
             for (int dh = 0; dh < NDH; ++dh) {
-                st.acc[dh * 8 + 0] = mfma16(vt_operand4<0>(vr[dh]), pb2, st.acc[dh * 8 + 0]);
-                st.acc[dh * 8 + 1] = mfma16(vt_operand4<1>(vr[dh]), pb2, st.acc[dh * 8 + 1]);
-                st.acc[dh * 8 + 2] = mfma16(vt_operand4<2>(vr[dh]), pb2, st.acc[dh * 8 + 2]);
-                st.acc[dh * 8 + 3] = mfma16(vt_operand4<3>(vr[dh]), pb2, st.acc[dh * 8 + 3]);
-                st.acc[dh * 8 + 4] = mfma16(vt_operand4<4>(vr[dh]), pb2, st.acc[dh * 8 + 4]);
-                st.acc[dh * 8 + 5] = mfma16(vt_operand4<5>(vr[dh]), pb2, st.acc[dh * 8 + 5]);
-                st.acc[dh * 8 + 6] = mfma16(vt_operand4<6>(vr[dh]), pb2, st.acc[dh * 8 + 6]);
-                st.acc[dh * 8 + 7] = mfma16(vt_operand4<7>(vr[dh]), pb2, st.acc[dh * 8 + 7]);
+                pv16<0>(st.acc[dh * 8 + 0], vr[dh], pb);
+                pv16<1>(st.acc[dh * 8 + 1], vr[dh], pb);
+                pv16<2>(st.acc[dh * 8 + 2], vr[dh], pb);
+                pv16<3>(st.acc[dh * 8 + 3], vr[dh], pb);
+                pv16<4>(st.acc[dh * 8 + 4], vr[dh], pb);
+                pv16<5>(st.acc[dh * 8 + 5], vr[dh], pb);
+                pv16<6>(st.acc[dh * 8 + 6], vr[dh], pb);
+                pv16<7>(st.acc[dh * 8 + 7], vr[dh], pb);
             }
         }
     }
 
     template <bool FULL>
     static __device__ __forceinline__ void compute(const DecodeArgs& a, State& st, const Buf& b,
-                                                   const uint4 (&qb)[NKC], int remain, int c) {
+                                                   const QReg& qb, int remain, int c) {
         const uint4 pb = qk_softmax<FULL>(a, st, b, qb, remain, c);
         pv(st, b, pb);
     }
 
-    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const uint4 (&qb)[NKC],
+    static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const QReg& qb,
                                                 int t_begin, int t_end, int g, int s, int wsub,
                                                 int lane, int i, int c, int pg_first, bool& bad) {
         const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
@@ -318,12 +427,20 @@ struct MfmaKernel {
         const int32_t pg_first =
             a.block_tables[(int64_t)s * a.max_blocks_per_seq +
                            min(t_first / BS + lane, a.max_blocks_per_seq - 1)];
-        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8); zero for i >= G.
-        uint4 qb[NKC];
+        // Q^T operand: head i of the group, dims [32 kk + 8 c, +8) (fp32:
+        // [c D/4, +D/4)); zero for i >= G.
+        QReg qb;
         {
-            const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D);
+            const int64_t qrow = ((int64_t)s * Hq + g * G + (i < G ? i : 0)) * D;
+            if constexpr (DT == 2) {
+                const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.q) + qrow);
 #pragma unroll
-            for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+                for (int u = 0; u < KQ; ++u) qb[u] = (i < G) ? qp[c * KQ + u] : make_uint4(0, 0, 0, 0);
+            } else {
+                const uint4* qp = reinterpret_cast<const uint4*>(a.q + qrow);
+#pragma unroll
+                for (int kk = 0; kk < NKC; ++kk) qb[kk] = (i < G) ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+            }
         }
         int L = a.seq_lens[s];
         bool poison = false;
@@ -388,24 +505,18 @@ struct MfmaKernel {
                     }
                 }
 #pragma unroll
-                for (int dh = 0; dh < NDH; ++dh)
+                for (int t = 0; t < NPT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int d = 128 * dh + 8 * (4 * c + rr) + e;
-                            dst[d] = out_bad ? __builtin_nanf("") : st.acc[dh * 8 + e][rr] / lsum;
-                        }
+                    for (int rr = 0; rr < 4; ++rr)
+                        dst[acc_dim(t, c, rr)] = out_bad ? __builtin_nanf("") : st.acc[t][rr] / lsum;
             }
         } else {
             if (i < G) {
 #pragma unroll
-                for (int dh = 0; dh < NDH; ++dh)
+                for (int t = 0; t < NPT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr)
-                            s_acc[wave][i][128 * dh + 8 * (4 * c + rr) + e] = st.acc[dh * 8 + e][rr];
+                    for (int rr = 0; rr < 4; ++rr)
+                        s_acc[wave][i][acc_dim(t, c, rr)] = st.acc[t][rr];
                 if (c == 0) {
                     s_m[wave][i] = st.m;
                     s_l[wave][i] = lsum;
@@ -571,6 +682,84 @@ struct MfmaKernel {
         item(a, blockIdx.x, blockIdx.y, blockIdx.z);
     }
 };
+
+// At least two resident waves per SIMD (a lane gets at most 256 registers),
+// except fp32 at D = 256, whose K, V, Q and accumulators take 64 registers
+// each: one wave per SIMD, 512 registers.
+template <int D, int G, int BS, int W, int WP, bool FUSED, int DT>
+__global__ __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu((DT == 2 && D == 256) ? 1 : VK_MFMA_WAVES_PER_EU)))
+void decode_mfma_kernel(DecodeArgs a) {
+    MfmaKernel<D, G, BS, W, WP, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128), FUSED, DT>::run(a);
+}
+
+template <int D, int G, int W, int WP, bool FUSED, int DT>
+hipError_t launch_bs(const DecodeArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    *ok = true;
+    const dim3 block(64 * W);
+    switch (bs) {
+        case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 8, W, WP, FUSED, DT>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 16, W, WP, FUSED, DT>), grid, block, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, G, 32, W, WP, FUSED, DT>), grid, block, 0, st, a); break;
+        default: *ok = false; return hipSuccess;
+    }
+    return hipGetLastError();
+}
+
+// Geometry sets, one translation unit each: 0 = grouped-query heads
+// (G = 4, 6, 8); 1 = multi-head (G = 1) and multi-query (G = 16).
+template <int SET, int W, int WP, bool FUSED, int DT>
+hipError_t launch_w(const DecodeArgs& a, int group, int head_dim, int bs, dim3 grid,
+                    hipStream_t st, bool* ok) {
+    if constexpr (SET == 0) {
+        if (group == 4 && head_dim == 128) return launch_bs<128, 4, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 6 && head_dim == 256) return launch_bs<256, 6, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 8 && head_dim == 128) return launch_bs<128, 8, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 8 && head_dim == 256) return launch_bs<256, 8, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+    } else {
+        if (group == 1 && head_dim == 128) return launch_bs<128, 1, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 1 && head_dim == 256) return launch_bs<256, 1, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 16 && head_dim == 128) return launch_bs<128, 16, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+        if (group == 16 && head_dim == 256) return launch_bs<256, 16, W, WP, FUSED, DT>(a, bs, grid, st, ok);
+    }
+    *ok = false;
+    return hipSuccess;
+}
+
+// Waves per workgroup (1, 2, 4), partitions per workgroup (1, or 2 with four
+// waves, split only) and the single-launch form (fp16 only) for one geometry
+// set and element type.
+template <int SET, int DT>
+hipError_t launch_mfma_set(const DecodeArgs& a, int group, int head_dim, int bs, int waves,
+                           int parts_per_wg, dim3 grid, hipStream_t st, bool* ok) {
+    *ok = false;
+    if (a.counters != nullptr && a.partition_size > 0) {
+        if constexpr (DT == 0) {
+            if (parts_per_wg != 1) return hipSuccess;
+            switch (waves) {
+                case 1: return launch_w<SET, 1, 1, true, DT>(a, group, head_dim, bs, grid, st, ok);
+                case 2: return launch_w<SET, 2, 2, true, DT>(a, group, head_dim, bs, grid, st, ok);
+                case 4: return launch_w<SET, 4, 4, true, DT>(a, group, head_dim, bs, grid, st, ok);
+                default: return hipSuccess;
+            }
+        }
+        return hipSuccess;
+    }
+    if (parts_per_wg == 2) {
+        if constexpr (DT == 0) {
+            if (waves == 4 && a.partition_size > 0)
+                return launch_w<SET, 4, 2, false, DT>(a, group, head_dim, bs, grid, st, ok);
+        }
+        return hipSuccess;
+    }
+    if (parts_per_wg != 1) return hipSuccess;
+    switch (waves) {
+        case 1: return launch_w<SET, 1, 1, false, DT>(a, group, head_dim, bs, grid, st, ok);
+        case 2: return launch_w<SET, 2, 2, false, DT>(a, group, head_dim, bs, grid, st, ok);
+        case 4: return launch_w<SET, 4, 4, false, DT>(a, group, head_dim, bs, grid, st, ok);
+        default: return hipSuccess;
+    }
+}
 
 }  // namespace
 }  // namespace vk

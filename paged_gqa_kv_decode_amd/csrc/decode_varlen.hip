@@ -213,6 +213,11 @@ hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, in
     if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, block_size, grid, stream, geometry_ok);
     if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, block_size, grid, stream, geometry_ok);
     if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, block_size, grid, stream, geometry_ok);
+    // multi-head: 16 query tokens of one head per tile; multi-query: 1 token x 16 heads
+    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, block_size, grid, stream, geometry_ok);
     *geometry_ok = false;
     return hipSuccess;
 }

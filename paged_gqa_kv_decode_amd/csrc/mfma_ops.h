@@ -50,6 +50,44 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// fp32 element type: one k-slot per lane group.
+__device__ __forceinline__ floatx4 mfma4_f32(uint32_t a, uint32_t b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a),
+                                                 __builtin_bit_cast(float, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma4_f32(float a, float b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 element type (K, V and q as bfloat16): the same products on the bf16
+// matrix instructions.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma32_bf16(const uint4& a, const uint4& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16_bf16(const uint2& a, const uint2& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                      __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+
+// Two weights as a bf16 pair (round to nearest even) and the pair of what
+// that rounding left (a - bf16(a), itself rounded): hi + lo carries a weight
+// to about 2^-16 relative, so the PV product done as two bf16 products keeps
+// the weights about as exact as the fp16 path does.
+__device__ __forceinline__ void pack_bf16_split(float a, float b, uint32_t& hi, uint32_t& lo) {
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    const bf2_t h = {(__bf16)a, (__bf16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const float ah = __builtin_bit_cast(float, hi << 16);
+    const float bh = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+    const bf2_t l = {(__bf16)(a - ah), (__bf16)(b - bh)};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // 8x8 fp16 transpose step: dims e of tokens 0..7 (lane group's k-slots) out of
 // 8 rows of 8 dims each.
 template <int E>

@@ -85,6 +85,7 @@ const char* vk_status_string(vk_status s) {
         case VK_ERR_SEQ_LEN: return "sequence length outside [1, max_blocks_per_seq * block_size]";
         case VK_ERR_SCRATCH_CAP: return "split-KV scratch over the cap";
         case VK_ERR_HIP: return "HIP error";
+        case VK_ERR_DTYPE: return "element type not supported";
         default: return "unknown status";
     }
 }
@@ -193,7 +194,10 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                       float scale, int32_t partition_size, int32_t max_num_partitions, float* out,
                       float* max_logits, float* exp_sums, float* tmp_out, uint32_t* counters,
-                      bool fused, void* stream) {
+                      bool fused, int32_t dtype, void* stream) {
+    if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16 && dtype != VK_DTYPE_F32)
+        return VK_ERR_DTYPE;
+    if (fused && dtype != VK_DTYPE_F16) return VK_ERR_DTYPE;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return VK_ERR_NULL_ARG;
     if (fused && (!out || (partition_size != 0 && !counters))) return VK_ERR_NULL_ARG;
     if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return VK_ERR_BAD_DIM;
@@ -242,10 +246,13 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     bool ok = false;
     int block = 0;
     int32_t kernel = t_kernel_choice;
-    // The in-place merge exists only in the matrix-core family, one
-    // partition per workgroup; two partitions per workgroup need a split.
-    if (fused && kernel == VK_KERNEL_DOT) kernel = VK_KERNEL_AUTO;
-    if (kernel == VK_KERNEL_MFMA_W4P2 && (fused || partition_size == 0)) kernel = VK_KERNEL_MFMA_W4;
+    // The in-place merge, the multi-head / multi-query geometries and the
+    // other element types exist only in the matrix-core family; two
+    // partitions per workgroup need an fp16 split without the in-place merge.
+    const bool mhq = group == 1 || group == 16;
+    if (kernel == VK_KERNEL_DOT && (fused || mhq || dtype != VK_DTYPE_F16)) kernel = VK_KERNEL_AUTO;
+    if (kernel == VK_KERNEL_MFMA_W4P2 && (fused || partition_size == 0 || dtype != VK_DTYPE_F16))
+        kernel = VK_KERNEL_MFMA_W4;
     const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
     const int64_t slots = kernel == VK_KERNEL_DOT ? 0 : wave_slots();
     const bool auto_waves = kernel == VK_KERNEL_AUTO || kernel == VK_KERNEL_MFMA;
@@ -280,8 +287,8 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
             kernel = waves == 4 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W2;
         }
         if (parts_per_wg == 2) grid.x = (grid.x + 1) / 2;
-        e = vk::launch_decode_mfma(a, group, head_dim, block_size, waves, parts_per_wg, grid, st,
-                                   &ok, &block);
+        e = vk::launch_decode_mfma(a, dtype, group, head_dim, block_size, waves, parts_per_wg,
+                                   grid, st, &ok, &block);
     }
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);
@@ -316,7 +323,21 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
-                       nullptr, false, stream);
+                       nullptr, false, VK_DTYPE_F16, stream);
+}
+
+vk_status vk_paged_gqa_decode_dt(int32_t dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                 int32_t partition_size, int32_t max_num_partitions, float* out,
+                                 float* max_logits, float* exp_sums, float* tmp_out,
+                                 void* stream) {
+    return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
+                       nullptr, false, dtype, stream);
 }
 
 vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const void* v_cache,
@@ -330,7 +351,7 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
-                       counters, true, stream);
+                       counters, true, VK_DTYPE_F16, stream);
 }
 
 vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_host,

@@ -68,11 +68,23 @@ struct AppendArgs {
 // false when no specialisation exists for the shape (host code checks first).
 hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,
                              dim3 grid, hipStream_t stream, bool* geometry_ok, int* block);
-// waves: 1, 2 or 4 wave64s per workgroup; parts_per_wg: partitions per
-// workgroup (1, or 2 with 4 waves in a split launch: grid.x = ceil(NP / 2)).
-hipError_t launch_decode_mfma(const DecodeArgs& a, int group, int head_dim, int block_size,
-                              int waves, int parts_per_wg, dim3 grid, hipStream_t stream,
-                              bool* geometry_ok, int* block);
+// dtype: element type of q, K and V (0 fp16, 1 bf16, 2 fp32); waves: 1, 2 or 4
+// wave64s per workgroup; parts_per_wg: partitions per workgroup (1, or 2 with
+// 4 waves in a split fp16 launch: grid.x = ceil(NP / 2)).  geometry_ok is
+// false when no instantiation matches (including the single-launch form or
+// two partitions per workgroup with bf16).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int group, int head_dim,
+                              int block_size, int waves, int parts_per_wg, dim3 grid,
+                              hipStream_t stream, bool* geometry_ok, int* block);
+hipError_t launch_decode_mfma_mhq(const DecodeArgs& a, int group, int head_dim, int block_size,
+                                  int waves, int parts_per_wg, dim3 grid, hipStream_t stream,
+                                  bool* geometry_ok);
+hipError_t launch_decode_mfma_bf16(const DecodeArgs& a, bool mhq, int group, int head_dim,
+                                   int block_size, int waves, int parts_per_wg, dim3 grid,
+                                   hipStream_t stream, bool* geometry_ok);
+hipError_t launch_decode_mfma_f32(const DecodeArgs& a, bool mhq, int group, int head_dim,
+                                  int block_size, int waves, int parts_per_wg, dim3 grid,
+                                  hipStream_t stream, bool* geometry_ok);
 // One wave per workgroup; grid (tiles * max(NP, 1), Hkv, S).  tokens_per_tile
 // receives 16 / G (query tokens per 16-column tile) for the caller's grid.
 hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, int block_size,

@@ -54,8 +54,10 @@ def run_hip(wl, partition_request: int, dev=None, kernel=None, keep_partials=Fal
     prev = vb.select_decode_kernel(kernel) if kernel is not None else None
     prev_order = vb.select_work_order(order) if order is not None else None
     try:
+        dtype = {"f16": vb.DTYPE_F16, "bf16": vb.DTYPE_BF16,
+                 "f32": vb.DTYPE_F32}[wl.meta.get("dtype", "f16")]
         step = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, partition_request,
-                             cu_count=cu_count, out=out, fused=fused)
+                             cu_count=cu_count, out=out, fused=fused, dtype=dtype)
         if step.tmp_out is not None and prefill_nan:
             step.max_logits.fill_(float("nan"))
             step.exp_sums.fill_(float("nan"))
