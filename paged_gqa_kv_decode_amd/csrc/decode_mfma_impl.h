@@ -58,6 +58,9 @@
 #ifndef VK_MFMA_WAVES_PER_EU
 #define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
 #endif
+#ifndef VK_MFMA_LDS_PF
+#define VK_MFMA_LDS_PF 1         // 16-bit types: next step's K/V loaded straight into LDS
+#endif
 #ifndef VK_MFMA_ORDER
 #define VK_MFMA_ORDER 1          // split launches of <= 64 sequences: longest-first work order
 #endif
@@ -370,9 +373,88 @@ struct MfmaKernel {
         pv(st, b, pb);
     }
 
+    // ---- Loads of the next step straight into LDS (16-bit types) ----
+    // While a wave computes a step, the next step's K/V are already on their
+    // way: global_load_lds_dwordx4 puts lane l's 16 bytes at base + 16 l of a
+    // per-wave LDS slot (one slot per 16-byte register of a Buf), so no
+    // registers hold them in flight; the step then reads its Buf back with
+    // ds_read_b128.  Lanes past the valid tokens load a clamped (valid) row
+    // and are zeroed on the way back.
+    static constexpr bool PF = VK_MFMA_LDS_PF && DT != 2 && T == 16;
+    static constexpr int SLOTS = NT * NKC + NDH * NJ;    // 16-byte registers of a Buf
+    static constexpr int WAVE_LDS = PF ? SLOTS * 64 * 16 : 0;   // bytes per wave
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+    template <bool FULL>
+    static __device__ __forceinline__ void issue_lds(const DecodeArgs& a, char* lds,
+                                                     const StepPages& sp, int g, int remain, int i,
+                                                     int c) {
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // elements
+        const uint16_t* kbase = a.k + (int64_t)g * BS * D;
+        const uint16_t* vbase = a.v + (int64_t)g * BS * D;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int tok = FULL ? 16 * tt + i : min(16 * tt + i, remain - 1);
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk)
+                __builtin_amdgcn_global_load_lds(kp + 4 * kk + c,
+                                                 (lds_ptr_t)(lds + (tt * NKC + kk) * 1024), 16, 0, 2);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int t0 = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
+            const int tok = FULL ? t0 : min(t0, remain - 1);
+            const uint4* vp = reinterpret_cast<const uint4*>(
+                vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                (int64_t)((sp.off_slot + tok) % BS) * D);
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh)
+                __builtin_amdgcn_global_load_lds(vp + 16 * dh + i,
+                                                 (lds_ptr_t)(lds + (NT * NKC + dh * NJ + j) * 1024),
+                                                 16, 0, 2);
+        }
+    }
+
+    template <bool FULL>
+    static __device__ __forceinline__ void read_lds(Buf& b, const char* lds, int remain, int lane,
+                                                    int i, int c) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) {
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + (tt * NKC + kk) * 1024 + 16 * lane);
+                b.kr[tt][kk] = (FULL || 16 * tt + i < remain) ? v : z;
+            }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh) {
+                const int tok = (j < 4) ? 4 * c + j : 16 + 4 * c + (j - 4);
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + (NT * NKC + dh * NJ + j) * 1024 + 16 * lane);
+                b.vr[dh][j] = (FULL || tok < remain) ? v : z;
+            }
+    }
+
+    // The compiler tracks neither order below (the loads into LDS go through
+    // M0, not through a pointer it follows), so both waits are explicit and
+    // are also compiler barriers:
+    //  * the step's loads into LDS have landed before it is read back;
+    //  * the read-back is done before the slot is loaded again.
+    static __device__ __forceinline__ void wait_lds_loads() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    static __device__ __forceinline__ void wait_lds_reads() {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
     static __device__ __forceinline__ void scan(const DecodeArgs& a, State& st, const QReg& qb,
                                                 int t_begin, int t_end, int g, int s, int wsub,
-                                                int lane, int i, int c, int pg_first, bool& bad) {
+                                                int lane, int i, int c, int pg_first, bool& bad,
+                                                char* lds) {
         const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
         for (int c0 = t_begin; c0 < t_end; c0 += CH) {
             const int c1 = min(t_end, c0 + CH);
@@ -389,16 +471,42 @@ struct MfmaKernel {
             const int first = c0 + wsub * T;
             constexpr int stride = WP * T;
             const int nfull = (first + T <= c1) ? (c1 - T - first) / stride + 1 : 0;
-            for (int k = 0; k < nfull; ++k) {
-                Buf b;
-                issue<true>(a, b, pg, g, first + k * stride - c0, T, i, c);
-                compute<true>(a, st, b, qb, T, c);
-            }
             const int tl = first + nfull * stride;
-            if (tl < c1) {
-                Buf bl;
-                issue<false>(a, bl, pg, g, tl - c0, c1 - tl, i, c);
-                compute<false>(a, st, bl, qb, c1 - tl, c);
+            if constexpr (PF) {
+                // step k + 1 is in flight to LDS while step k computes
+                if (nfull > 0)
+                    issue_lds<true>(a, lds, step_pages(pg, first - c0), g, T, i, c);
+                else if (tl < c1)
+                    issue_lds<false>(a, lds, step_pages(pg, tl - c0), g, c1 - tl, i, c);
+                for (int k = 0; k < nfull; ++k) {
+                    Buf b;
+                    wait_lds_loads();
+                    read_lds<true>(b, lds, T, lane, i, c);
+                    wait_lds_reads();
+                    if (k + 1 < nfull)
+                        issue_lds<true>(a, lds, step_pages(pg, first + (k + 1) * stride - c0), g, T, i, c);
+                    else if (tl < c1)
+                        issue_lds<false>(a, lds, step_pages(pg, tl - c0), g, c1 - tl, i, c);
+                    compute<true>(a, st, b, qb, T, c);
+                }
+                if (tl < c1) {
+                    Buf bl;
+                    wait_lds_loads();
+                    read_lds<false>(bl, lds, c1 - tl, lane, i, c);
+                    wait_lds_reads();
+                    compute<false>(a, st, bl, qb, c1 - tl, c);
+                }
+            } else {
+                for (int k = 0; k < nfull; ++k) {
+                    Buf b;
+                    issue<true>(a, b, pg, g, first + k * stride - c0, T, i, c);
+                    compute<true>(a, st, b, qb, T, c);
+                }
+                if (tl < c1) {
+                    Buf bl;
+                    issue<false>(a, bl, pg, g, tl - c0, c1 - tl, i, c);
+                    compute<false>(a, st, bl, qb, c1 - tl, c);
+                }
             }
         }
     }
@@ -406,7 +514,12 @@ struct MfmaKernel {
     // Workgroup `unit` of (KV head g, sequence s): partitions
     // [unit * PPW, unit * PPW + PPW), WP waves each.
     static __device__ void item(const DecodeArgs& a, const int unit, const int g, const int s) {
-        __shared__ float s_acc[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1];
+        // The per-wave prefetch slots and the end-of-partition merge area
+        // are never live together: one allocation holds both.
+        constexpr int MERGE_BYTES = (W > 1 ? W * G * D : 1) * 4;
+        constexpr int RAW_BYTES = W * WAVE_LDS > MERGE_BYTES ? W * WAVE_LDS : MERGE_BYTES;
+        __shared__ __attribute__((aligned(16))) char s_raw[RAW_BYTES];
+        auto& s_acc = *reinterpret_cast<float (*)[W > 1 ? W : 1][W > 1 ? G : 1][W > 1 ? D : 1]>(s_raw);
         __shared__ float s_m[W][G];
         __shared__ float s_l[W][G];
         __shared__ int s_bad[W];
@@ -481,7 +594,9 @@ struct MfmaKernel {
 
         // (With PPW > 1 the waves of an empty partition skip the scan but
         // still meet the others at the barrier below.)
-        if (PPW == 1 || active) scan(a, st, qb, t_begin, t_end, g, s, wsub, lane, i, c, pg_first, bad);
+        if (PPW == 1 || active)
+            scan(a, st, qb, t_begin, t_end, g, s, wsub, lane, i, c, pg_first, bad,
+                 s_raw + wave * WAVE_LDS);
 
         // Sum the per-lane exp-sums over the 4 lane groups (same head, same m).
         float lsum = st.l + __shfl_xor(st.l, 16);
@@ -511,6 +626,8 @@ struct MfmaKernel {
                         dst[acc_dim(t, c, rr)] = out_bad ? __builtin_nanf("") : st.acc[t][rr] / lsum;
             }
         } else {
+            // the merge area overlaps other waves' prefetch slots: all scans first
+            if constexpr (PF) __syncthreads();
             if (i < G) {
 #pragma unroll
                 for (int t = 0; t < NPT; ++t)
