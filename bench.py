@@ -256,7 +256,11 @@ def bench_varlen(args, wl, gen_s):
     ncopies = max(2, min(args.max_copies, -(-(4 * MALL_BYTES) // kv_bytes)))
     pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(ncopies - 1)]
     stream = torch.cuda.current_stream()
+    vb.select_varlen_kernel({"auto": vb.KERNEL_AUTO, "columns": vb.KERNEL_VARLEN_COLUMNS,
+                             "tiles": vb.KERNEL_VARLEN_TILES}[args.varlen_kernel])
     step0 = vb.VarlenStep(q, k, v, bt, sl, cu, wl.seq_lens, ql, wl.scale, P_req)
+    kname = {vb.KERNEL_VARLEN_COLUMNS: "varlen_columns",
+             vb.KERNEL_VARLEN_TILES: "varlen_tiles"}[step0.plan.kernel]
     P, NP, mq = step0.plan.partition_size, step0.plan.max_num_partitions, step0.max_q_len
     counter = [0]
 
@@ -320,7 +324,7 @@ def bench_varlen(args, wl, gen_s):
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "total_q": int(ql.sum()), "max_q_len": mq, "partition_size": P,
-                   "max_num_partitions": NP, "decode_kernel": "varlen_w1"},
+                   "max_num_partitions": NP, "decode_kernel": kname},
         "roofline": roof,
         "kernel_us": {"varlen_mean": round(float(dec_ms.mean()) * 1e3, 2),
                       "varlen_median": round(float(np.median(dec_ms)) * 1e3, 2),
@@ -348,6 +352,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None,
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4", "mfma4p2"])
+    ap.add_argument("--varlen-kernel", default="auto", choices=["auto", "columns", "tiles"],
+                    help="multi-token workloads: kernel (auto: tiles from 64 query tokens)")
     ap.add_argument("--order", default="auto", choices=["auto", "grid", "longest"],
                     help="work order of the matrix-core decode (A/B switch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

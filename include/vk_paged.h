@@ -97,9 +97,14 @@ enum {
     VK_KERNEL_MFMA_W1 = 3,  /* matrix cores, 1 wave64 per workgroup (A/B tuning) */
     VK_KERNEL_MFMA_W2 = 4,  /* matrix cores, 2 wave64s per workgroup (A/B tuning) */
     VK_KERNEL_MFMA_W4 = 5,  /* matrix cores, 4 wave64s per workgroup (A/B tuning) */
-    VK_KERNEL_MFMA_W4P2 = 6 /* matrix cores, 4 wave64s per workgroup over two
+    VK_KERNEL_MFMA_W4P2 = 6, /* matrix cores, 4 wave64s per workgroup over two
                                consecutive partitions, two waves each (split
                                launches; A/B tuning) */
+    /* vk_paged_gqa_varlen kernels; see vk_select_varlen_kernel */
+    VK_KERNEL_VARLEN_COLUMNS = 7, /* one wave per 16 (token, head) columns, keys
+                                     streamed through registers */
+    VK_KERNEL_VARLEN_TILES = 8    /* four waves per 128 columns, keys staged in
+                                     LDS tiles shared by all of them */
 };
 
 /* Work order of the matrix-core decode; see vk_select_work_order. */
@@ -261,12 +266,15 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
  * vk_plan_varlen — plan a vk_paged_gqa_varlen call (host only; no HIP call
  * when cu_count > 0).  seq_lens_host[s] (>= 1, within the page table) counts
  * all of sequence s's cached tokens including its q_lens_host[s] new query
- * tokens (0 <= q_len <= seq_len).  A column tile holds 16 / G query tokens of
- * one KV head's G heads; with partition_request == -1 the call is unsplit
- * when the tiles alone give one wave per wave slot (Hkv * sum ceil(q_len /
- * (16/G)) >= 8 * cu_count), otherwise split at 512 when
- * Hkv * sum ceil(q_len / (16/G)) * floor(L / 512) >= 33 * cu_count, else
- * 256.  NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
+ * tokens (0 <= q_len <= seq_len).  The kernel follows vk_select_varlen_kernel
+ * and is reported in plan_out->kernel.  A tile holds T query tokens of one KV
+ * head's G heads and runs on w waves: T = 16 / G, w = 1 for
+ * VK_KERNEL_VARLEN_COLUMNS; T = 128 / G, w = 4 for VK_KERNEL_VARLEN_TILES.
+ * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
+ * call is unsplit when the tiles alone give one wave per wave slot
+ * (w * n >= 8 * cu_count), otherwise split at 512 when
+ * n * floor(L / 512) summed per sequence >= 33 * cu_count, else 256.
+ * NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
  * against the cap.  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
  * q_len outside [0, seq_len]; VK_ERR_BAD_DIM if a q_len exceeds 65535.
  */
@@ -371,6 +379,19 @@ int32_t vk_select_decode_kernel(int32_t kernel);
  * previous setting, or -1 for an unknown value (setting kept).
  */
 int32_t vk_select_work_order(int32_t order);
+
+/*
+ * vk_select_varlen_kernel — A/B switch for this thread's later
+ * vk_plan_varlen and vk_paged_gqa_varlen calls: VK_KERNEL_AUTO (tiles when
+ * the longest query run of the batch is at least VK_VARLEN_TILE_MIN_Q
+ * tokens, else columns), VK_KERNEL_VARLEN_COLUMNS or VK_KERNEL_VARLEN_TILES.
+ * Both kernels compute the same rows to the same tolerance; the planner's
+ * split rule depends on the kernel, so plan and launch under the same
+ * setting.  Returns the previous setting, or -1 for an unknown value
+ * (setting kept).
+ */
+#define VK_VARLEN_TILE_MIN_Q 64
+int32_t vk_select_varlen_kernel(int32_t kernel);
 
 /* Human-readable name of a status code (static storage). */
 const char* vk_status_string(vk_status s);

@@ -22,13 +22,15 @@ STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_S
 DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4, KERNEL_MFMA_W4P2 = 3, 4, 5, 6
+KERNEL_VARLEN_COLUMNS, KERNEL_VARLEN_TILES = 7, 8
+VARLEN_TILE_MIN_Q = 64
 ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
             "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
             "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce",
-            "vk_paged_gqa_decode_dt")
+            "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel")
 
 
 class VkError(RuntimeError):
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.vk_select_decode_kernel.restype = i32
     L.vk_select_work_order.argtypes = [i32]
     L.vk_select_work_order.restype = i32
+    L.vk_select_varlen_kernel.argtypes = [i32]
+    L.vk_select_varlen_kernel.restype = i32
     L.vk_status_string.argtypes = [i32]
     L.vk_status_string.restype = ctypes.c_char_p
     L.vk_last_hip_error.argtypes = []
@@ -145,6 +149,13 @@ def select_work_order(order: int) -> int:
     prev = lib().vk_select_work_order(int(order))
     if prev < 0:
         raise ValueError(f"unknown work order {order}")
+    return prev
+
+
+def select_varlen_kernel(kernel: int) -> int:
+    prev = lib().vk_select_varlen_kernel(int(kernel))
+    if prev < 0:
+        raise ValueError(f"unknown varlen kernel {kernel}")
     return prev
 
 

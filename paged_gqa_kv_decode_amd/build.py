@@ -25,7 +25,8 @@ BENCH_LIB = os.path.join(PKG, "libvkbench.so")   # measurement-only kernels
 ARCH = "gfx950"
 
 SOURCES = ["vk_host.cpp", "decode_dot.hip", "decode_mfma.hip", "decode_mfma_mhq.hip",
-           "decode_mfma_bf16.hip", "decode_mfma_f32.hip", "decode_varlen.hip", "reduce.hip",
+           "decode_mfma_bf16.hip", "decode_mfma_f32.hip", "decode_varlen.hip",
+           "decode_varlen_tile.hip", "reduce.hip",
            "kv_append.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 

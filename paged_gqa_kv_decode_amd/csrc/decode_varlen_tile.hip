@@ -1,0 +1,383 @@
+// Many query tokens per sequence over the paged KV cache, causal: the
+// chunked-prefill shape of the variable-length attention (the vllm-metal
+// kernels page, cf-1.com/news/5525226, section "什么是 Paged Attention",
+// names one paged variable-length kernel for prefill and speculative decode;
+// the scores, masking and log2-space softmax are those of the column kernel
+// in decode_varlen.hip and of the decode).
+//
+// The column kernel gives each wave 16 (token, head) columns and streams the
+// keys through registers, so every 16 / G query tokens re-read the whole
+// context.  Here a workgroup of four waves owns 128 columns (BQ = 128 / G
+// query tokens x G heads) and streams the keys through LDS in 32-key tiles:
+// each tile is fetched once per workgroup and serves all 128 columns.
+//
+//  * Loads: the tile's K and V go straight from the paged cache into LDS
+//    (global_load_lds_dwordx4: lane l's 16 bytes land at slot base + 16 l),
+//    double-buffered, tile t + 1 in flight while tile t is computed.  A slot
+//    is one matrix-core operand register of the whole wave, so every LDS read
+//    is one conflict-free ds_read_b128 of 1 KiB.  K slot (kb, kk): lane
+//    (i, c) holds K[16 kb + i][32 kk + 8 c, +8); V slot (dh, j): lane (i, c)
+//    holds V[tok(j, c)][128 dh + 8 i, +8) with tok = 4c + j (j < 4) or
+//    16 + 4c + j - 4, the 32-key PV operand order of the decode.
+//  * Per wave and tile: S^T = K Q^T for two 16-column blocks (16x16x32
+//    products, Q^T held in registers), log2 online softmax per column with
+//    the causal limit applied by select on the diagonal tiles only, then
+//    O^T += V^T P^T (16x16x32, V transposed in registers by v_perm).
+//  * Waves whose columns see none of a tile's keys skip its arithmetic but
+//    still take part in its loads and barriers.
+//  * Page ids of tile t + 2 are loaded while tile t is computed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mfma_ops.h"
+#include "vk_kernels.h"
+
+namespace vk {
+namespace {
+
+using namespace mfma;
+
+template <int D, int G, int BS>
+struct TileKernel {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int CB = 2;                 // 16-column blocks per wave
+    static constexpr int BQ = NW * CB * 16 / G;  // query tokens per workgroup
+    static constexpr int NCOL = BQ * G;          // columns in use
+    static constexpr int KT = 32;                // keys per tile
+    static constexpr int NKC = D / 32;           // QK k-chunks of 32 dims
+    static constexpr int NDH = D / 128;          // 128-dim halves of a V row
+    static constexpr int NACC = NDH * 8;         // PV output tiles per column block
+    static constexpr int KSLOTS = 2 * NKC;       // [key block][dim chunk]
+    static constexpr int SLOTS = KSLOTS + 8 * NDH;
+    static constexpr int BUF = SLOTS * 1024;     // bytes of one tile in LDS
+    static constexpr int NPG = KT / BS;          // pages per tile
+    static_assert(KSLOTS % NW == 0 && (8 * NDH) % NW == 0, "slots split evenly over the waves");
+    static_assert(BS <= KT && KT % BS == 0, "a tile covers whole pages");
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+    struct Col {
+        floatx4 acc[NACC];
+        float m, l;
+    };
+
+    static __device__ __forceinline__ int tok_of(int j, int c) { return j < 4 ? 4 * c + j : 12 + 4 * c + j; }
+
+    // Page id of key offset x of the tile (lane k of `ids` holds page k);
+    // readlane keeps the ids in scalar registers rather than in an array.
+    static __device__ __forceinline__ int page_of(int x, int ids) {
+        int p = __builtin_amdgcn_readlane(ids, 0);
+#pragma unroll
+        for (int k = 1; k < NPG; ++k) p = (x >= k * BS) ? __builtin_amdgcn_readlane(ids, k) : p;
+        return p;
+    }
+
+    // Loads of the tile at key k0 into LDS buffer `lb`: this wave's share of
+    // the slots.  `last` is the tile's last valid key offset; later keys load
+    // that row again (their scores are masked).
+    static __device__ __forceinline__ void issue_tile(const DecodeArgs& a, char* lb, int ids, int last,
+                                                      int g, int wave, int i, int c) {
+        const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;
+        const int64_t head_off = (int64_t)g * BS * D;
+#pragma unroll
+        for (int u = 0; u < KSLOTS / NW; ++u) {
+            const int s = wave + NW * u;
+            const int kb = s / NKC, kk = s % NKC;
+            const int x = min(16 * kb + i, last);
+            const uint16_t* p = a.k + (int64_t)page_of(x, ids) * page_stride + head_off +
+                                (int64_t)(x % BS) * D + 32 * kk + 8 * c;
+            __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lb + s * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8 * NDH / NW; ++u) {
+            const int s = wave + NW * u;
+            const int dh = s / 8, j = s % 8;
+            const int x = min(tok_of(j, c), last);
+            const uint16_t* p = a.v + (int64_t)page_of(x, ids) * page_stride + head_off +
+                                (int64_t)(x % BS) * D + 128 * dh + 8 * i;
+            __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lb + (KSLOTS + s) * 1024), 16, 0, 0);
+        }
+    }
+
+    static __device__ __forceinline__ uint4 lds16(const char* lb, int slot, int lane) {
+        return *reinterpret_cast<const uint4*>(lb + slot * 1024 + 16 * lane);
+    }
+
+    // One tile for this wave's two column blocks; rem[cb]: keys of the tile
+    // the lane's column sees (MASK: some column sees fewer than 32).
+    template <bool MASK>
+    static __device__ __forceinline__ void compute(const DecodeArgs& a, Col (&st)[CB], const char* lb,
+                                                   const uint4 (&qb)[CB][NKC], const int (&rem)[CB],
+                                                   int lane, int c) {
+        floatx4 sc[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKC; ++kk) {
+            const uint4 k0 = lds16(lb, kk, lane);
+            const uint4 k1 = lds16(lb, NKC + kk, lane);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                sc[cb][0] = mfma32(k0, qb[cb][kk], sc[cb][0]);
+                sc[cb][1] = mfma32(k1, qb[cb][kk], sc[cb][1]);
+            }
+        }
+        uint4 pb[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            float x[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = mul_rounded(sc[cb][kb][r], a.scale_log2e);
+                    x[4 * kb + r] = (!MASK || 16 * kb + 4 * c + r < rem[cb]) ? v : -INFINITY;
+                }
+            float mx = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(st[cb].m, mx);
+            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = exp2_fast(st[cb].m - mref);
+            float p[8];
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                p[j] = exp2_fast(x[j] - mref);
+                ps += p[j];
+            }
+            st[cb].l = st[cb].l * alpha + ps;
+            st[cb].m = mnew;
+#pragma unroll
+            for (int t = 0; t < NACC; ++t) st[cb].acc[t] *= alpha;
+            pb[cb].x = pack_half2(p[0], p[1]);
+            pb[cb].y = pack_half2(p[2], p[3]);
+            pb[cb].z = pack_half2(p[4], p[5]);
+            pb[cb].w = pack_half2(p[6], p[7]);
+        }
+#pragma unroll
+        for (int dh = 0; dh < NDH; ++dh) {
+            uint4 vr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vr[j] = lds16(lb, KSLOTS + 8 * dh + j, lane);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                st[cb].acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr), pb[cb], st[cb].acc[dh * 8 + 0]);
+                st[cb].acc[dh * 8 + 1] = mfma32(vt_operand<1>(vr), pb[cb], st[cb].acc[dh * 8 + 1]);
+                st[cb].acc[dh * 8 + 2] = mfma32(vt_operand<2>(vr), pb[cb], st[cb].acc[dh * 8 + 2]);
+                st[cb].acc[dh * 8 + 3] = mfma32(vt_operand<3>(vr), pb[cb], st[cb].acc[dh * 8 + 3]);
+                st[cb].acc[dh * 8 + 4] = mfma32(vt_operand<4>(vr), pb[cb], st[cb].acc[dh * 8 + 4]);
+                st[cb].acc[dh * 8 + 5] = mfma32(vt_operand<5>(vr), pb[cb], st[cb].acc[dh * 8 + 5]);
+                st[cb].acc[dh * 8 + 6] = mfma32(vt_operand<6>(vr), pb[cb], st[cb].acc[dh * 8 + 6]);
+                st[cb].acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr), pb[cb], st[cb].acc[dh * 8 + 7]);
+            }
+        }
+    }
+
+    // Page ids of the tile at k0 (lane k < NPG: page k of the tile), clamped
+    // to the range's last page.
+    static __device__ __forceinline__ int load_ids(const int32_t* bt, int k0, int t_end, int lane) {
+        return lane < NPG ? bt[min(k0 / BS + lane, (t_end - 1) / BS)] : 0;
+    }
+    // Out-of-pool ids read page 0 instead and flag the tile.
+    static __device__ __forceinline__ int checked_ids(const DecodeArgs& a, int ids, int lane, bool& bad) {
+        const bool b = lane < NPG && (ids < 0 || (int64_t)ids >= a.num_blocks);
+        bad = __ballot(b) != 0;
+        return b ? 0 : ids;
+    }
+
+    static __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+    static __device__ void run(const VarlenArgs& va) {
+        __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+        const DecodeArgs& a = va.d;
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, c = lane >> 4;
+        // Later tiles see more keys: they start first.
+        const int tile = va.tiles - 1 - (int)(blockIdx.x % (unsigned)va.tiles);
+        const int part = (int)(blockIdx.x / (unsigned)va.tiles);
+        const int g = blockIdx.y, s = blockIdx.z;
+        const int q0 = va.cu_q[s], qlen = va.cu_q[s + 1] - q0;
+        if (qlen <= 0 || tile * BQ >= qlen) return;
+        const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
+        const int L = a.seq_lens[s];
+        const bool poison = L > a.max_blocks_per_seq * BS;
+        // The workgroup's key range ends where its last query token's does.
+        const int kv_end = L - qlen + min(qlen, (tile + 1) * BQ);
+        int t_begin = 0, t_end = kv_end;
+        if (P > 0) {
+            t_begin = part * P;
+            t_end = min(kv_end, t_begin + P);
+        }
+
+        // Columns: lane column i of block cb is workgroup column 32 wave + 16 cb + i.
+        bool valid[CB], col_poison[CB];
+        int lim[CB];
+        int64_t row[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int cw = 32 * wave + 16 * cb + i;
+            const int jt = tile * BQ + cw / G;
+            valid[cb] = cw < NCOL && jt < qlen;
+            lim[cb] = valid[cb] ? L - qlen + jt + 1 : 0;
+            row[cb] = ((int64_t)q0 + jt) * Hq + g * G + cw % G;
+            col_poison[cb] = P > 0 && part == NP - 1 && lim[cb] > t_begin + P;
+        }
+        if (t_end <= t_begin || poison) {   // uniform over the workgroup
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                if (valid[cb] && P == 0) {   // no visible key: zeros; poisoned: NaN
+                    const float z = (poison && lim[cb] > 0) ? __builtin_nanf("") : 0.f;
+                    float* o = a.out + row[cb] * D;
+                    for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(z, z, z, z);
+                } else if (valid[cb] && poison && lim[cb] > t_begin) {   // the partials the reduce reads
+                    const int64_t pr = row[cb] * NP + part;
+                    if (c == 0) a.max_logits[pr] = a.exp_sums[pr] = __builtin_nanf("");
+                    const float z = __builtin_nanf("");
+                    float* o = a.tmp_out + pr * D;
+                    for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(z, z, z, z);
+                }
+            }
+            return;
+        }
+
+        const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+        int ids_next = load_ids(bt, t_begin, t_end, lane);
+        uint4 qb[CB][NKC];
+        int e_lim[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint4* qp = reinterpret_cast<const uint4*>(a.q + (valid[cb] ? row[cb] : 0) * D);
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk) qb[cb][kk] = valid[cb] ? qp[4 * kk + c] : make_uint4(0, 0, 0, 0);
+            // keys of the range this column sees (other columns: all, harmlessly)
+            e_lim[cb] = valid[cb] ? min(lim[cb], t_end) : t_end;
+        }
+        // The wave's key span: tiles past its largest limit are skipped, tiles
+        // below its smallest need no mask.
+        int w_max = max(valid[0] ? e_lim[0] : t_begin, valid[1] ? e_lim[1] : t_begin);
+        int w_min = min(e_lim[0], e_lim[1]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            w_max = max(w_max, __shfl_xor(w_max, off));
+            w_min = min(w_min, __shfl_xor(w_min, off));
+        }
+
+        Col st[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int t = 0; t < NACC; ++t) st[cb].acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            st[cb].m = -INFINITY;
+            st[cb].l = 0.f;
+        }
+        const int nt = (t_end - t_begin + KT - 1) / KT;
+        bool bad = false, tbad_cur = false;
+        {
+            const int ids = checked_ids(a, ids_next, lane, tbad_cur);
+            issue_tile(a, lds, ids, min(KT, t_end - t_begin) - 1, g, wave, i, c);
+            if (nt > 1) ids_next = load_ids(bt, t_begin + KT, t_end, lane);
+        }
+        for (int t = 0; t < nt; ++t) {
+            const int k0 = t_begin + t * KT;
+            // This wave's loads of tile t (and the next ids) have landed; the
+            // barrier makes every wave's visible and closes the reads of the
+            // buffer that is loaded next.
+            wait_loads();
+            __syncthreads();
+            bool tbad_next = false;
+            if (t + 1 < nt) {
+                const int ids = checked_ids(a, ids_next, lane, tbad_next);
+                issue_tile(a, lds + ((t + 1) & 1) * BUF, ids, min(KT, t_end - k0 - KT) - 1, g, wave, i, c);
+                if (t + 2 < nt) ids_next = load_ids(bt, k0 + 2 * KT, t_end, lane);
+            }
+            if (k0 < w_max) {
+                bad = bad || tbad_cur;
+                const char* lb = lds + (t & 1) * BUF;
+                if (k0 + KT <= w_min) {
+                    const int rem[CB] = {KT, KT};
+                    compute<false>(a, st, lb, qb, rem, lane, c);
+                } else {
+                    const int rem[CB] = {e_lim[0] - k0, e_lim[1] - k0};
+                    compute<true>(a, st, lb, qb, rem, lane, c);
+                }
+            }
+            tbad_cur = tbad_next;
+        }
+
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            float lsum = st[cb].l + __shfl_xor(st[cb].l, 16);
+            lsum += __shfl_xor(lsum, 32);
+            if (!valid[cb]) continue;
+            if (P == 0 && lim[cb] <= 0) {   // a query that sees no key: zeros
+                float* o = a.out + row[cb] * D;
+                for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+                continue;
+            }
+            if (lim[cb] <= t_begin) continue;   // this column does not see this partition
+            const bool out_bad = bad || col_poison[cb];
+            float* dst;
+            if (P == 0) {
+                dst = a.out + row[cb] * D;
+            } else {
+                const int64_t pr = row[cb] * NP + part;
+                dst = a.tmp_out + pr * D;
+                if (c == 0) {
+                    a.max_logits[pr] = st[cb].m;
+                    a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                }
+            }
+            const float inv = 1.f / lsum;
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = out_bad ? __builtin_nanf("") : st[cb].acc[dh * 8 + e][rr] * inv;
+                    float4* o = reinterpret_cast<float4*>(dst + 128 * dh + 8 * (4 * c + rr));
+                    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+                }
+        }
+    }
+};
+
+template <int D, int G, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+void varlen_tile_kernel(VarlenArgs a) {
+    TileKernel<D, G, BS>::run(a);
+}
+
+template <int D, int G>
+hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    *ok = true;
+    switch (bs) {
+        case 8: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 8>), grid, dim3(256), 0, st, a); break;
+        case 16: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 16>), grid, dim3(256), 0, st, a); break;
+        case 32: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 32>), grid, dim3(256), 0, st, a); break;
+        default: *ok = false; return hipSuccess;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int varlen_tile_tokens(int group) { return group > 0 && group <= 16 ? 128 / group : 0; }
+
+hipError_t launch_varlen_tile(const VarlenArgs& a, int group, int head_dim, int block_size,
+                              dim3 grid, hipStream_t stream, bool* geometry_ok) {
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, block_size, grid, stream, geometry_ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, block_size, grid, stream, geometry_ok);
+    *geometry_ok = false;
+    return hipSuccess;
+}
+
+}  // namespace vk

@@ -19,6 +19,13 @@ thread_local vk_plan t_last_plan = {};
 thread_local int32_t t_last_hip_error = 0;
 thread_local int32_t t_kernel_choice = VK_KERNEL_AUTO;
 thread_local int32_t t_order_choice = VK_ORDER_AUTO;
+thread_local int32_t t_varlen_choice = VK_KERNEL_AUTO;
+
+// The multi-token kernel for a batch whose longest query run is max_q tokens.
+int32_t varlen_kernel(int64_t max_q) {
+    if (t_varlen_choice != VK_KERNEL_AUTO) return t_varlen_choice;
+    return max_q >= VK_VARLEN_TILE_MIN_Q ? VK_KERNEL_VARLEN_TILES : VK_KERNEL_VARLEN_COLUMNS;
+}
 
 struct Geometry {
     int hq, hkv, d;
@@ -102,6 +109,15 @@ int32_t vk_select_decode_kernel(int32_t kernel) {
     if (kernel < VK_KERNEL_AUTO || kernel > VK_KERNEL_MFMA_W4P2) return -1;
     const int32_t prev = t_kernel_choice;
     t_kernel_choice = kernel;
+    return prev;
+}
+
+int32_t vk_select_varlen_kernel(int32_t kernel) {
+    if (kernel != VK_KERNEL_AUTO && kernel != VK_KERNEL_VARLEN_COLUMNS &&
+        kernel != VK_KERNEL_VARLEN_TILES)
+        return -1;
+    const int32_t prev = t_varlen_choice;
+    t_varlen_choice = kernel;
     return prev;
 }
 
@@ -370,14 +386,19 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     if (cu_count < 0) return VK_ERR_BAD_DIM;
     const int64_t cap_tokens = (int64_t)max_blocks_per_seq * block_size;
     if (cap_tokens > INT32_MAX) return VK_ERR_BAD_DIM;
-    const int tpt = vk::varlen_tokens_per_tile(num_q_heads / num_kv_heads);
-    int64_t max_len = 0, total_q = 0, tiles = 0, full512 = 0, full256 = 0, max_q = 0;
+    int64_t max_q = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) max_q = std::max<int64_t>(max_q, q_lens_host[s]);
+    const int32_t kernel = varlen_kernel(max_q);
+    const int group = num_q_heads / num_kv_heads;
+    const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
+    const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
+    const int waves_per_tile = tiled ? 4 : 1;
+    int64_t max_len = 0, total_q = 0, tiles = 0, full512 = 0, full256 = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int64_t L = seq_lens_host[s], ql = q_lens_host[s];
         if (L < 1 || L > cap_tokens) return VK_ERR_SEQ_LEN;
         if (ql < 0 || ql > L) return VK_ERR_SEQ_LEN;
         if (L > max_len) max_len = L;
-        if (ql > max_q) max_q = ql;
         total_q += ql;
         const int64_t t = (ql + tpt - 1) / tpt;
         tiles += t;
@@ -398,12 +419,13 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     vk_plan p = {};
     p.cu_count = cu_count;
     p.budget = (int64_t)VK_DEFAULT_BUDGET_PER_CU * cu_count;
+    p.kernel = kernel;
     int32_t P = partition_request;
     if (P == -1) {
-        // One wave per (column tile, KV head) when unsplit: enough of them to
-        // fill the wave slots once (8 per CU) needs no split; otherwise the
-        // decode's rule over (tile, full partition) units.
-        if ((int64_t)num_kv_heads * tiles >= 8 * (int64_t)cu_count)
+        // Unsplit when the (tile, KV head) workgroups fill the wave slots
+        // once (8 per CU); otherwise the decode's rule over (tile, full
+        // partition) units.
+        if ((int64_t)waves_per_tile * num_kv_heads * tiles >= 8 * (int64_t)cu_count)
             P = 0;
         else
             P = ((int64_t)num_kv_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
@@ -453,7 +475,9 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
         return VK_ERR_PARTITION;
     }
     const int group = num_q_heads / num_kv_heads;
-    const int tpt = vk::varlen_tokens_per_tile(group);
+    const int32_t kernel = varlen_kernel(max_q_len);
+    const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
+    const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
     const int64_t tiles = (max_q_len + tpt - 1) / tpt;
     const int64_t gx = tiles * (partition_size == 0 ? 1 : max_num_partitions);
     if (gx > INT32_MAX) return VK_ERR_BAD_DIM;
@@ -483,21 +507,23 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
     va.tiles = (int32_t)tiles;
     const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);
     bool ok = false;
-    hipError_t e = vk::launch_decode_varlen(va, group, head_dim, block_size, grid,
-                                            static_cast<hipStream_t>(stream), &ok);
+    hipError_t e = tiled ? vk::launch_varlen_tile(va, group, head_dim, block_size, grid,
+                                                  static_cast<hipStream_t>(stream), &ok)
+                         : vk::launch_decode_varlen(va, group, head_dim, block_size, grid,
+                                                    static_cast<hipStream_t>(stream), &ok);
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);
     vk_plan p = {};
     p.partition_size = partition_size;
     p.max_num_partitions = max_num_partitions;
-    p.kernel = VK_KERNEL_MFMA_W1;
+    p.kernel = kernel;
     p.scratch_bytes = partition_size == 0 ? 0
                       : (uint64_t)total_q * num_q_heads * (uint64_t)max_num_partitions *
                             (uint64_t)(head_dim + 2) * 4u;
     p.grid[0] = (int32_t)grid.x;
     p.grid[1] = (int32_t)grid.y;
     p.grid[2] = (int32_t)grid.z;
-    p.block = 64;
+    p.block = tiled ? 256 : 64;
     p.work_order = VK_ORDER_GRID;
     t_last_plan = p;
     return VK_OK;

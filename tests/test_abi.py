@@ -223,3 +223,38 @@ def test_plan_varlen_scratch_cap():
     with pytest.raises(vb.VkError) as e:
         _pv([4096], [4], (32, 8, 128), P=256, cu=4, cap=1000)
     assert e.value.name == "SCRATCH_CAP"
+
+
+def test_plan_varlen_kernel_choice():
+    # The longest query run decides: >= 64 tokens -> LDS tiles, else columns.
+    assert _pv([2000, 1500], [63, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
+    assert _pv([2000, 1500], [64, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
+    prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
+    try:
+        assert _pv([2000, 1500], [100, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
+        vb.select_varlen_kernel(vb.KERNEL_VARLEN_TILES)
+        assert _pv([2000, 1500], [2, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
+    finally:
+        assert vb.select_varlen_kernel(prev) == vb.KERNEL_VARLEN_TILES
+    with pytest.raises(ValueError):
+        vb.select_varlen_kernel(vb.KERNEL_MFMA_W1)
+
+
+def test_plan_varlen_tiles_split_rule():
+    # G = 4: 128 / 4 = 32 tokens per tile; tiles 4 + 2 = 6, n = 8 * 6 = 48
+    # (KV head, tile) workgroups of 4 waves = 192 waves.
+    p = _pv([2000, 1500], [100, 64], (32, 8, 128), cu=24)          # 192 >= 8 * 24
+    assert (p.partition_size, p.max_num_partitions, p.scratch_bytes) == (0, 1, 0)
+    assert p.work_full_parts == 48
+    # 192 < 8 * 25 -> split; full-512 units 8 * (4 * 3 + 2 * 2) = 128 < 33 * 25 -> 256
+    p = _pv([2000, 1500], [100, 64], (32, 8, 128), cu=25)
+    assert (p.partition_size, p.max_num_partitions) == (256, 8)
+    assert p.scratch_bytes == 164 * 32 * 8 * 130 * 4
+    # one 16k sequence, 64 query tokens: 2 tiles, 64 waves < 8 * 10 -> split;
+    # full-512 units 8 * 2 * 32 = 512 >= 33 * 10 -> 512
+    p = _pv([16384], [64], (32, 8, 128), cu=10)
+    assert (p.partition_size, p.max_num_partitions) == (512, 32)
+    # G = 6, D = 256: 21 tokens per tile; 4 chunks of 1024 -> 4 * 4 * 49 = 784
+    # workgroups, 3136 waves >= 8 * 256: the chunked-prefill shape runs unsplit.
+    p = _pv([3000, 5000, 8000, 2048], [1024] * 4, (24, 4, 256), bs=32, cu=256)
+    assert (p.kernel, p.partition_size, p.work_full_parts) == (vb.KERNEL_VARLEN_TILES, 0, 784)

@@ -1,0 +1,151 @@
+"""GPU parity of the LDS-tiled multi-token kernel (VK_KERNEL_VARLEN_TILES:
+four waves per 128 (token, head) columns, K/V tiles shared through LDS)
+against the float64 oracle.
+
+Same tolerance as the decode: max |gpu - ref| <= 2e-3 and per-row relative
+L2 <= 1e-2.  Every (G, D) instantiation and page size, unsplit and both
+partition sizes, with query runs shorter than, equal to and longer than a
+workgroup's 128 / G tokens, prefixes that put the causal diagonal off the
+32-key tiles, an empty sequence and canaries around every page.
+"""
+import copy
+
+import numpy as np
+import pytest
+
+from gpu_helpers import assert_parity, say
+from paged_gqa_kv_decode_amd import binding as vb
+from paged_gqa_kv_decode_amd.workloads import make_varlen, make_varlen_custom
+from test_gpu_varlen import _dev, oracle_varlen, run_varlen, sampled_rows_ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def tiles():
+    prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_TILES)
+    yield
+    vb.select_varlen_kernel(prev)
+
+
+def test_prefill_workload_picks_tiles_and_matches(orc):
+    """The chunked-prefill workload: auto picks the tiled kernel, unsplit."""
+    wl = make_varlen("prefill4_chunk1k")
+    gpu, plan, _ = run_varlen(wl, -1)
+    assert plan.kernel == vb.KERNEL_VARLEN_TILES and plan.partition_size == 0
+    assert vb.last_plan().kernel == vb.KERNEL_VARLEN_TILES
+    assert np.all(np.isfinite(gpu))
+    rows, ref = sampled_rows_ref(orc, wl, 64, seed=9)
+    assert_parity(gpu[rows], ref, f"prefill4_chunk1k tiles ({len(rows)} rows)")
+
+
+GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256), (16, 16, 128), (8, 8, 256),
+         (16, 1, 128), (16, 1, 256)]
+CASES = [(g, bs) for g in GEOMS for bs in (8, 16, 32)]
+
+
+@pytest.mark.parametrize("geom,bs", CASES, ids=[f"{g[0]}-{g[1]}-{g[2]}-bs{b}" for g, b in CASES])
+def test_tiles_all_specialisations(orc, tiles, geom, bs):
+    Hq, Hkv, D = geom
+    G = Hq // Hkv
+    bq = 128 // G
+    lens = [1, 100, 700, 64, 1100, 5, 40, 900]
+    qlens = [1, 40, bq + 1, 0, 2 * bq, 5, 33, min(900, 3 * bq + 7)]
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim=D, block_size=bs, seed=Hq * 7 + D + bs, pool_factor=1.5,
+                            canaries=True, sigma_k=2.0)
+    ref = oracle_varlen(orc, wl)
+    for P in (0, 256, 512):
+        gpu, plan, _ = run_varlen(wl, P)
+        assert plan.kernel == vb.KERNEL_VARLEN_TILES
+        assert_parity(gpu, ref, f"tiles {geom} bs{bs} P{P}")
+
+
+def test_tiles_whole_prompt_and_long_chunks(orc, tiles):
+    """q_len = L (a whole prompt, the diagonal from key 0) and chunks on long
+    prefixes, several workgroups per sequence."""
+    wl = make_varlen_custom(seq_lens=[700, 3000, 129], q_lens=[700, 300, 129], num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16, seed=31, canaries=True)
+    ref = oracle_varlen(orc, wl)
+    for P in (0, 512):
+        gpu, _, _ = run_varlen(wl, P)
+        assert_parity(gpu, ref, f"tiles prompt/chunks P{P}")
+
+
+def test_tiles_agree_with_columns(orc):
+    """Both multi-token kernels on one batch: each within the oracle's bar."""
+    wl = make_varlen_custom(seq_lens=[300, 1000, 77], q_lens=[90, 64, 70], num_q_heads=24,
+                            num_kv_heads=4, head_dim=256, block_size=32, seed=8)
+    ref = oracle_varlen(orc, wl)
+    out = {}
+    for k in (vb.KERNEL_VARLEN_COLUMNS, vb.KERNEL_VARLEN_TILES):
+        prev = vb.select_varlen_kernel(k)
+        try:
+            out[k], plan, _ = run_varlen(wl, 0)
+        finally:
+            vb.select_varlen_kernel(prev)
+        assert plan.kernel == k
+        assert_parity(out[k], ref, f"kernel {k}")
+    assert np.max(np.abs(out[vb.KERNEL_VARLEN_COLUMNS] - out[vb.KERNEL_VARLEN_TILES])) <= 2e-3
+
+
+def test_tiles_causality_is_structural(tiles):
+    """Changing the K/V of the last token of every sequence leaves every row
+    that does not see it bit-identical, and changes the last row."""
+    wl = make_varlen_custom(seq_lens=[600, 200], q_lens=[140, 200], num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16, seed=12)
+    a, _, _ = run_varlen(wl, 0)
+    w2 = copy.copy(wl)
+    w2.k_cache = wl.k_cache.copy()
+    w2.v_cache = wl.v_cache.copy()
+    for s, L in enumerate(wl.seq_lens):
+        b = wl.block_tables[s, (L - 1) // 16]
+        w2.k_cache[b, :, (L - 1) % 16] *= np.float16(-1)
+        w2.v_cache[b, :, (L - 1) % 16] += np.float16(3)
+    b_, _, _ = run_varlen(w2, 0)
+    cu = wl.meta["cu_q"]
+    for s in range(2):
+        last = cu[s + 1] - 1
+        assert np.array_equal(a[cu[s]:last], b_[cu[s]:last]), "a row saw a later token"
+        assert not np.array_equal(a[last], b_[last])
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_tiles_device_side_guards(tiles, P):
+    """Sequence 1: a page id outside the pool (NaN rows); sequence 2: length
+    beyond the page table (NaN rows, nothing read); sequence 3: q_len > L
+    (its first rows see nothing: zeros); sequence 4: q_len = 0 (no rows)."""
+    import torch
+    lens, qlens = [300, 300, 300, 4, 20], [70, 70, 70, 6, 0]
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=16, num_kv_heads=2,
+                            head_dim=128, block_size=16, seed=4, pool_factor=2.0)
+    q, k, v, bt, sl, cu = _dev(wl)
+    bt_h = wl.block_tables.copy()
+    bt_h[1, 3] = wl.num_blocks + 7       # keys 48..63: every row of sequence 1 sees them
+    bt = torch.from_numpy(bt_h).cuda()
+    sl_h = wl.seq_lens.copy()
+    sl_h[2] = bt_h.shape[1] * 16 + 100
+    sl = torch.from_numpy(sl_h).cuda()
+    T = wl.q.shape[0]
+    NP = -(-int(sl_h.max()) // P) if P else 1
+    out = torch.full((T, 16, 128), 7.0, device="cuda")
+    if P:
+        ml = torch.empty((T, 16, NP), device="cuda")
+        es = torch.empty((T, 16, NP), device="cuda")
+        to = torch.empty((T, 16, NP, 128), device="cuda")
+        vb.paged_gqa_varlen(q, k, v, bt, sl, cu, 70, wl.scale, P, NP, None, ml, es, to)
+        assert vb.last_plan().kernel == vb.KERNEL_VARLEN_TILES
+        vb.paged_gqa_varlen_reduce(ml, es, to, sl, cu, 70, P, out)
+    else:
+        vb.paged_gqa_varlen(q, k, v, bt, sl, cu, 70, wl.scale, 0, 1, out)
+        assert vb.last_plan().kernel == vb.KERNEL_VARLEN_TILES
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    c = wl.meta["cu_q"]
+    say(f"[tiles guards] P={P}")
+    assert np.all(np.isfinite(o[c[0]:c[1]]))
+    assert np.all(np.isnan(o[c[1]:c[2]])), "bad page id must poison the rows that see it"
+    assert np.all(np.isnan(o[c[2]:c[3]])), "length beyond the table must poison"
+    # sequence 3: L = 4, q_len = 6: rows 0, 1 see nothing, rows 2.. see 1..4 tokens
+    assert np.all(o[c[3]:c[3] + 2] == 0.0)
+    assert np.all(np.isfinite(o[c[3] + 2:c[4]]))
