@@ -36,11 +36,18 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function"]
 
 
+# Per-source flags.  The LDS-tiled multi-token kernel keeps its matrix-core
+# accumulators in VGPRs: with the default AGPR form the compiler copied all
+# of them out of AGPRs on every key tile for the (rarely taken) softmax
+# rescale.
+EXTRA = {"decode_varlen_tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC, *COMMON, *lang, "-c", path, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

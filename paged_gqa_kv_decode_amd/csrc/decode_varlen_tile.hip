@@ -13,7 +13,7 @@
 //
 //  * Loads: the tile's K and V go straight from the paged cache into LDS
 //    (global_load_lds_dwordx4: lane l's 16 bytes land at slot base + 16 l),
-//    double-buffered, tile t + 1 in flight while tile t is computed.  A slot
+//    four buffers, tiles t + 1 .. t + 3 in flight while tile t is computed.  A slot
 //    is one matrix-core operand register of the whole wave, so every LDS read
 //    is one conflict-free ds_read_b128 of 1 KiB.  K slot (kb, kk): lane
 //    (i, c) holds K[16 kb + i][32 kk + 8 c, +8); V slot (dh, j): lane (i, c)
@@ -22,10 +22,12 @@
 //  * Per wave and tile: S^T = K Q^T for two 16-column blocks (16x16x32
 //    products, Q^T held in registers), log2 online softmax per column with
 //    the causal limit applied by select on the diagonal tiles only, then
-//    O^T += V^T P^T (16x16x32, V transposed in registers by v_perm).
+//    O^T += V^T P^T (16x16x32, V transposed in registers by v_perm).  The
+//    softmax's exponent reference trails the running max by up to 2^8, so
+//    the accumulators are rescaled only on the rare tiles that move it.
 //  * Waves whose columns see none of a tile's keys skip its arithmetic but
 //    still take part in its loads and barriers.
-//  * Page ids of tile t + 2 are loaded while tile t is computed.
+//  * Page ids of a tile are loaded two tiles ahead of its K/V loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,14 +53,51 @@ struct TileKernel {
     static constexpr int SLOTS = KSLOTS + 8 * NDH;
     static constexpr int BUF = SLOTS * 1024;     // bytes of one tile in LDS
     static constexpr int NPG = KT / BS;          // pages per tile
+    static constexpr int NBUF = 4;               // tiles in LDS: 3 in flight while 1 is computed
+    static constexpr int ISSUE = SLOTS / NW;     // loads into LDS per wave and tile
     static_assert(KSLOTS % NW == 0 && (8 * NDH) % NW == 0, "slots split evenly over the waves");
     static_assert(BS <= KT && KT % BS == 0, "a tile covers whole pages");
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+    // Per column: m is the running max score (log2 units); the weights are
+    // exp2(score - r) against a reference r that trails m by at most kTau, and
+    // l sums them.  r moves (and acc, l are rescaled) only when m outgrows it
+    // by more than kTau, so after the first tiles of a row the rescale is
+    // skipped; the weights stay <= 2^kTau, well inside fp16.
+    static constexpr float kTau = 8.f;
     struct Col {
         floatx4 acc[NACC];
-        float m, l;
+        float m, r, l;
     };
+
+    // Loads into LDS (lane l's 4 or 16 bytes land at lds + 4 l or + 16 l).
+    // Issued as inline assembly so that the compiler does not see them: it
+    // would otherwise wait for every one of them (vmcnt(0)) before each LDS
+    // read, since it cannot tell which buffer they fill; the kernel orders
+    // them itself (wait_tile, lds_barrier).  M0 holds the LDS address and is
+    // restored afterwards.
+    static __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+    }
+    // Scalar base + 32-bit lane offset (bytes): no per-lane address arithmetic.
+    static __device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds) {
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+    }
+    static __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+    }
+    static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
+        return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+    }
 
     static __device__ __forceinline__ int tok_of(int j, int c) { return j < 4 ? 4 * c + j : 12 + 4 * c + j; }
 
@@ -74,10 +113,37 @@ struct TileKernel {
     // Loads of the tile at key k0 into LDS buffer `lb`: this wave's share of
     // the slots.  `last` is the tile's last valid key offset; later keys load
     // that row again (their scores are masked).
-    static __device__ __forceinline__ void issue_tile(const DecodeArgs& a, char* lb, int ids, int last,
+    static __device__ __forceinline__ void issue_tile(const DecodeArgs& a, char* lbuf, int ids, int last,
                                                       int g, int wave, int i, int c) {
+        const uint32_t lb = lds_addr(lbuf);
         const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;
         const int64_t head_off = (int64_t)g * BS * D;
+        if constexpr (BS >= 16) {
+            if (last == KT - 1) {
+                // A whole tile with pages of >= 16 tokens: each slot's 16 keys
+                // sit in one page, so the page base is wave-uniform (scalar
+                // registers) and each lane adds a fixed in-page offset.
+#pragma unroll
+                for (int u = 0; u < KSLOTS / NW; ++u) {
+                    const int s = wave + NW * u;
+                    const int kb = s / NKC, kk = s % NKC;
+                    const int page = __builtin_amdgcn_readlane(ids, (16 * kb) / BS);
+                    const uint16_t* pb = a.k + (int64_t)page * page_stride + head_off;
+                    const int off = ((16 * kb + i) % BS) * D + 32 * kk + 8 * c;
+                    dma16_s(pb, 2u * (uint32_t)off, lb + s * 1024);
+                }
+#pragma unroll
+                for (int u = 0; u < 8 * NDH / NW; ++u) {
+                    const int s = wave + NW * u;
+                    const int dh = s / 8, j = s % 8;
+                    const int page = __builtin_amdgcn_readlane(ids, j < 4 ? 0 : 16 / BS);
+                    const uint16_t* pb = a.v + (int64_t)page * page_stride + head_off;
+                    const int off = (tok_of(j, c) % BS) * D + 128 * dh + 8 * i;
+                    dma16_s(pb, 2u * (uint32_t)off, lb + (KSLOTS + s) * 1024);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < KSLOTS / NW; ++u) {
             const int s = wave + NW * u;
@@ -85,7 +151,7 @@ struct TileKernel {
             const int x = min(16 * kb + i, last);
             const uint16_t* p = a.k + (int64_t)page_of(x, ids) * page_stride + head_off +
                                 (int64_t)(x % BS) * D + 32 * kk + 8 * c;
-            __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lb + s * 1024), 16, 0, 0);
+            dma16(p, lb + s * 1024);
         }
 #pragma unroll
         for (int u = 0; u < 8 * NDH / NW; ++u) {
@@ -94,7 +160,7 @@ struct TileKernel {
             const int x = min(tok_of(j, c), last);
             const uint16_t* p = a.v + (int64_t)page_of(x, ids) * page_stride + head_off +
                                 (int64_t)(x % BS) * D + 128 * dh + 8 * i;
-            __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lb + (KSLOTS + s) * 1024), 16, 0, 0);
+            dma16(p, lb + (KSLOTS + s) * 1024);
         }
     }
 
@@ -138,19 +204,25 @@ struct TileKernel {
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mnew = fmaxf(st[cb].m, mx);
-            const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = exp2_fast(st[cb].m - mref);
+            st[cb].m = mnew;
+            const bool grow = mnew > st[cb].r + kTau;
+            if (__ballot(grow) != 0) {   // some column of the block moves its reference
+                const float rnew = grow ? mnew : st[cb].r;
+                const float alpha = grow ? exp2_fast(st[cb].r - rnew) : 1.f;   // r = -inf: 0
+                st[cb].r = rnew;
+                st[cb].l *= alpha;
+#pragma unroll
+                for (int t = 0; t < NACC; ++t) st[cb].acc[t] *= alpha;
+            }
+            const float rref = (st[cb].r == -INFINITY) ? 0.f : st[cb].r;
             float p[8];
             float ps = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                p[j] = exp2_fast(x[j] - mref);
+                p[j] = exp2_fast(x[j] - rref);
                 ps += p[j];
             }
-            st[cb].l = st[cb].l * alpha + ps;
-            st[cb].m = mnew;
-#pragma unroll
-            for (int t = 0; t < NACC; ++t) st[cb].acc[t] *= alpha;
+            st[cb].l += ps;
             pb[cb].x = pack_half2(p[0], p[1]);
             pb[cb].y = pack_half2(p[2], p[3]);
             pb[cb].z = pack_half2(p[4], p[5]);
@@ -175,10 +247,12 @@ struct TileKernel {
         }
     }
 
-    // Page ids of the tile at k0 (lane k < NPG: page k of the tile), clamped
-    // to the range's last page.
-    static __device__ __forceinline__ int load_ids(const int32_t* bt, int k0, int t_end, int lane) {
-        return lane < NPG ? bt[min(k0 / BS + lane, (t_end - 1) / BS)] : 0;
+    // Page ids of the tile at k0 into a 256-byte LDS slot: lane k holds page
+    // k / BS + k of the tile, clamped to the range's last page (only lanes
+    // k < NPG are used).
+    static __device__ __forceinline__ void load_ids(const int32_t* bt, int k0, int t_end, int lane,
+                                                    int* slot) {
+        dma4(bt + min(k0 / BS + lane, (t_end - 1) / BS), lds_addr(slot));
     }
     // Out-of-pool ids read page 0 instead and flag the tile.
     static __device__ __forceinline__ int checked_ids(const DecodeArgs& a, int ids, int lane, bool& bad) {
@@ -187,10 +261,32 @@ struct TileKernel {
         return b ? 0 : ids;
     }
 
-    static __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+    // This wave's loads of a tile have landed once at most `n` of its later
+    // loads are outstanding (loads complete in issue order).
+    template <int N>
+    static __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+    // Workgroup barrier for the LDS pipeline.  __syncthreads() would also wait
+    // for every outstanding global load (its fence covers global memory),
+    // i.e. for the tiles still in flight; here only this wave's LDS reads are
+    // drained (the buffer loaded next is free once every wave is past), and
+    // the memory clobber keeps the compiler from moving LDS accesses across.
+    static __device__ __forceinline__ void lds_barrier() {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    static __device__ __forceinline__ void wait_tile(int later_tiles) {
+        static_assert(NBUF == 4 && 2 * (ISSUE + 1) < 64, "vmcnt range");
+        // each later tile: its page-id load and its K/V loads
+        if (later_tiles >= 2)
+            wait_vm<2 * (ISSUE + 1)>();
+        else if (later_tiles == 1)
+            wait_vm<ISSUE + 1>();
+        else
+            wait_vm<0>();
+    }
 
     static __device__ void run(const VarlenArgs& va) {
-        __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+        __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF];
+        __shared__ int ring[NW][NBUF][64];   // per wave: page ids of tile u in slot u % NBUF
         const DecodeArgs& a = va.d;
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, c = lane >> 4;
         // Later tiles see more keys: they start first.
@@ -242,7 +338,11 @@ struct TileKernel {
         }
 
         const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-        int ids_next = load_ids(bt, t_begin, t_end, lane);
+        // Page ids of tiles 0 .. NBUF - 2; later ones are loaded NBUF - 1
+        // tiles ahead of their K/V, ahead of the loads of the tile that frees
+        // their slot, so they have landed whenever that tile has.
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u) load_ids(bt, t_begin + u * KT, t_end, lane, ring[wave][u]);
         uint4 qb[CB][NKC];
         int e_lim[CB];
 #pragma unroll
@@ -268,32 +368,46 @@ struct TileKernel {
         for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
             for (int t = 0; t < NACC; ++t) st[cb].acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-            st[cb].m = -INFINITY;
+            st[cb].m = st[cb].r = -INFINITY;
             st[cb].l = 0.f;
         }
         const int nt = (t_end - t_begin + KT - 1) / KT;
-        bool bad = false, tbad_cur = false;
-        {
-            const int ids = checked_ids(a, ids_next, lane, tbad_cur);
-            issue_tile(a, lds, ids, min(KT, t_end - t_begin) - 1, g, wave, i, c);
-            if (nt > 1) ids_next = load_ids(bt, t_begin + KT, t_end, lane);
-        }
+        // Tile u goes to buffer u % NBUF; bit u % NBUF of tbad flags a page id
+        // of tile u that was outside the pool.
+        bool bad = false;
+        unsigned tbad = 0;
+        // Every issue makes ISSUE + 1 loads (the page-id load is clamped past
+        // the range), which wait_tile counts on.
+        auto issue = [&](int u) {
+            bool b = false;
+            const int ids = checked_ids(a, ring[wave][u % NBUF][lane], lane, b);
+            const int k0 = t_begin + u * KT;
+            load_ids(bt, k0 + (NBUF - 1) * KT, t_end, lane, ring[wave][(u + NBUF - 1) % NBUF]);
+            issue_tile(a, lds + (u % NBUF) * BUF, ids, min(KT, t_end - k0) - 1, g, wave, i, c);
+            tbad = b ? (tbad | (1u << (u % NBUF))) : (tbad & ~(1u << (u % NBUF)));
+        };
+        wait_vm<0>();
+        // Mark the query registers as used here, so the compiler's own wait
+        // for their loads falls before the loop rather than inside it.
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int kk = 0; kk < NKC; ++kk)
+                asm volatile("" ::"v"(qb[cb][kk].x), "v"(qb[cb][kk].y), "v"(qb[cb][kk].z), "v"(qb[cb][kk].w));
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u)
+            if (u < nt) issue(u);
         for (int t = 0; t < nt; ++t) {
             const int k0 = t_begin + t * KT;
-            // This wave's loads of tile t (and the next ids) have landed; the
-            // barrier makes every wave's visible and closes the reads of the
-            // buffer that is loaded next.
-            wait_loads();
-            __syncthreads();
-            bool tbad_next = false;
-            if (t + 1 < nt) {
-                const int ids = checked_ids(a, ids_next, lane, tbad_next);
-                issue_tile(a, lds + ((t + 1) & 1) * BUF, ids, min(KT, t_end - k0 - KT) - 1, g, wave, i, c);
-                if (t + 2 < nt) ids_next = load_ids(bt, k0 + 2 * KT, t_end, lane);
-            }
+            // This wave's loads of tile t have landed; the barrier makes every
+            // wave's visible and closes the reads of tile t - 1, whose buffer
+            // is loaded next.
+            wait_tile(min(nt - 1 - t, NBUF - 2));
+            lds_barrier();
+            if (t + NBUF - 1 < nt) issue(t + NBUF - 1);
             if (k0 < w_max) {
-                bad = bad || tbad_cur;
-                const char* lb = lds + (t & 1) * BUF;
+                bad = bad || ((tbad >> (t % NBUF)) & 1u);
+                const char* lb = lds + (t % NBUF) * BUF;
                 if (k0 + KT <= w_min) {
                     const int rem[CB] = {KT, KT};
                     compute<false>(a, st, lb, qb, rem, lane, c);
@@ -302,13 +416,14 @@ struct TileKernel {
                     compute<true>(a, st, lb, qb, rem, lane, c);
                 }
             }
-            tbad_cur = tbad_next;
         }
 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             float lsum = st[cb].l + __shfl_xor(st[cb].l, 16);
             lsum += __shfl_xor(lsum, 32);
+            // the partial's exp-sum is taken against the max itself
+            const float lmax = st[cb].r == -INFINITY ? lsum : lsum * exp2_fast(st[cb].r - st[cb].m);
             if (!valid[cb]) continue;
             if (P == 0 && lim[cb] <= 0) {   // a query that sees no key: zeros
                 float* o = a.out + row[cb] * D;
@@ -325,7 +440,7 @@ struct TileKernel {
                 dst = a.tmp_out + pr * D;
                 if (c == 0) {
                     a.max_logits[pr] = st[cb].m;
-                    a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                    a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lmax;
                 }
             }
             const float inv = 1.f / lsum;
