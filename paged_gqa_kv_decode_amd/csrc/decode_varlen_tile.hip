@@ -13,21 +13,23 @@
 //
 //  * Loads: the tile's K and V go straight from the paged cache into LDS
 //    (global_load_lds_dwordx4: lane l's 16 bytes land at slot base + 16 l),
-//    four buffers, tiles t + 1 .. t + 3 in flight while tile t is computed.  A slot
-//    is one matrix-core operand register of the whole wave, so every LDS read
-//    is one conflict-free ds_read_b128 of 1 KiB.  K slot (kb, kk): lane
-//    (i, c) holds K[16 kb + i][32 kk + 8 c, +8); V slot (dh, j): lane (i, c)
-//    holds V[tok(j, c)][128 dh + 8 i, +8) with tok = 4c + j (j < 4) or
-//    16 + 4c + j - 4, the 32-key PV operand order of the decode.
+//    four buffers, tiles t + 1 .. t + 3 in flight while tile t is computed.
+//    K: a slot is one matrix-core operand register of the whole wave, so
+//    every K read is one conflict-free ds_read_b128 of 1 KiB; K slot
+//    (kb, kk): lane (i, c) holds K[16 kb + i][32 kk + 8 c, +8).  V: rows in
+//    order, 16-byte chunks permuted per row against bank conflicts, read with
+//    the transposing ds_read_b64_tr_b16, which hands each lane four keys of
+//    one dim, so V^T needs no register shuffles.
 //  * Per wave and tile: S^T = K Q^T for two 16-column blocks (16x16x32
 //    products, Q^T held in registers), log2 online softmax per column with
 //    the causal limit applied by select on the diagonal tiles only, then
-//    O^T += V^T P^T (16x16x32, V transposed in registers by v_perm).  The
-//    softmax's exponent reference trails the running max by up to 2^8, so
-//    the accumulators are rescaled only on the rare tiles that move it.
+//    O^T += V^T P^T (16x16x32).  The softmax's exponent reference trails the
+//    running max by up to 2^8, so the accumulators are rescaled only on the
+//    rare tiles that move it.
 //  * Waves whose columns see none of a tile's keys skip its arithmetic but
 //    still take part in its loads and barriers.
-//  * Page ids of a tile are loaded two tiles ahead of its K/V loads.
+//  * Page ids of a tile go into a per-wave LDS ring three tiles ahead of its
+//    K/V loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,14 +50,19 @@ struct TileKernel {
     static constexpr int KT = 32;                // keys per tile
     static constexpr int NKC = D / 32;           // QK k-chunks of 32 dims
     static constexpr int NDH = D / 128;          // 128-dim halves of a V row
-    static constexpr int NACC = NDH * 8;         // PV output tiles per column block
+    static constexpr int NACC = D / 16;          // PV output tiles per column block (dims 16 m + 4 c + rr)
     static constexpr int KSLOTS = 2 * NKC;       // [key block][dim chunk]
-    static constexpr int SLOTS = KSLOTS + 8 * NDH;
+    static constexpr int VSLOTS = 8 * NDH;       // V: 32 rows of 2D bytes
+    static constexpr int SLOTS = KSLOTS + VSLOTS;
+    static constexpr int RB = 2 * D;             // bytes of a V row
+    static constexpr int RPI = 1024 / RB;        // V rows per slot
+    static constexpr int CPR = RB / 16;          // 16-byte chunks of a V row
     static constexpr int BUF = SLOTS * 1024;     // bytes of one tile in LDS
     static constexpr int NPG = KT / BS;          // pages per tile
     static constexpr int NBUF = 4;               // tiles in LDS: 3 in flight while 1 is computed
     static constexpr int ISSUE = SLOTS / NW;     // loads into LDS per wave and tile
-    static_assert(KSLOTS % NW == 0 && (8 * NDH) % NW == 0, "slots split evenly over the waves");
+    static_assert(KSLOTS % NW == 0 && VSLOTS % NW == 0, "slots split evenly over the waves");
+    static_assert(RPI <= BS, "the rows of a V slot sit in one page");
     static_assert(BS <= KT && KT % BS == 0, "a tile covers whole pages");
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -99,8 +106,6 @@ struct TileKernel {
         return (uint32_t)(uintptr_t)(lds_ptr_t)p;
     }
 
-    static __device__ __forceinline__ int tok_of(int j, int c) { return j < 4 ? 4 * c + j : 12 + 4 * c + j; }
-
     // Page id of key offset x of the tile (lane k of `ids` holds page k);
     // readlane keeps the ids in scalar registers rather than in an array.
     static __device__ __forceinline__ int page_of(int x, int ids) {
@@ -116,13 +121,24 @@ struct TileKernel {
     static __device__ __forceinline__ void issue_tile(const DecodeArgs& a, char* lbuf, int ids, int last,
                                                       int g, int wave, int i, int c) {
         const uint32_t lb = lds_addr(lbuf);
+        const int lane = 16 * c + i;
         const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;
         const int64_t head_off = (int64_t)g * BS * D;
-        if constexpr (BS >= 16) {
-            if (last == KT - 1) {
-                // A whole tile with pages of >= 16 tokens: each slot's 16 keys
-                // sit in one page, so the page base is wave-uniform (scalar
-                // registers) and each lane adds a fixed in-page offset.
+        if (last == KT - 1) {
+            // A whole tile: each V slot's rows, and with pages of >= 16
+            // tokens each K slot's 16 keys, sit in one page, so the page base
+            // is wave-uniform (scalar registers) and each lane adds a fixed
+            // in-page offset.
+#pragma unroll
+            for (int u = 0; u < VSLOTS / NW; ++u) {
+                const int v = wave + NW * u;
+                const int t = v * RPI + lane / CPR;
+                const int page = __builtin_amdgcn_readlane(ids, (v * RPI) / BS);
+                const uint16_t* pb = a.v + (int64_t)page * page_stride + head_off;
+                const int off = (t % BS) * D + 8 * vchunk(t, lane % CPR);
+                dma16_s(pb, 2u * (uint32_t)off, lb + (KSLOTS + v) * 1024);
+            }
+            if constexpr (BS >= 16) {
 #pragma unroll
                 for (int u = 0; u < KSLOTS / NW; ++u) {
                     const int s = wave + NW * u;
@@ -132,16 +148,17 @@ struct TileKernel {
                     const int off = ((16 * kb + i) % BS) * D + 32 * kk + 8 * c;
                     dma16_s(pb, 2u * (uint32_t)off, lb + s * 1024);
                 }
-#pragma unroll
-                for (int u = 0; u < 8 * NDH / NW; ++u) {
-                    const int s = wave + NW * u;
-                    const int dh = s / 8, j = s % 8;
-                    const int page = __builtin_amdgcn_readlane(ids, j < 4 ? 0 : 16 / BS);
-                    const uint16_t* pb = a.v + (int64_t)page * page_stride + head_off;
-                    const int off = (tok_of(j, c) % BS) * D + 128 * dh + 8 * i;
-                    dma16_s(pb, 2u * (uint32_t)off, lb + (KSLOTS + s) * 1024);
-                }
                 return;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < VSLOTS / NW; ++u) {
+                const int v = wave + NW * u;
+                const int t = v * RPI + lane / CPR;
+                const int x = min(t, last);
+                const uint16_t* p = a.v + (int64_t)page_of(x, ids) * page_stride + head_off +
+                                    (int64_t)(x % BS) * D + 8 * vchunk(t, lane % CPR);
+                dma16(p, lb + (KSLOTS + v) * 1024);
             }
         }
 #pragma unroll
@@ -153,15 +170,24 @@ struct TileKernel {
                                 (int64_t)(x % BS) * D + 32 * kk + 8 * c;
             dma16(p, lb + s * 1024);
         }
-#pragma unroll
-        for (int u = 0; u < 8 * NDH / NW; ++u) {
-            const int s = wave + NW * u;
-            const int dh = s / 8, j = s % 8;
-            const int x = min(tok_of(j, c), last);
-            const uint16_t* p = a.v + (int64_t)page_of(x, ids) * page_stride + head_off +
-                                (int64_t)(x % BS) * D + 128 * dh + 8 * i;
-            dma16(p, lb + (KSLOTS + s) * 1024);
-        }
+    }
+
+    // V row t of a tile sits in LDS at t * RB with its 16-byte chunks
+    // permuted (chunk ch at position ch ^ 2 (t & 3)), so that the four rows
+    // one transposing read touches fall in different banks.
+    static __device__ __forceinline__ int vchunk(int t, int pos) { return pos ^ ((t & 3) << 1); }
+
+    // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+    // lanes, lane i receives, for e = 0..3, 16-bit element i % 4 of the 8
+    // bytes addressed by lane 4 e + i / 4 of the group.  When lane 4 e + r of
+    // group c addresses V[row0 + e][16 m + 4 r ...], lane (i, c) receives
+    // V[row0 + e][16 m + i] for e = 0..3: four keys of one dim, a quarter of
+    // the PV product's V^T operand.
+    static __device__ __forceinline__ uint2 read_vt(const char* p) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+        const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)p);
+        return __builtin_bit_cast(uint2, r);
     }
 
     static __device__ __forceinline__ uint4 lds16(const char* lb, int slot, int lane) {
@@ -173,7 +199,7 @@ struct TileKernel {
     template <bool MASK>
     static __device__ __forceinline__ void compute(const DecodeArgs& a, Col (&st)[CB], const char* lb,
                                                    const uint4 (&qb)[CB][NKC], const int (&rem)[CB],
-                                                   int lane, int c) {
+                                                   const int (&voff)[4], int lane, int c) {
         floatx4 sc[CB][2];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -228,22 +254,16 @@ struct TileKernel {
             pb[cb].z = pack_half2(p[4], p[5]);
             pb[cb].w = pack_half2(p[6], p[7]);
         }
+        // O^T += V^T P^T, 16 dims at a time: k-slots of lane group c are keys
+        // 4c + e, then 16 + 4c + e (the order of the weights in pb).
+        const char* vb = lb + KSLOTS * 1024;
 #pragma unroll
-        for (int dh = 0; dh < NDH; ++dh) {
-            uint4 vr[8];
+        for (int m = 0; m < NACC; ++m) {
+            const char* p = vb + voff[m & 3] + 128 * (m >> 2);
+            const uint2 lo = read_vt(p), hi = read_vt(p + 16 * RB);
+            const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) vr[j] = lds16(lb, KSLOTS + 8 * dh + j, lane);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                st[cb].acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr), pb[cb], st[cb].acc[dh * 8 + 0]);
-                st[cb].acc[dh * 8 + 1] = mfma32(vt_operand<1>(vr), pb[cb], st[cb].acc[dh * 8 + 1]);
-                st[cb].acc[dh * 8 + 2] = mfma32(vt_operand<2>(vr), pb[cb], st[cb].acc[dh * 8 + 2]);
-                st[cb].acc[dh * 8 + 3] = mfma32(vt_operand<3>(vr), pb[cb], st[cb].acc[dh * 8 + 3]);
-                st[cb].acc[dh * 8 + 4] = mfma32(vt_operand<4>(vr), pb[cb], st[cb].acc[dh * 8 + 4]);
-                st[cb].acc[dh * 8 + 5] = mfma32(vt_operand<5>(vr), pb[cb], st[cb].acc[dh * 8 + 5]);
-                st[cb].acc[dh * 8 + 6] = mfma32(vt_operand<6>(vr), pb[cb], st[cb].acc[dh * 8 + 6]);
-                st[cb].acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr), pb[cb], st[cb].acc[dh * 8 + 7]);
-            }
+            for (int cb = 0; cb < CB; ++cb) st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
         }
     }
 
@@ -371,6 +391,15 @@ struct TileKernel {
             st[cb].m = st[cb].r = -INFINITY;
             st[cb].l = 0.f;
         }
+        // Transposing-read addresses of dims 16 m .. 16 m + 15 (m % 4 = mm;
+        // + 128 (m / 4) bytes), keys 4c + e: lane 4e + r of group c points at
+        // V[4c + e][16 m + 4 r], its chunk permuted as stored.
+        int voff[4];
+        {
+            const int e = (lane & 15) >> 2, r = lane & 3;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) voff[mm] = (4 * c + e) * RB + 32 * (mm ^ e) + 8 * r;
+        }
         const int nt = (t_end - t_begin + KT - 1) / KT;
         // Tile u goes to buffer u % NBUF; bit u % NBUF of tbad flags a page id
         // of tile u that was outside the pool.
@@ -410,10 +439,10 @@ struct TileKernel {
                 const char* lb = lds + (t % NBUF) * BUF;
                 if (k0 + KT <= w_min) {
                     const int rem[CB] = {KT, KT};
-                    compute<false>(a, st, lb, qb, rem, lane, c);
+                    compute<false>(a, st, lb, qb, rem, voff, lane, c);
                 } else {
                     const int rem[CB] = {e_lim[0] - k0, e_lim[1] - k0};
-                    compute<true>(a, st, lb, qb, rem, lane, c);
+                    compute<true>(a, st, lb, qb, rem, voff, lane, c);
                 }
             }
         }
@@ -445,16 +474,12 @@ struct TileKernel {
             }
             const float inv = 1.f / lsum;
 #pragma unroll
-            for (int dh = 0; dh < NDH; ++dh)
+            for (int m = 0; m < NACC; ++m) {
+                float v[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    float v[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = out_bad ? __builtin_nanf("") : st[cb].acc[dh * 8 + e][rr] * inv;
-                    float4* o = reinterpret_cast<float4*>(dst + 128 * dh + 8 * (4 * c + rr));
-                    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-                    o[1] = make_float4(v[4], v[5], v[6], v[7]);
-                }
+                for (int rr = 0; rr < 4; ++rr) v[rr] = out_bad ? __builtin_nanf("") : st[cb].acc[m][rr] * inv;
+                *reinterpret_cast<float4*>(dst + 16 * m + 4 * c) = make_float4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
 };
