@@ -353,7 +353,7 @@ def main():
                     help="-1 planner, 0 unsplit, 256/512 forced (default: the workload's own)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "dot", "mfma", "mfma1", "mfma2", "mfma4", "mfma4p2"])
     ap.add_argument("--varlen-kernel", default="auto", choices=["auto", "columns", "tiles"],
-                    help="multi-token workloads: kernel (auto: tiles from 64 query tokens)")
+                    help="multi-token workloads: kernel (auto: tiles from 4 query tokens)")
     ap.add_argument("--order", default="auto", choices=["auto", "grid", "longest"],
                     help="work order of the matrix-core decode (A/B switch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

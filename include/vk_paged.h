@@ -273,9 +273,10 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
  * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
  * call is unsplit when the tiles alone give one wave per wave slot
  * (w * n >= 8 * cu_count), otherwise split at 512 when
- * n * floor(L / 512) summed per sequence >= 33 * cu_count, else 256.
+ * n * floor(L / 512) summed per sequence >= 33 * cu_count, else 256; when
+ * that split's scratch would exceed the cap, 512, and failing that unsplit.
  * NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
- * against the cap.  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
+ * against the cap (an explicit partition request over it is an error).  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
  * q_len outside [0, seq_len]; VK_ERR_BAD_DIM if a q_len exceeds 65535.
  */
 vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_host,
@@ -384,13 +385,16 @@ int32_t vk_select_work_order(int32_t order);
  * vk_select_varlen_kernel — A/B switch for this thread's later
  * vk_plan_varlen and vk_paged_gqa_varlen calls: VK_KERNEL_AUTO (tiles when
  * the longest query run of the batch is at least VK_VARLEN_TILE_MIN_Q
- * tokens, else columns), VK_KERNEL_VARLEN_COLUMNS or VK_KERNEL_VARLEN_TILES.
+ * tokens, else columns: measured on MI355X, the tiles win from 4 query
+ * tokens on for every admitted grouped geometry, the columns below, and
+ * one token is the decode's own step), VK_KERNEL_VARLEN_COLUMNS or
+ * VK_KERNEL_VARLEN_TILES.
  * Both kernels compute the same rows to the same tolerance; the planner's
  * split rule depends on the kernel, so plan and launch under the same
  * setting.  Returns the previous setting, or -1 for an unknown value
  * (setting kept).
  */
-#define VK_VARLEN_TILE_MIN_Q 64
+#define VK_VARLEN_TILE_MIN_Q 4
 int32_t vk_select_varlen_kernel(int32_t kernel);
 
 /* Human-readable name of a status code (static storage). */

@@ -421,14 +421,21 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     p.budget = (int64_t)VK_DEFAULT_BUDGET_PER_CU * cu_count;
     p.kernel = kernel;
     int32_t P = partition_request;
+    const auto scratch_at = [&](int32_t Pc) -> uint64_t {
+        return (uint64_t)total_q * (uint64_t)num_q_heads * (uint64_t)((max_len + Pc - 1) / Pc) *
+               (uint64_t)(head_dim + 2) * 4u;
+    };
     if (P == -1) {
         // Unsplit when the (tile, KV head) workgroups fill the wave slots
         // once (8 per CU); otherwise the decode's rule over (tile, full
-        // partition) units.
+        // partition) units.  Many query rows can make the partials outgrow
+        // the cap: then 512, and failing that unsplit (which needs none).
         if ((int64_t)waves_per_tile * num_kv_heads * tiles >= 8 * (int64_t)cu_count)
             P = 0;
         else
             P = ((int64_t)num_kv_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
+        if (P == VK_PARTITION_SMALL && scratch_at(P) > cap) P = VK_PARTITION_LARGE;
+        if (P == VK_PARTITION_LARGE && scratch_at(P) > cap) P = 0;
     }
     p.partition_size = P;
     if (P == 0) {
@@ -437,8 +444,7 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     } else {
         p.max_num_partitions = (int32_t)((max_len + P - 1) / P);
         p.work_full_parts = (int64_t)num_kv_heads * (P == VK_PARTITION_LARGE ? full512 : full256);
-        p.scratch_bytes = (uint64_t)total_q * (uint64_t)num_q_heads *
-                          (uint64_t)p.max_num_partitions * (uint64_t)(head_dim + 2) * 4u;
+        p.scratch_bytes = scratch_at(P);
         if (p.scratch_bytes > cap) return VK_ERR_SCRATCH_CAP;
     }
     *plan_out = p;

@@ -176,13 +176,20 @@ def test_planner_device_query_without_gpu_is_hip_error():
 # ----------------------------------------------------------------------------
 # vk_plan_varlen: hand-computed decisions (host only; cu_count given).
 # ----------------------------------------------------------------------------
+@pytest.fixture
+def columns():
+    prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
+    yield
+    vb.select_varlen_kernel(prev)
+
+
 def _pv(lens, qlens, geom, bs=16, P=-1, cu=256, cap=0, mb=None):
     Hq, Hkv, D = geom
     mb = mb or max(-(-L // bs) for L in lens)
     return vb.plan_varlen(lens, qlens, Hq, Hkv, D, bs, mb, P, cu, cap)
 
 
-def test_plan_varlen_split_small_work():
+def test_plan_varlen_split_small_work(columns):
     # G = 4: 4 query tokens per tile; tiles 1 + 1, units 8 * 2 = 16 < 8 * 4.
     # Full-512 work 8 * (1 + 1) = 16 < 33 * 4 -> 256; NP = ceil(1000 / 256) = 4.
     p = _pv([1000, 600], [4, 1], (32, 8, 128), cu=4)
@@ -191,14 +198,14 @@ def test_plan_varlen_split_small_work():
     assert p.budget == 33 * 4
 
 
-def test_plan_varlen_unsplit_when_tiles_fill_the_slots():
+def test_plan_varlen_unsplit_when_tiles_fill_the_slots(columns):
     # G = 8: 2 tokens per tile; tiles 4 + 4 + 2 = 10, units 2 * 10 = 20 >= 8 * 1.
     p = _pv([100, 100, 100], [8, 8, 4], (16, 2, 128), cu=1)
     assert (p.partition_size, p.max_num_partitions, p.scratch_bytes) == (0, 1, 0)
     assert p.work_full_parts == 20
 
 
-def test_plan_varlen_large_partition_at_the_budget():
+def test_plan_varlen_large_partition_at_the_budget(columns):
     # G = 8, tiles 1 + 1 -> units 4 < 8.  Full-512 units: 2 * (16 + 8) = 48 >= 33.
     p = _pv([8192, 4096], [2, 2], (16, 2, 256), bs=32, cu=1)
     assert (p.partition_size, p.max_num_partitions) == (512, 16)
@@ -226,9 +233,10 @@ def test_plan_varlen_scratch_cap():
 
 
 def test_plan_varlen_kernel_choice():
-    # The longest query run decides: >= 64 tokens -> LDS tiles, else columns.
-    assert _pv([2000, 1500], [63, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
-    assert _pv([2000, 1500], [64, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
+    # The longest query run decides: >= 4 tokens -> LDS tiles, else columns.
+    assert vb.VARLEN_TILE_MIN_Q == 4
+    assert _pv([2000, 1500], [3, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
+    assert _pv([2000, 1500], [4, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
     prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
     try:
         assert _pv([2000, 1500], [100, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
@@ -258,3 +266,19 @@ def test_plan_varlen_tiles_split_rule():
     # workgroups, 3136 waves >= 8 * 256: the chunked-prefill shape runs unsplit.
     p = _pv([3000, 5000, 8000, 2048], [1024] * 4, (24, 4, 256), bs=32, cu=256)
     assert (p.kernel, p.partition_size, p.work_full_parts) == (vb.KERNEL_VARLEN_TILES, 0, 784)
+
+
+def test_plan_varlen_auto_falls_back_under_the_scratch_cap():
+    # 32 sequences x 32 query tokens of (32, 8, 128) on 16k contexts: one tile
+    # per sequence, 4 * 8 * 32 = 1024 waves < 8 * 256 -> split; at 256 the
+    # partials need 1024 * 32 * 64 * 130 * 4 = 1.09 GB > 512 MiB, at 512
+    # 545 MB > 512 MiB -> unsplit.  An explicit 256 is refused.
+    lens, ql = [16384] * 32, [32] * 32
+    p = _pv(lens, ql, (32, 8, 128), cu=256)
+    assert (p.kernel, p.partition_size, p.scratch_bytes) == (vb.KERNEL_VARLEN_TILES, 0, 0)
+    with pytest.raises(vb.VkError) as e:
+        _pv(lens, ql, (32, 8, 128), P=256, cu=256)
+    assert e.value.name == "SCRATCH_CAP"
+    # with a larger cap the rule's own choice stands
+    p = _pv(lens, ql, (32, 8, 128), cu=256, cap=2 << 30)
+    assert p.partition_size in (256, 512)

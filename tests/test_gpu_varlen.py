@@ -17,6 +17,15 @@ from paged_gqa_kv_decode_amd.workloads import make_varlen, make_varlen_custom
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def column_kernel():
+    """These tests cover the column kernel (auto would pick the LDS-tiled one
+    from 4 query tokens on; that kernel has its own tests)."""
+    prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
+    yield
+    vb.select_varlen_kernel(prev)
+
+
 def _dev(wl):
     import torch
     return (torch.from_numpy(wl.q).cuda(), torch.from_numpy(wl.k_cache).cuda(),

@@ -39,6 +39,18 @@ def test_prefill_workload_picks_tiles_and_matches(orc):
     assert_parity(gpu[rows], ref, f"prefill4_chunk1k tiles ({len(rows)} rows)")
 
 
+@pytest.mark.parametrize("P", [-1, 0, 512])
+def test_verify_workload_picks_tiles_and_matches(orc, P):
+    """Speculative-decode verification (4 query tokens): auto picks the tiled
+    kernel; the whole batch against the oracle."""
+    wl = make_varlen("verify32_q4")
+    ref = oracle_varlen(orc, wl)
+    gpu, plan, _ = run_varlen(wl, P)
+    assert plan.kernel == vb.KERNEL_VARLEN_TILES
+    say(f"[tiles] verify32_q4 P={plan.partition_size}")
+    assert_parity(gpu, ref, f"verify32_q4 tiles P={plan.partition_size}")
+
+
 GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256), (16, 16, 128), (8, 8, 256),
          (16, 1, 128), (16, 1, 256)]
 CASES = [(g, bs) for g in GEOMS for bs in (8, 16, 32)]
