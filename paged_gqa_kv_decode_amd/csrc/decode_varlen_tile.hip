@@ -36,15 +36,27 @@
 #include "mfma_ops.h"
 #include "vk_kernels.h"
 
+#ifndef VK_TILE_D256_ONE_BLOCK
+#define VK_TILE_D256_ONE_BLOCK 1   // D = 256: eight waves of one column block
+#endif
+
 namespace vk {
 namespace {
 
 using namespace mfma;
 
+// 16-column blocks per wave and waves per workgroup (128 columns in all):
+// at D = 128 four waves of two blocks (two workgroups per CU, two waves per
+// SIMD); at D = 256 eight waves of one block, so that a wave fits in 256
+// registers and two share each SIMD (with two blocks a wave needs ~300 and
+// runs alone).
+constexpr int tile_blocks(int D) { return (D == 256 && VK_TILE_D256_ONE_BLOCK) ? 1 : 2; }
+constexpr int tile_waves(int D) { return 8 / tile_blocks(D); }
+
 template <int D, int G, int BS>
 struct TileKernel {
-    static constexpr int NW = 4;                 // waves per workgroup
-    static constexpr int CB = 2;                 // 16-column blocks per wave
+    static constexpr int CB = tile_blocks(D);    // 16-column blocks per wave
+    static constexpr int NW = tile_waves(D);     // waves per workgroup
     static constexpr int BQ = NW * CB * 16 / G;  // query tokens per workgroup
     static constexpr int NCOL = BQ * G;          // columns in use
     static constexpr int KT = 32;                // keys per tile
@@ -332,7 +344,7 @@ struct TileKernel {
         int64_t row[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const int cw = 32 * wave + 16 * cb + i;
+            const int cw = 16 * CB * wave + 16 * cb + i;
             const int jt = tile * BQ + cw / G;
             valid[cb] = cw < NCOL && jt < qlen;
             lim[cb] = valid[cb] ? L - qlen + jt + 1 : 0;
@@ -375,8 +387,12 @@ struct TileKernel {
         }
         // The wave's key span: tiles past its largest limit are skipped, tiles
         // below its smallest need no mask.
-        int w_max = max(valid[0] ? e_lim[0] : t_begin, valid[1] ? e_lim[1] : t_begin);
-        int w_min = min(e_lim[0], e_lim[1]);
+        int w_max = t_begin, w_min = t_end;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (valid[cb]) w_max = max(w_max, e_lim[cb]);
+            w_min = min(w_min, e_lim[cb]);
+        }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             w_max = max(w_max, __shfl_xor(w_max, off));
@@ -438,10 +454,14 @@ struct TileKernel {
                 bad = bad || ((tbad >> (t % NBUF)) & 1u);
                 const char* lb = lds + (t % NBUF) * BUF;
                 if (k0 + KT <= w_min) {
-                    const int rem[CB] = {KT, KT};
+                    int rem[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) rem[cb] = KT;
                     compute<false>(a, st, lb, qb, rem, voff, lane, c);
                 } else {
-                    const int rem[CB] = {e_lim[0] - k0, e_lim[1] - k0};
+                    int rem[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) rem[cb] = e_lim[cb] - k0;
                     compute<true>(a, st, lb, qb, rem, voff, lane, c);
                 }
             }
@@ -485,7 +505,8 @@ struct TileKernel {
 };
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(64 * tile_waves(D))
+__attribute__((amdgpu_waves_per_eu(tile_blocks(D) == 2 && D == 256 ? 1 : 2)))
 void varlen_tile_kernel(VarlenArgs a) {
     TileKernel<D, G, BS>::run(a);
 }
@@ -494,9 +515,9 @@ template <int D, int G>
 hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
     *ok = true;
     switch (bs) {
-        case 8: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 8>), grid, dim3(256), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 16>), grid, dim3(256), 0, st, a); break;
-        case 32: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 32>), grid, dim3(256), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 8>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
+        case 16: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 16>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
+        case 32: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 32>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
         default: *ok = false; return hipSuccess;
     }
     return hipGetLastError();
@@ -505,6 +526,7 @@ hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, boo
 }  // namespace
 
 int varlen_tile_tokens(int group) { return group > 0 && group <= 16 ? 128 / group : 0; }
+int varlen_tile_threads(int head_dim) { return 64 * tile_waves(head_dim); }
 
 hipError_t launch_varlen_tile(const VarlenArgs& a, int group, int head_dim, int block_size,
                               dim3 grid, hipStream_t stream, bool* geometry_ok) {

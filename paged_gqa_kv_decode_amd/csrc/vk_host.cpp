@@ -392,7 +392,7 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     const int group = num_q_heads / num_kv_heads;
     const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
     const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
-    const int waves_per_tile = tiled ? 4 : 1;
+    const int waves_per_tile = tiled ? vk::varlen_tile_threads(head_dim) / 64 : 1;
     int64_t max_len = 0, total_q = 0, tiles = 0, full512 = 0, full256 = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int64_t L = seq_lens_host[s], ql = q_lens_host[s];
@@ -529,7 +529,7 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
     p.grid[0] = (int32_t)grid.x;
     p.grid[1] = (int32_t)grid.y;
     p.grid[2] = (int32_t)grid.z;
-    p.block = tiled ? 256 : 64;
+    p.block = tiled ? vk::varlen_tile_threads(head_dim) : 64;
     p.work_order = VK_ORDER_GRID;
     t_last_plan = p;
     return VK_OK;

@@ -95,6 +95,7 @@ int varlen_tokens_per_tile(int group);
 hipError_t launch_varlen_tile(const VarlenArgs& a, int group, int head_dim, int block_size,
                               dim3 grid, hipStream_t stream, bool* geometry_ok);
 int varlen_tile_tokens(int group);
+int varlen_tile_threads(int head_dim);
 hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,
                          bool* geometry_ok);
