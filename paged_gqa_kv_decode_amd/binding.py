@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m paged_gqa_kv_decode_amd.build` (no CPU fallback exists)")
+    # PyTorch ships its own HIP runtime.  Loading it first lets this library
+    # bind to that same runtime (one per process); loaded the other way round
+    # the process holds two, and this library's HIP calls found no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
     L.vk_plan_partitions.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, u64,
