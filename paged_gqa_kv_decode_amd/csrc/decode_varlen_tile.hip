@@ -185,9 +185,9 @@ struct TileKernel {
     }
 
     // V row t of a tile sits in LDS at t * RB with its 16-byte chunks
-    // permuted (chunk ch at position ch ^ 2 (t & 3)), so that the four rows
-    // one transposing read touches fall in different banks.
-    static __device__ __forceinline__ int vchunk(int t, int pos) { return pos ^ ((t & 3) << 1); }
+    // permuted (chunk ch at position ch ^ 2 (t & 7)), so that the eight rows
+    // that 32 lanes of one transposing read touch fall in different banks.
+    static __device__ __forceinline__ int vchunk(int t, int pos) { return pos ^ ((t & 7) << 1); }
 
     // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
     // lanes, lane i receives, for e = 0..3, 16-bit element i % 4 of the 8
@@ -211,7 +211,7 @@ struct TileKernel {
     template <bool MASK>
     static __device__ __forceinline__ void compute(const DecodeArgs& a, Col (&st)[CB], const char* lb,
                                                    const uint4 (&qb)[CB][NKC], const int (&rem)[CB],
-                                                   const int (&voff)[4], int lane, int c) {
+                                                   const int (&voff)[8], int lane, int c) {
         floatx4 sc[CB][2];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -271,7 +271,7 @@ struct TileKernel {
         const char* vb = lb + KSLOTS * 1024;
 #pragma unroll
         for (int m = 0; m < NACC; ++m) {
-            const char* p = vb + voff[m & 3] + 128 * (m >> 2);
+            const char* p = vb + voff[m & 7] + 256 * (m >> 3);
             const uint2 lo = read_vt(p), hi = read_vt(p + 16 * RB);
             const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
@@ -407,14 +407,15 @@ struct TileKernel {
             st[cb].m = st[cb].r = -INFINITY;
             st[cb].l = 0.f;
         }
-        // Transposing-read addresses of dims 16 m .. 16 m + 15 (m % 4 = mm;
-        // + 128 (m / 4) bytes), keys 4c + e: lane 4e + r of group c points at
-        // V[4c + e][16 m + 4 r], its chunk permuted as stored.
-        int voff[4];
+        // Transposing-read addresses of dims 16 m .. 16 m + 15 (m % 8 = mm;
+        // + 256 (m / 8) bytes), keys 4c + e: lane 4e + r of group c points at
+        // V[4c + e][16 m + 4 r], its chunk permuted as stored (row t = 4c + e,
+        // also for the keys 16 + 4c + e, read 16 rows further).
+        int voff[8];
         {
-            const int e = (lane & 15) >> 2, r = lane & 3;
+            const int e = (lane & 15) >> 2, r = lane & 3, t = 4 * c + e;
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) voff[mm] = (4 * c + e) * RB + 32 * (mm ^ e) + 8 * r;
+            for (int mm = 0; mm < 8; ++mm) voff[mm] = t * RB + 32 * (mm ^ (t & 7)) + 8 * r;
         }
         const int nt = (t_end - t_begin + KT - 1) / KT;
         // Tile u goes to buffer u % NBUF; bit u % NBUF of tbad flags a page id
