@@ -163,6 +163,18 @@ def ceilings(wl, dev, P, reps=10):
             "flushed": "512 MiB read before each timed run"}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), or ""."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
     """Time the float64 oracle, as it stands, on a bounded sample of the
     workload: whole sequences, taken in order and cycling over the batch,
@@ -191,7 +203,7 @@ def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
                                     4 if wl.meta.get("dtype") == "f32" else 2)
         per_token = total / max(done_tokens, 1)
     return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s (KV-read)",
-            "cores": nthreads, "kind": "oracle",
+            "cores": nthreads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{runs} single-sequence oracle calls cycling over the {wl.num_seqs} "
                       f"sequences ({done_tokens} tokens, all {wl.num_q_heads} q heads), "
                       f"{total:.2f} s wall",
@@ -229,7 +241,7 @@ def cpu_baseline_varlen(wl, min_seconds: float, max_seconds: float, flops_unit: 
         per = total / work
     value = work / total / (1e12 if flops_unit else 1e9)
     return {"value": round(value, 6), "unit": "TFLOP/s" if flops_unit else "GB/s (KV-read)",
-            "cores": nthreads, "kind": "oracle",
+            "cores": nthreads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{runs} single-sequence oracle calls cycling over the {wl.num_seqs} "
                       f"sequences ({done} query rows, all {wl.num_q_heads} q heads), "
                       f"{total:.2f} s wall",
