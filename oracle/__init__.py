@@ -92,6 +92,9 @@ class Oracle:
         lib.oracle_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                             ctypes.c_longlong, ctypes.c_double, P, i32]
         lib.oracle_paged_varlen.restype = i32
+        lib.oracle_paged_varlen_dt.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                               ctypes.c_longlong, ctypes.c_double, i32, P, i32]
+        lib.oracle_paged_varlen_dt.restype = i32
         self.lib = lib
         self.path = path
 
@@ -128,10 +131,11 @@ class Oracle:
         return out
 
     def paged_varlen_arrays(self, q, k_cache, v_cache, block_tables, seq_lens, cu_q, scale,
-                            nthreads: int | None = None) -> np.ndarray:
+                            nthreads: int | None = None, dtype: str = "f16") -> np.ndarray:
         """Causal attention of packed query rows q [total_q, Hq, D] (sequence s
-        owns rows cu_q[s] .. cu_q[s+1]-1, the last qlen_s of its L_s tokens)."""
-        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens)
+        owns rows cu_q[s] .. cu_q[s+1]-1, the last qlen_s of its L_s tokens);
+        dtype of q, K, V as for paged_attention_arrays."""
+        q, k, v, bt, sl = self._args(q, k_cache, v_cache, block_tables, seq_lens, dtype)
         cu = _c(cu_q, np.int32)
         T, Hq, D = q.shape
         nb, Hkv, bs, D2 = k.shape
@@ -139,9 +143,10 @@ class Oracle:
         assert D2 == D and v.shape == k.shape and bt.shape[0] == S and cu.shape == (S + 1,)
         assert int(cu[0]) == 0 and int(cu[-1]) == T and np.all(np.diff(cu) >= 0)
         out = np.empty((T, Hq, D), dtype=np.float64)
-        st = self.lib.oracle_paged_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl),
-                                          _ptr(cu), S, Hq, Hkv, D, bs, bt.shape[1], nb,
-                                          float(scale), _ptr(out), nthreads or default_threads())
+        st = self.lib.oracle_paged_varlen_dt(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl),
+                                             _ptr(cu), S, Hq, Hkv, D, bs, bt.shape[1], nb,
+                                             float(scale), self.DTYPES[dtype][1], _ptr(out),
+                                             nthreads or default_threads())
         if st != 0:
             raise ValueError(f"oracle_paged_varlen failed: {st}")
         return out

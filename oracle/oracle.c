@@ -344,18 +344,29 @@ int oracle_partials(const uint16_t *q, const uint16_t *k_cache, const uint16_t *
  * rows cu_q[s] .. cu_q[s+1]-1 (packed [total_q][Hq][D] fp16) and its cache
  * holds L = seq_lens[s] tokens including them; row j attends causally (see
  * the header).  Same return codes as oracle_paged_attention. */
-int oracle_paged_varlen(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                        const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_q,
-                        int S, int Hq, int Hkv, int D, int bs, int max_blocks,
-                        long long num_blocks, double scale, double *out, int nthreads)
+int oracle_paged_varlen_dt(const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_q,
+                           int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                           long long num_blocks, double scale, int dtype, double *out, int nthreads)
 {
+    if (dtype < 0 || dtype > 2) return -4;
     job_t J;
     memset(&J, 0, sizeof(J));
+    J.dtype = dtype;
     J.q = q; J.k = k_cache; J.v = v_cache;
     J.block_tables = block_tables; J.seq_lens = seq_lens; J.cu_q = cu_q;
     J.S = S; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = bs; J.max_blocks = max_blocks;
     J.num_blocks = num_blocks; J.scale = scale; J.out = out;
     return run_jobs(&J, nthreads, varlen_worker);
+}
+
+int oracle_paged_varlen(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                        const int32_t *block_tables, const int32_t *seq_lens, const int32_t *cu_q,
+                        int S, int Hq, int Hkv, int D, int bs, int max_blocks,
+                        long long num_blocks, double scale, double *out, int nthreads)
+{
+    return oracle_paged_varlen_dt(q, k_cache, v_cache, block_tables, seq_lens, cu_q, S, Hq, Hkv, D,
+                                  bs, max_blocks, num_blocks, scale, 0, out, nthreads);
 }
 
 /* Merge per-partition triples of every (s, h) into out[S][Hq][D]. */

@@ -466,8 +466,38 @@ def pin_other_element_types(orc):
         _close(orc.merge(m, l, o, sl, 16), ref, 1e-12, f"split/merge {dtype}")
 
 
+def pin_varlen_bf16(orc):
+    """bf16 q/K/V through the causal multi-token path: the oracle against torch
+    float64 SDPA with a causal mask on the values torch itself decodes from
+    the bf16 bits."""
+    for i, (lens, qlens, Hq, Hkv, D, bs) in enumerate(VARLEN_CASES):
+        c = varlen_case(230 + i, lens, qlens, Hq, Hkv, D, bs)
+        rng = np.random.default_rng(240 + i)
+
+        def bf16(shape):
+            u = rng.standard_normal(shape, dtype=np.float32).view(np.uint32)
+            bits = (((u + (((u >> 16) & 1) + np.uint32(0x7FFF))) >> 16)).astype(np.uint16)
+            vals = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+            return bits, vals
+
+        qb, c["qv"] = bf16(c["qv"].shape)
+        kc = np.zeros(c["k_cache"].shape, dtype=np.uint16)
+        vc = np.zeros(c["v_cache"].shape, dtype=np.uint16)
+        for s, L in enumerate(lens):
+            kb_, c["dk"][s] = bf16((Hkv, L, D))
+            vb_, c["dv"][s] = bf16((Hkv, L, D))
+            for p in range(-(-L // bs)):
+                blk = c["block_tables"][s, p]
+                n = min(bs, L - p * bs)
+                kc[blk, :, :n, :] = kb_[:, p * bs:p * bs + n, :]
+                vc[blk, :, :n, :] = vb_[:, p * bs:p * bs + n, :]
+        got = orc.paged_varlen_arrays(qb, kc, vc, c["block_tables"], c["seq_lens"], c["cu"],
+                                      c["scale"], dtype="bf16")
+        _close(got, sdpa_varlen(c), 1e-12, f"varlen bf16 case {i}")
+
+
 ALL_PINS = [pin_half_decode, pin_sdpa, pin_closed_forms, pin_large_scores, pin_permutation,
             pin_split_merge, pin_partials_closed, pin_merge_closed, pin_shift_invariance,
             pin_gqa_to_mha, pin_onehot, pin_golden, pin_varlen_sdpa,
             pin_varlen_rows_are_truncated_decodes, pin_varlen_one_token_is_decode,
-            pin_bf16_decode, pin_other_element_types]
+            pin_bf16_decode, pin_other_element_types, pin_varlen_bf16]
