@@ -233,7 +233,8 @@ def cpu_baseline_varlen(wl, min_seconds: float, max_seconds: float, flops_unit: 
         oracle.paged_varlen_arrays(wl.q[cu[s]:cu[s + 1]], wl.k_cache, wl.v_cache,
                                    wl.block_tables[s:s + 1], wl.seq_lens[s:s + 1],
                                    np.array([0, ql[s]], dtype=np.int32), wl.scale,
-                                   nthreads=nthreads)
+                                   nthreads=nthreads,
+                                   dtype="bf16" if wl.q.dtype == np.uint16 else "f16")
         total += time.perf_counter() - t
         runs += 1
         done += int(ql[s])
@@ -257,9 +258,12 @@ def bench_varlen(args, wl, gen_s):
     from paged_gqa_kv_decode_amd.workloads import kv_read_bytes, varlen_pairs
     P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
     ql = wl.meta["q_lens"]
-    q = torch.from_numpy(wl.q).cuda()
-    k = torch.from_numpy(wl.k_cache).cuda()
-    v = torch.from_numpy(wl.v_cache).cuda()
+
+    def dev(x):       # bf16 workloads hold bit patterns as uint16
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+    q, k, v = dev(wl.q), dev(wl.k_cache), dev(wl.v_cache)
     bt = torch.from_numpy(wl.block_tables).cuda()
     sl = torch.from_numpy(wl.seq_lens).cuda()
     cu = torch.from_numpy(wl.meta["cu_q"]).cuda()
@@ -329,8 +333,8 @@ def bench_varlen(args, wl, gen_s):
                   ("causal attention TFLOP/s" if compute_bound else "KV-read HBM GB/s") + ")",
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic (seeded N(0, 1) fp16 K/V/q, shuffled pages)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+        "data": f"synthetic (seeded N(0, 1) {args.dtype} K/V/q, shuffled pages)",
         "config": {"workload": wl.name, "description": DESCRIPTIONS[wl.name],
                    "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
@@ -432,7 +436,9 @@ def main():
                                        f"({Hq_}q, {Hkv_}kv, {D_}), block {bs_}, {args.dtype}")
     elif args.workload in VARLEN:
         from paged_gqa_kv_decode_amd.workloads import make_varlen
-        wl = make_varlen(args.workload)
+        if args.dtype not in ("f16", "bf16"):
+            raise SystemExit("bench.py: multi-token workloads run in f16 or bf16")
+        wl = make_varlen(args.workload, dtype=args.dtype)
         return bench_varlen(args, wl, time.time() - t0)
     else:
         wl = make_workload(args.workload)

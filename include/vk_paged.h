@@ -323,6 +323,25 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
                               float* exp_sums, float* tmp_out, void* stream);
 
 /*
+ * vk_paged_gqa_varlen_dt — vk_paged_gqa_varlen with the element type of q,
+ * k_cache and v_cache given by dtype: VK_DTYPE_F16 or VK_DTYPE_BF16 (bf16 as
+ * in vk_paged_gqa_decode_dt: the same steps on the bf16 matrix instructions,
+ * each softmax weight taken through PV as a bf16 value plus its bf16
+ * residual).  Same layouts in elements, outputs and partials fp32.  Errors:
+ * those of vk_paged_gqa_varlen; VK_ERR_DTYPE for any other dtype (fp32
+ * q/K/V run only through the single-token decode).
+ */
+vk_status vk_paged_gqa_varlen_dt(int32_t dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, int32_t partition_size, int32_t max_num_partitions,
+                                 float* out, float* max_logits, float* exp_sums, float* tmp_out,
+                                 void* stream);
+
+/*
  * vk_paged_gqa_varlen_reduce — the merge of vk_paged_gqa_reduce for
  * variable-length rows: row cu_seqlens_q[s] + j merges its
  * n = min(ceil((L - q_len + j + 1) / P), NP) partitions into out

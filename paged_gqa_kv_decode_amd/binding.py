@@ -30,7 +30,7 @@ EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fu
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
             "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
             "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce",
-            "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel")
+            "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel", "vk_paged_gqa_varlen_dt")
 
 
 class VkError(RuntimeError):
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                       i32, i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_varlen.restype = i32
+    L.vk_paged_gqa_varlen_dt.argtypes = [i32] + L.vk_paged_gqa_varlen.argtypes
+    L.vk_paged_gqa_varlen_dt.restype = i32
     L.vk_paged_gqa_varlen_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                              vp, vp]
     L.vk_paged_gqa_varlen_reduce.restype = i32
@@ -328,11 +330,13 @@ def paged_gqa_varlen(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, 
                      scale: float, partition_size: int, max_num_partitions: int, out=None,
                      max_logits=None, exp_sums=None, tmp_out=None, stream=None) -> None:
     """Enqueue the multi-token (causal, packed rows) kernel: q [total_q,Hq,D]
-    fp16, cu_seqlens_q [S+1] int32; out [total_q,Hq,D] fp32 (unsplit) or the
-    partials [total_q,Hq,NP(,D)] (split)."""
+    fp16 or bf16 (K/V the same type), cu_seqlens_q [S+1] int32; out
+    [total_q,Hq,D] fp32 (unsplit) or the partials [total_q,Hq,NP(,D)] (split)."""
     import torch
-    for t, dt, n in ((q, torch.float16, "q"), (k_cache, torch.float16, "k_cache"),
-                     (v_cache, torch.float16, "v_cache"), (block_tables, torch.int32, "block_tables"),
+    et = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16
+    dtype = DTYPE_BF16 if et == torch.bfloat16 else DTYPE_F16
+    for t, dt, n in ((q, et, "q"), (k_cache, et, "k_cache"),
+                     (v_cache, et, "v_cache"), (block_tables, torch.int32, "block_tables"),
                      (seq_lens, torch.int32, "seq_lens"), (cu_seqlens_q, torch.int32, "cu_seqlens_q"),
                      (out, torch.float32, "out"), (max_logits, torch.float32, "max_logits"),
                      (exp_sums, torch.float32, "exp_sums"), (tmp_out, torch.float32, "tmp_out")):
@@ -352,12 +356,12 @@ def paged_gqa_varlen(q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, 
                           (tmp_out, (T, Hq, max_num_partitions, D), "tmp_out")):
             if t is not None and tuple(t.shape) != shp:
                 raise ValueError(f"{n} must be {shp}")
-    code = lib().vk_paged_gqa_varlen(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+    code = lib().vk_paged_gqa_varlen_dt(
+        dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         _ptr(cu_seqlens_q), S, T, int(max_q_len), Hq, Hkv, D, bs, block_tables.shape[1], nb,
         float(scale), int(partition_size), int(max_num_partitions), _ptr(out), _ptr(max_logits),
         _ptr(exp_sums), _ptr(tmp_out), _stream_handle(stream))
-    _check("vk_paged_gqa_varlen", code)
+    _check("vk_paged_gqa_varlen_dt", code)
 
 
 def paged_gqa_varlen_reduce(max_logits, exp_sums, tmp_out, seq_lens, cu_seqlens_q,

@@ -21,9 +21,11 @@
 namespace vk {
 namespace {
 
-template <int D, int G, int BS>
+// DT: element type of q, K and V (0 fp16, 1 bf16; the decode's bf16 steps,
+// weights split into a bf16 value and its residual for PV).
+template <int D, int G, int BS, int DT>
 struct VarlenKernel {
-    using M = MfmaKernel<D, G, BS, 1, 1, 16, false>;
+    using M = MfmaKernel<D, G, BS, 1, 1, 16, false, DT>;
     using Buf = typename M::Buf;
     using State = typename M::State;
     static constexpr int TPT = 16 / G;    // query tokens per column tile
@@ -36,7 +38,7 @@ struct VarlenKernel {
                                                        const uint4 (&qb)[NKC], int rem, int c) {
         floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < NKC; ++kk) sc = mfma32(b.kr[0][kk], qb[kk], sc);
+        for (int kk = 0; kk < NKC; ++kk) sc = M::qk_mma(b.kr[0][kk], qb[kk], sc);
         float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -60,11 +62,7 @@ struct VarlenKernel {
         st.m = mnew;
 #pragma unroll
         for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
-        uint4 pb;
-        pb.x = pack_half2(p[0], p[1]);
-        pb.y = pack_half2(p[2], p[3]);
-        pb.z = pb.w = 0;
-        return pb;
+        return M::pack_weights(p[0], p[1], p[2], p[3]);
     }
 
     static __device__ void run(const VarlenArgs& va) {
@@ -185,39 +183,45 @@ struct VarlenKernel {
     }
 };
 
-template <int D, int G, int BS>
+template <int D, int G, int BS, int DT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(VK_MFMA_WAVES_PER_EU)))
 void decode_varlen_kernel(VarlenArgs a) {
-    VarlenKernel<D, G, BS>::run(a);
+    VarlenKernel<D, G, BS, DT>::run(a);
 }
 
-template <int D, int G>
-hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+template <int D, int G, int DT>
+hipError_t launch_bs_dt(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
     *ok = true;
     switch (bs) {
-        case 8: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 8>), grid, dim3(64), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 16>), grid, dim3(64), 0, st, a); break;
-        case 32: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 32>), grid, dim3(64), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 8, DT>), grid, dim3(64), 0, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 16, DT>), grid, dim3(64), 0, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_varlen_kernel<D, G, 32, DT>), grid, dim3(64), 0, st, a); break;
         default: *ok = false; return hipSuccess;
     }
     return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_bs(const VarlenArgs& a, int dtype, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    if (dtype == 1) return launch_bs_dt<D, G, 1>(a, bs, grid, st, ok);
+    return launch_bs_dt<D, G, 0>(a, bs, grid, st, ok);
 }
 
 }  // namespace
 
 int varlen_tokens_per_tile(int group) { return group > 0 && group <= 16 ? 16 / group : 0; }
 
-hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, int block_size,
-                                dim3 grid, hipStream_t stream, bool* geometry_ok) {
-    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, block_size, grid, stream, geometry_ok);
-    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, block_size, grid, stream, geometry_ok);
-    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, block_size, grid, stream, geometry_ok);
-    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, block_size, grid, stream, geometry_ok);
+hipError_t launch_decode_varlen(const VarlenArgs& a, int dtype, int group, int head_dim,
+                                int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok) {
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, dtype, block_size, grid, stream, geometry_ok);
     // multi-head: 16 query tokens of one head per tile; multi-query: 1 token x 16 heads
-    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, block_size, grid, stream, geometry_ok);
-    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, block_size, grid, stream, geometry_ok);
-    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, block_size, grid, stream, geometry_ok);
-    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, dtype, block_size, grid, stream, geometry_ok);
     *geometry_ok = false;
     return hipSuccess;
 }

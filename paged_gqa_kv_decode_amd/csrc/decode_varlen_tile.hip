@@ -53,7 +53,11 @@ using namespace mfma;
 constexpr int tile_blocks(int D) { return (D == 256 && VK_TILE_D256_ONE_BLOCK) ? 1 : 2; }
 constexpr int tile_waves(int D) { return 8 / tile_blocks(D); }
 
-template <int D, int G, int BS>
+// DT: element type of q, K and V (0 fp16, 1 bf16).  bf16 runs the same
+// steps on the bf16 matrix instructions, with each softmax weight split into
+// a bf16 value and its bf16 residual and both taken through PV (as the bf16
+// decode does), so the weights keep ~2^-16 relative precision.
+template <int D, int G, int BS, int DT>
 struct TileKernel {
     static constexpr int CB = tile_blocks(D);    // 16-column blocks per wave
     static constexpr int NW = tile_waves(D);     // waves per workgroup
@@ -202,6 +206,13 @@ struct TileKernel {
         return __builtin_bit_cast(uint2, r);
     }
 
+    static __device__ __forceinline__ floatx4 qk_mma(const uint4& a, const uint4& b, const floatx4& c) {
+        if constexpr (DT == 1)
+            return mfma32_bf16(a, b, c);
+        else
+            return mfma32(a, b, c);
+    }
+
     static __device__ __forceinline__ uint4 lds16(const char* lb, int slot, int lane) {
         return *reinterpret_cast<const uint4*>(lb + slot * 1024 + 16 * lane);
     }
@@ -221,11 +232,11 @@ struct TileKernel {
             const uint4 k1 = lds16(lb, NKC + kk, lane);
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                sc[cb][0] = mfma32(k0, qb[cb][kk], sc[cb][0]);
-                sc[cb][1] = mfma32(k1, qb[cb][kk], sc[cb][1]);
+                sc[cb][0] = qk_mma(k0, qb[cb][kk], sc[cb][0]);
+                sc[cb][1] = qk_mma(k1, qb[cb][kk], sc[cb][1]);
             }
         }
-        uint4 pb[CB];
+        uint4 pb[CB], pl[CB];   // weights (bf16: and their residuals)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             float x[8];
@@ -261,10 +272,18 @@ struct TileKernel {
                 ps += p[j];
             }
             st[cb].l += ps;
-            pb[cb].x = pack_half2(p[0], p[1]);
-            pb[cb].y = pack_half2(p[2], p[3]);
-            pb[cb].z = pack_half2(p[4], p[5]);
-            pb[cb].w = pack_half2(p[6], p[7]);
+            if constexpr (DT == 1) {
+                pack_bf16_split(p[0], p[1], pb[cb].x, pl[cb].x);
+                pack_bf16_split(p[2], p[3], pb[cb].y, pl[cb].y);
+                pack_bf16_split(p[4], p[5], pb[cb].z, pl[cb].z);
+                pack_bf16_split(p[6], p[7], pb[cb].w, pl[cb].w);
+            } else {
+                pb[cb].x = pack_half2(p[0], p[1]);
+                pb[cb].y = pack_half2(p[2], p[3]);
+                pb[cb].z = pack_half2(p[4], p[5]);
+                pb[cb].w = pack_half2(p[6], p[7]);
+                pl[cb] = pb[cb];
+            }
         }
         // O^T += V^T P^T, 16 dims at a time: k-slots of lane group c are keys
         // 4c + e, then 16 + 4c + e (the order of the weights in pb).
@@ -275,7 +294,14 @@ struct TileKernel {
             const uint2 lo = read_vt(p), hi = read_vt(p + 16 * RB);
             const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
+            for (int cb = 0; cb < CB; ++cb) {
+                if constexpr (DT == 1) {
+                    st[cb].acc[m] = mfma32_bf16(av, pb[cb], st[cb].acc[m]);
+                    st[cb].acc[m] = mfma32_bf16(av, pl[cb], st[cb].acc[m]);
+                } else {
+                    st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
+                }
+            }
         }
     }
 
@@ -505,23 +531,30 @@ struct TileKernel {
     }
 };
 
-template <int D, int G, int BS>
+template <int D, int G, int BS, int DT>
 __global__ __launch_bounds__(64 * tile_waves(D))
 __attribute__((amdgpu_waves_per_eu(tile_blocks(D) == 2 && D == 256 ? 1 : 2)))
 void varlen_tile_kernel(VarlenArgs a) {
-    TileKernel<D, G, BS>::run(a);
+    TileKernel<D, G, BS, DT>::run(a);
 }
 
-template <int D, int G>
-hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
+template <int D, int G, int DT>
+hipError_t launch_bs_dt(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, bool* ok) {
     *ok = true;
+    const dim3 block(64 * tile_waves(D));
     switch (bs) {
-        case 8: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 8>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 16>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
-        case 32: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 32>), grid, dim3(64 * tile_waves(D)), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 8, DT>), grid, block, 0, st, a); break;
+        case 16: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 16, DT>), grid, block, 0, st, a); break;
+        case 32: hipLaunchKernelGGL((varlen_tile_kernel<D, G, 32, DT>), grid, block, 0, st, a); break;
         default: *ok = false; return hipSuccess;
     }
     return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_bs(const VarlenArgs& a, int dtype, int bs, dim3 grid, hipStream_t st, bool* ok) {
+    if (dtype == 1) return launch_bs_dt<D, G, 1>(a, bs, grid, st, ok);
+    return launch_bs_dt<D, G, 0>(a, bs, grid, st, ok);
 }
 
 }  // namespace
@@ -529,16 +562,16 @@ hipError_t launch_bs(const VarlenArgs& a, int bs, dim3 grid, hipStream_t st, boo
 int varlen_tile_tokens(int group) { return group > 0 && group <= 16 ? 128 / group : 0; }
 int varlen_tile_threads(int head_dim) { return 64 * tile_waves(head_dim); }
 
-hipError_t launch_varlen_tile(const VarlenArgs& a, int group, int head_dim, int block_size,
-                              dim3 grid, hipStream_t stream, bool* geometry_ok) {
-    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, block_size, grid, stream, geometry_ok);
-    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, block_size, grid, stream, geometry_ok);
-    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, block_size, grid, stream, geometry_ok);
-    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, block_size, grid, stream, geometry_ok);
-    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, block_size, grid, stream, geometry_ok);
-    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, block_size, grid, stream, geometry_ok);
-    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, block_size, grid, stream, geometry_ok);
-    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, block_size, grid, stream, geometry_ok);
+hipError_t launch_varlen_tile(const VarlenArgs& a, int dtype, int group, int head_dim,
+                              int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok) {
+    if (group == 4 && head_dim == 128) return launch_bs<128, 4>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 6 && head_dim == 256) return launch_bs<256, 6>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 128) return launch_bs<128, 8>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 8 && head_dim == 256) return launch_bs<256, 8>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 128) return launch_bs<128, 1>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 1 && head_dim == 256) return launch_bs<256, 1>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 128) return launch_bs<128, 16>(a, dtype, block_size, grid, stream, geometry_ok);
+    if (group == 16 && head_dim == 256) return launch_bs<256, 16>(a, dtype, block_size, grid, stream, geometry_ok);
     *geometry_ok = false;
     return hipSuccess;
 }

@@ -452,14 +452,15 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     return VK_OK;
 }
 
-vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_tables, const int32_t* seq_lens,
-                              const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
-                              int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                              int64_t num_blocks, float scale, int32_t partition_size,
-                              int32_t max_num_partitions, float* out, float* max_logits,
-                              float* exp_sums, float* tmp_out, void* stream) {
+static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, float scale, int32_t partition_size,
+                             int32_t max_num_partitions, float* out, float* max_logits,
+                             float* exp_sums, float* tmp_out, void* stream) {
+    if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16) return VK_ERR_DTYPE;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q)
         return VK_ERR_NULL_ARG;
     if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
@@ -513,9 +514,9 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
     va.tiles = (int32_t)tiles;
     const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);
     bool ok = false;
-    hipError_t e = tiled ? vk::launch_varlen_tile(va, group, head_dim, block_size, grid,
+    hipError_t e = tiled ? vk::launch_varlen_tile(va, dtype, group, head_dim, block_size, grid,
                                                   static_cast<hipStream_t>(stream), &ok)
-                         : vk::launch_decode_varlen(va, group, head_dim, block_size, grid,
+                         : vk::launch_decode_varlen(va, dtype, group, head_dim, block_size, grid,
                                                     static_cast<hipStream_t>(stream), &ok);
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);
@@ -533,6 +534,35 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
     p.work_order = VK_ORDER_GRID;
     t_last_plan = p;
     return VK_OK;
+}
+
+vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t total_q,
+                              int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t partition_size,
+                              int32_t max_num_partitions, float* out, float* max_logits,
+                              float* exp_sums, float* tmp_out, void* stream) {
+    return varlen_impl(VK_DTYPE_F16, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
+                       num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
+                       max_num_partitions, out, max_logits, exp_sums, tmp_out, stream);
+}
+
+vk_status vk_paged_gqa_varlen_dt(int32_t dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                 int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, int32_t partition_size, int32_t max_num_partitions,
+                                 float* out, float* max_logits, float* exp_sums, float* tmp_out,
+                                 void* stream) {
+    return varlen_impl(dtype, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, num_seqs,
+                       total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, scale, partition_size, max_num_partitions,
+                       out, max_logits, exp_sums, tmp_out, stream);
 }
 
 vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_sums,

@@ -87,13 +87,14 @@ hipError_t launch_decode_mfma_f32(const DecodeArgs& a, bool mhq, int group, int 
                                   hipStream_t stream, bool* geometry_ok);
 // One wave per workgroup; grid (tiles * max(NP, 1), Hkv, S).  tokens_per_tile
 // receives 16 / G (query tokens per 16-column tile) for the caller's grid.
-hipError_t launch_decode_varlen(const VarlenArgs& a, int group, int head_dim, int block_size,
-                                dim3 grid, hipStream_t stream, bool* geometry_ok);
+// dtype: element type of q, K and V (0 fp16, 1 bf16).
+hipError_t launch_decode_varlen(const VarlenArgs& a, int dtype, int group, int head_dim,
+                                int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok);
 int varlen_tokens_per_tile(int group);
 // Four waves per workgroup of 128 / G query tokens; grid (tiles * max(NP, 1),
 // Hkv, S) with tiles = ceil(max_q_len / varlen_tile_tokens(G)).
-hipError_t launch_varlen_tile(const VarlenArgs& a, int group, int head_dim, int block_size,
-                              dim3 grid, hipStream_t stream, bool* geometry_ok);
+hipError_t launch_varlen_tile(const VarlenArgs& a, int dtype, int group, int head_dim,
+                              int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok);
 int varlen_tile_tokens(int group);
 int varlen_tile_threads(int head_dim);
 hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);

@@ -365,24 +365,27 @@ def make_varlen_custom(*, seq_lens, q_lens, num_q_heads: int, num_kv_heads: int,
                        block_size: int, seed: int, pool_factor: float = 1.0,
                        sigma_q: float = 1.0, sigma_k: float = 1.0, sigma_v: float = 1.0,
                        canaries: bool = False, extra_blocks_per_seq: int = 0,
-                       name: str = "varlen") -> Workload:
+                       name: str = "varlen", dtype: str = "f16") -> Workload:
     """A seeded cache as make_custom builds it, with packed query rows: q is
-    [sum q_lens, Hq, D]; meta holds cu_q (int32 [S + 1]) and q_lens."""
+    [sum q_lens, Hq, D]; meta holds cu_q (int32 [S + 1]) and q_lens.  dtype:
+    "f16" or "bf16" (uint16 bit patterns), as for make_custom."""
     wl = make_custom(seq_lens=seq_lens, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                      head_dim=head_dim, block_size=block_size, seed=seed,
                      pool_factor=pool_factor, sigma_q=sigma_q, sigma_k=sigma_k, sigma_v=sigma_v,
-                     canaries=canaries, extra_blocks_per_seq=extra_blocks_per_seq, name=name)
+                     canaries=canaries, extra_blocks_per_seq=extra_blocks_per_seq, name=name,
+                     dtype=dtype)
     q_lens = np.asarray(q_lens, dtype=np.int32)
     r_q = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(5)[4]))
     total = int(q_lens.sum())
-    wl.q = _draw_fp16(r_q, (total, num_q_heads, head_dim), sigma_q)
+    wl.q = _draw(r_q, (total, num_q_heads, head_dim), sigma_q, dtype)
     wl.meta["cu_q"] = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     wl.meta["q_lens"] = q_lens
     return wl
 
 
-def make_varlen(name: str, *, canaries: bool = False) -> Workload:
-    """Build one named variable-length workload deterministically."""
+def make_varlen(name: str, *, canaries: bool = False, dtype: str = "f16") -> Workload:
+    """Build one named variable-length workload deterministically (dtype:
+    element type of q, K and V, "f16" or "bf16")."""
     spec = VARLEN_WORKLOADS[name]
     i, S = spec["index"], spec["S"]
     r_len = _rngs(i)[0]
@@ -393,6 +396,6 @@ def make_varlen(name: str, *, canaries: bool = False) -> Workload:
         lens = r_len.integers(spec["ctx"][0], spec["ctx"][1], size=S, endpoint=True) + q_lens
     wl = make_varlen_custom(seq_lens=lens, q_lens=q_lens, num_q_heads=spec["Hq"],
                             num_kv_heads=spec["Hkv"], head_dim=spec["D"], block_size=spec["bs"],
-                            seed=1000 + i, canaries=canaries, name=name)
+                            seed=1000 + i, canaries=canaries, name=name, dtype=dtype)
     wl.partition_sizes = (-1,)
     return wl

@@ -282,3 +282,13 @@ def test_plan_varlen_auto_falls_back_under_the_scratch_cap():
     # with a larger cap the rule's own choice stands
     p = _pv(lens, ql, (32, 8, 128), cu=256, cap=2 << 30)
     assert p.partition_size in (256, 512)
+
+
+def test_varlen_dt_rejects_other_element_types():
+    """fp32 (and unknown) element types are refused on the host, before any
+    pointer is looked at or any HIP call is made."""
+    L = vb.lib()
+    for dtype in (vb.DTYPE_F32, 7, -1):
+        code = L.vk_paged_gqa_varlen_dt(dtype, None, None, None, None, None, None, 1, 1, 1, 32, 8,
+                                        128, 16, 1, 1, 1.0, 0, 1, None, None, None, None, None)
+        assert vb.STATUS_NAMES[code] == "DTYPE"
