@@ -46,6 +46,12 @@
  * keeps buffers alive until that work has finished and must enqueue
  * vk_paged_gqa_reduce on the same stream after vk_paged_gqa_decode.
  *
+ * Alignment: q, k_cache, v_cache, out and tmp_out are read and written in
+ * 16-byte vectors and must be 16-byte aligned; the int32 and fp32 arrays
+ * (block_tables, seq_lens, cu_seqlens_q, max_logits, exp_sums, counters)
+ * 4-byte aligned; VK_ERR_ALIGN otherwise.  (torch allocations are 256-byte
+ * aligned; a view that starts mid-row may not be.)
+ *
  * Errors: every function returns a vk_status.  All argument validation is
  * host-only and happens before any HIP call, so a rejected call launches
  * nothing and writes nothing.  A failed launch returns VK_ERR_HIP and
@@ -79,7 +85,8 @@ enum {
     VK_ERR_SEQ_LEN = 6,     /* a host seq_len is < 1 or beyond the page table */
     VK_ERR_SCRATCH_CAP = 7, /* split-KV scratch would exceed the cap */
     VK_ERR_HIP = 8,         /* a HIP runtime call or launch failed */
-    VK_ERR_DTYPE = 9        /* element type not supported by this entry point */
+    VK_ERR_DTYPE = 9,       /* element type not supported by this entry point */
+    VK_ERR_ALIGN = 10       /* a device pointer is not aligned as its kernel reads it */
 };
 
 /* Element type of q, K and V (vk_paged_gqa_decode_dt). */

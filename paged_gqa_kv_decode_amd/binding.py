@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libvkpaged.so")
 
 VK_OK = 0
 STATUS_NAMES = {0: "OK", 1: "NULL_ARG", 2: "BAD_DIM", 3: "GEOMETRY", 4: "BLOCK_SIZE",
-                5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP", 9: "DTYPE"}
+                5: "PARTITION", 6: "SEQ_LEN", 7: "SCRATCH_CAP", 8: "HIP", 9: "DTYPE",
+                10: "ALIGN"}
 DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4, KERNEL_MFMA_W4P2 = 3, 4, 5, 6

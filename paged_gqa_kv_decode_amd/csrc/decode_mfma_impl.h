@@ -100,6 +100,20 @@ struct MfmaKernel {
         float m, l;
     };
 
+    // A split partial (16 bytes of tmp_out) stored at device scope (`sc1`),
+    // i.e. written through this XCD's L2.  Measured on MI355X: partials
+    // kept dirty in L2 until the kernel ends cost split launches of
+    // thousands of workgroups about 3% of their time (32 sequences of 4k-16k
+    // tokens, (24, 4, 256): 222.8 -> 215.5 us at P = 512, 230.0 -> 223.4 us
+    // at P = 256); nontemporal stores did not help.  The merge that reads
+    // them runs in a later launch, or after the single-launch form's own
+    // device-scope release.
+    static __device__ __forceinline__ void store_through(float* p, const float4& v) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        const f4v x = {v.x, v.y, v.z, v.w};
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
+    }
+
     // Page id of token `tok` (0..31 within the step) from the step's ids.
     static __device__ __forceinline__ int page_of(int tok, const int (&pid)[T / BS < 1 ? 1 : T / BS]) {
         if constexpr (BS >= T) {
@@ -380,6 +394,19 @@ struct MfmaKernel {
     // registers hold them in flight; the step then reads its Buf back with
     // ds_read_b128.  Lanes past the valid tokens load a clamped (valid) row
     // and are zeroed on the way back.
+    //
+    // K is loaded in whole 128-byte lines: the operand of QK chunk kk (row i,
+    // 16-byte piece 4 kk + c for lane (i, c)) touches 16 rows at 64 bytes
+    // each, half a line per row, so loading it as it is used costs two
+    // requests per line.  Instead, chunks 2m and 2m + 1 (line m of every row)
+    // come in as two loads of 8 full rows: slot 2m + hf holds rows 8 hf..8 hf+7,
+    // lane l taking row 8 hf + l / 8 and piece (l % 8) ^ f(l / 8) of the line,
+    // with f(r) = r for hf = 0 and r ^ 1 for hf = 1.  The read-back of chunk
+    // kk by lane (i, c) then finds piece 4 (kk % 2) + c of row i at position
+    // 8 (i % 8) + (piece ^ f(i % 8)) of slot 2 (kk / 2) + i / 8; the swizzle
+    // puts the 16 lanes of one read (rows 0..15, same piece) on 16 distinct
+    // 16-byte bank groups.  Registers end up holding exactly the operands of
+    // the direct loads.
     static constexpr bool PF = VK_MFMA_LDS_PF && DT != 2 && T == 16;
     static constexpr int SLOTS = NT * NKC + NDH * NJ;    // 16-byte registers of a Buf
     static constexpr int WAVE_LDS = PF ? SLOTS * 64 * 16 : 0;   // bytes per wave
@@ -392,16 +419,22 @@ struct MfmaKernel {
         const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // elements
         const uint16_t* kbase = a.k + (int64_t)g * BS * D;
         const uint16_t* vbase = a.v + (int64_t)g * BS * D;
+        static_assert(NT == 1 && NKC % 2 == 0, "LDS prefetch: 16-token steps, whole K lines");
+        {
+            const int l = i + 16 * c, r0 = l >> 3;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int tok = FULL ? 16 * tt + i : min(16 * tt + i, remain - 1);
-            const uint4* kp = reinterpret_cast<const uint4*>(
-                kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
-                (int64_t)((sp.off_slot + tok) % BS) * D);
+            for (int hf = 0; hf < 2; ++hf) {
+                const int row = r0 + 8 * hf;
+                const int tok = FULL ? row : min(row, remain - 1);
+                const uint4* kp = reinterpret_cast<const uint4*>(
+                    kbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                    (int64_t)((sp.off_slot + tok) % BS) * D);
+                const int piece = (l & 7) ^ (hf ? (r0 ^ 1) : r0);
 #pragma unroll
-            for (int kk = 0; kk < NKC; ++kk)
-                __builtin_amdgcn_global_load_lds(kp + 4 * kk + c,
-                                                 (lds_ptr_t)(lds + (tt * NKC + kk) * 1024), 16, 0, 2);
+                for (int m = 0; m < NKC / 2; ++m)
+                    __builtin_amdgcn_global_load_lds(kp + 8 * m + piece,
+                                                     (lds_ptr_t)(lds + (2 * m + hf) * 1024), 16, 0, 2);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -426,7 +459,9 @@ struct MfmaKernel {
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int kk = 0; kk < NKC; ++kk) {
-                const uint4 v = *reinterpret_cast<const uint4*>(lds + (tt * NKC + kk) * 1024 + 16 * lane);
+                const int r = i & 7, hf = i >> 3;
+                const int pos = 8 * r + ((4 * (kk & 1) + c) ^ (hf ? (r ^ 1) : r));
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + ((kk >> 1) * 2 + hf) * 1024 + 16 * pos);
                 b.kr[tt][kk] = (FULL || 16 * tt + i < remain) ? v : z;
             }
 #pragma unroll
@@ -604,7 +639,39 @@ struct MfmaKernel {
         const bool wave_bad = __ballot(bad) != 0;
 
         const int64_t row0 = (int64_t)s * Hq + g * G;   // first query head of the group
-        if constexpr (W == 1) {
+        if constexpr (W == 1 && PF) {
+            // The accumulator layout scatters a head's dims over the lanes
+            // (64 four-byte stores per wave, each touching 24 lines); the
+            // normalised rows go through this wave's (now idle) prefetch
+            // slots instead and leave as one 16-byte store per lane and row.
+            static_assert(G * D * 4 <= WAVE_LDS, "staging fits the prefetch slots");
+            const bool out_bad = poison || wave_bad;
+            float* stage = reinterpret_cast<float*>(s_raw);
+            if (i < G) {
+#pragma unroll
+                for (int t = 0; t < NPT; ++t)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        stage[i * D + acc_dim(t, c, rr)] = st.acc[t][rr] / lsum;
+            }
+            __syncthreads();
+            const float nanv = __builtin_nanf("");
+            for (int e = lane; e < G * D / 4; e += 64) {
+                const int h = e / (D / 4), d = 4 * (e % (D / 4));
+                const int64_t r = row0 + h;
+                float4 o = *reinterpret_cast<const float4*>(stage + 4 * e);
+                if (out_bad) o = make_float4(nanv, nanv, nanv, nanv);
+                if (direct)
+                    *reinterpret_cast<float4*>(a.out + r * D + d) = o;
+                else
+                    store_through(a.tmp_out + (r * NP + part) * D + d, o);
+            }
+            if (!direct && i < G && c == 0) {
+                const int64_t pr = (row0 + i) * NP + part;
+                a.max_logits[pr] = st.m;
+                a.exp_sums[pr] = out_bad ? nanv : lsum;
+            }
+        } else if constexpr (W == 1) {
             const bool out_bad = poison || wave_bad;
             if (i < G) {
                 const int64_t r = row0 + i;
@@ -641,7 +708,9 @@ struct MfmaKernel {
             }
             if (lane == 0) s_bad[wave] = wave_bad || poison;
             __syncthreads();
-            for (int idx = tid; idx < PPW * G * D; idx += 64 * W) {
+            // Four dims per thread, one 16-byte store each.
+            const float nanv = __builtin_nanf("");
+            for (int idx = 4 * tid; idx < PPW * G * D; idx += 4 * 64 * W) {
                 const int b = idx / (G * D), h = (idx / D) % G, d = idx % D;
                 const int pb = unit * PPW + b;        // partition of wave group b
                 if constexpr (PPW > 1) {
@@ -654,24 +723,31 @@ struct MfmaKernel {
                 float M = s_m[w0][h];
 #pragma unroll
                 for (int w = 1; w < WP; ++w) M = fmaxf(M, s_m[w0 + w][h]);
-                float num = 0.f, den = 0.f;
+                float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+                float den = 0.f;
 #pragma unroll
                 for (int w = 0; w < WP; ++w) {
                     const float mw = s_m[w0 + w][h];
                     const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-                    num += sc * s_acc[w0 + w][h][d];
+                    const float4 x = *reinterpret_cast<const float4*>(&s_acc[w0 + w][h][d]);
+                    num.x += sc * x.x;
+                    num.y += sc * x.y;
+                    num.z += sc * x.z;
+                    num.w += sc * x.w;
                     den += sc * s_l[w0 + w][h];
                 }
-                const float o = out_bad ? __builtin_nanf("") : num / den;
+                const float4 o = out_bad ? make_float4(nanv, nanv, nanv, nanv)
+                                         : make_float4(num.x / den, num.y / den, num.z / den,
+                                                       num.w / den);
                 const int64_t r = row0 + h;
                 if (direct) {
-                    a.out[r * D + d] = o;
+                    *reinterpret_cast<float4*>(a.out + r * D + d) = o;
                 } else {
                     const int64_t pr = r * NP + pb;
-                    a.tmp_out[pr * D + d] = o;
+                    store_through(a.tmp_out + pr * D + d, o);
                     if (d == 0) {
                         a.max_logits[pr] = M;
-                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : den;
+                        a.exp_sums[pr] = out_bad ? nanv : den;
                     }
                 }
             }

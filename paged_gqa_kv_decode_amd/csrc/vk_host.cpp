@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <initializer_list>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -39,6 +40,17 @@ bool log_enabled() {
         return e && e[0] && e[0] != '0';
     }();
     return on;
+}
+
+// Null pointers pass (their own checks decide whether they are allowed).
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+bool vectors_aligned(std::initializer_list<const void*> v16, std::initializer_list<const void*> v4) {
+    for (const void* p : v16)
+        if (!aligned(p, 16)) return false;
+    for (const void* p : v4)
+        if (!aligned(p, 4)) return false;
+    return true;
 }
 
 vk_status geometry_status(int32_t hq, int32_t hkv, int32_t d) {
@@ -93,6 +105,7 @@ const char* vk_status_string(vk_status s) {
         case VK_ERR_SCRATCH_CAP: return "split-KV scratch over the cap";
         case VK_ERR_HIP: return "HIP error";
         case VK_ERR_DTYPE: return "element type not supported";
+        case VK_ERR_ALIGN: return "device pointer not aligned (16 bytes for q, K, V, out, tmp_out; 4 for int32/fp32 arrays)";
         default: return "unknown status";
     }
 }
@@ -216,6 +229,9 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     if (fused && dtype != VK_DTYPE_F16) return VK_ERR_DTYPE;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return VK_ERR_NULL_ARG;
     if (fused && (!out || (partition_size != 0 && !counters))) return VK_ERR_NULL_ARG;
+    if (!vectors_aligned({q, k_cache, v_cache, out, tmp_out},
+                         {block_tables, seq_lens, max_logits, exp_sums, counters}))
+        return VK_ERR_ALIGN;
     if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0) return VK_ERR_BAD_DIM;
     if (num_seqs > 65535) return VK_ERR_BAD_DIM;  // grid.z limit
     vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
@@ -463,6 +479,9 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
     if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16) return VK_ERR_DTYPE;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seqlens_q)
         return VK_ERR_NULL_ARG;
+    if (!vectors_aligned({q, k_cache, v_cache, out, tmp_out},
+                         {block_tables, seq_lens, cu_seqlens_q, max_logits, exp_sums}))
+        return VK_ERR_ALIGN;
     if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
         total_q <= 0 || max_q_len <= 0 || max_q_len > 65535 || max_q_len > total_q)
         return VK_ERR_BAD_DIM;
@@ -573,6 +592,8 @@ vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_s
                                      float* out, void* stream) {
     if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !cu_seqlens_q || !out)
         return VK_ERR_NULL_ARG;
+    if (!vectors_aligned({tmp_out, out}, {max_logits, exp_sums, seq_lens, cu_seqlens_q}))
+        return VK_ERR_ALIGN;
     if (num_seqs <= 0 || num_seqs > 65535 || num_q_heads <= 0 || num_q_heads > 256 ||
         max_q_len <= 0 || max_q_len > 65535)
         return VK_ERR_BAD_DIM;
@@ -634,6 +655,7 @@ vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums, co
                               int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,
                               float* out, void* stream) {
     if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !out) return VK_ERR_NULL_ARG;
+    if (!vectors_aligned({tmp_out, out}, {max_logits, exp_sums, seq_lens})) return VK_ERR_ALIGN;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_seqs > 65535) return VK_ERR_BAD_DIM;
     if (head_dim != 128 && head_dim != 256) return VK_ERR_GEOMETRY;
     if (partition_size != VK_PARTITION_SMALL && partition_size != VK_PARTITION_LARGE)

@@ -157,6 +157,21 @@ def test_decode_validation(kw, code):
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("kw", [dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2),
+                                dict(P=0, NP=1, out=FAKE + 4), dict(to=FAKE + 12),
+                                dict(bt=FAKE + 2), dict(sl=FAKE + 1), dict(ml=FAKE + 2),
+                                dict(es=FAKE + 3)])
+def test_decode_rejects_misaligned_pointers(kw):
+    """16-byte vectors for q, K, V, out and tmp_out; 4 bytes for the int32 and
+    fp32 arrays: anything else is refused on the host."""
+    assert _decode(**kw) == CODES["ALIGN"]
+    # a 16-byte aligned address that is not 256-byte aligned is fine
+    # (validation then stops at the first real check: none here, so the call
+    # would launch; only check that alignment alone is not the reason)
+    assert _decode(q=FAKE + 16, S=0) == CODES["BAD_DIM"]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
 def test_reduce_validation():
     R = vb.lib().vk_paged_gqa_reduce
     assert R(None, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["NULL_ARG"]
@@ -165,6 +180,9 @@ def test_reduce_validation():
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 96, 512, 4, FAKE, None) == CODES["GEOMETRY"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 0, 4, FAKE, None) == CODES["PARTITION"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 0, FAKE, None) == CODES["PARTITION"]
+    assert R(FAKE, FAKE, FAKE + 4, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE + 8, None) == CODES["ALIGN"]
+    assert R(FAKE + 2, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
