@@ -100,18 +100,25 @@ struct MfmaKernel {
         float m, l;
     };
 
-    // A split partial (16 bytes of tmp_out) stored at device scope (`sc1`),
-    // i.e. written through this XCD's L2.  Measured on MI355X: partials
-    // kept dirty in L2 until the kernel ends cost split launches of
-    // thousands of workgroups about 3% of their time (32 sequences of 4k-16k
-    // tokens, (24, 4, 256): 222.8 -> 215.5 us at P = 512, 230.0 -> 223.4 us
-    // at P = 256); nontemporal stores did not help.  The merge that reads
-    // them runs in a later launch, or after the single-launch form's own
-    // device-scope release.
-    static __device__ __forceinline__ void store_through(float* p, const float4& v) {
-        typedef float f4v __attribute__((ext_vector_type(4)));
-        const f4v x = {v.x, v.y, v.z, v.w};
-        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
+    // A split partial (16 bytes of tmp_out).  With a.write_through it is
+    // stored at device scope (`sc1`), i.e. written through this XCD's L2.
+    // Measured on MI355X: in longest-first launches of several rounds,
+    // partials kept dirty in L2 until the kernel ends cost about 3% of the
+    // launch (32 sequences of 4k-16k tokens, (24, 4, 256): 222.8 -> 215.5 us
+    // at P = 512, 230.0 -> 223.4 us at P = 256; the reduce that reads them
+    // is unchanged); single-round and grid-order launches gained nothing
+    // and keep plain stores.  Nontemporal stores did not help.  The merge
+    // that reads partials runs in a later launch, or after the single-launch
+    // form's own device-scope release.
+    static __device__ __forceinline__ void store_partial(const DecodeArgs& a, float* p,
+                                                         const float4& v) {
+        if (a.write_through) {
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v x = {v.x, v.y, v.z, v.w};
+            asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
+        } else {
+            *reinterpret_cast<float4*>(p) = v;
+        }
     }
 
     // Page id of token `tok` (0..31 within the step) from the step's ids.
@@ -664,7 +671,7 @@ struct MfmaKernel {
                 if (direct)
                     *reinterpret_cast<float4*>(a.out + r * D + d) = o;
                 else
-                    store_through(a.tmp_out + (r * NP + part) * D + d, o);
+                    store_partial(a, a.tmp_out + (r * NP + part) * D + d, o);
             }
             if (!direct && i < G && c == 0) {
                 const int64_t pr = (row0 + i) * NP + part;
@@ -744,7 +751,7 @@ struct MfmaKernel {
                     *reinterpret_cast<float4*>(a.out + r * D + d) = o;
                 } else {
                     const int64_t pr = r * NP + pb;
-                    store_through(a.tmp_out + pr * D + d, o);
+                    store_partial(a, a.tmp_out + pr * D + d, o);
                     if (d == 0) {
                         a.max_logits[pr] = M;
                         a.exp_sums[pr] = out_bad ? nanv : den;

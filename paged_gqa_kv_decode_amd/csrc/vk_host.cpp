@@ -297,6 +297,7 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         kernel = 2 * wgs <= slots ? VK_KERNEL_MFMA_W4 : wgs <= slots ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2;
     }
     a.work_order = 0;
+    a.write_through = 0;
     hipError_t e;
     if (kernel == VK_KERNEL_DOT) {
         e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
@@ -314,6 +315,11 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
             a.work_order = 1;
         // In longest-first order, waves of 8 steps (P / 128 waves per
         // partition) balanced best: 4 waves at P = 512, 2 at P = 256.
+        // Partials written through L2 in the same case: measured on MI355X,
+        // longest-first launches of several rounds lose 3% to partials kept
+        // dirty in L2 until the launch ends; single-round and grid-order
+        // launches gained nothing from writing through.
+        a.write_through = a.work_order;
         if (auto_waves && a.work_order == 1) {
             waves = partition_size / 128;
             kernel = waves == 4 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W2;
@@ -529,6 +535,7 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
     a.max_num_partitions = max_num_partitions;
     a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
     a.work_order = 0;
+    a.write_through = 0;
     va.cu_q = cu_seqlens_q;
     va.tiles = (int32_t)tiles;
     const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);

@@ -27,6 +27,7 @@ struct DecodeArgs {
     int32_t max_num_partitions;
     float scale_log2e;            // scale * log2(e), rounded once to fp32
     int32_t work_order;           // 0: grid order; 1: longest first (split, <= 64 sequences)
+    int32_t write_through;        // 1: split partials stored through L2 (device scope)
 };
 
 // Several query tokens per sequence (causal): `d` as for the decode, with
