@@ -118,8 +118,8 @@ enum {
 enum {
     VK_ORDER_AUTO = 0,           /* longest first when the split grid over <= 64
                                     sequences takes more than one round of the
-                                    device's resident wave slots and pages hold
-                                    >= 16 tokens; else grid order */
+                                    device's resident wave slots; else grid
+                                    order */
     VK_ORDER_GRID = 1,           /* (partition, KV head, sequence) in launch order */
     VK_ORDER_LONGEST_FIRST = 2   /* split, <= 64 sequences: full partitions, then
                                     ragged ones by decreasing length */

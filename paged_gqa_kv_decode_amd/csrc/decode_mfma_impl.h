@@ -100,8 +100,9 @@ struct MfmaKernel {
         float m, l;
     };
 
-    // A split partial (16 bytes of tmp_out).  With a.write_through it is
-    // stored at device scope (`sc1`), i.e. written through this XCD's L2.
+    // A split partial (16 bytes of tmp_out).  With a.write_through, and
+    // always in the single-launch form, it is stored at device scope (`sc1`),
+    // i.e. written through this XCD's L2.
     // Measured on MI355X: in longest-first launches of several rounds,
     // partials kept dirty in L2 until the kernel ends cost about 3% of the
     // launch (32 sequences of 4k-16k tokens, (24, 4, 256): 222.8 -> 215.5 us
@@ -112,13 +113,20 @@ struct MfmaKernel {
     // form's own device-scope release.
     static __device__ __forceinline__ void store_partial(const DecodeArgs& a, float* p,
                                                          const float4& v) {
-        if (a.write_through) {
+        if (FUSED || a.write_through) {
             typedef float f4v __attribute__((ext_vector_type(4)));
             const f4v x = {v.x, v.y, v.z, v.w};
             asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
         } else {
             *reinterpret_cast<float4*>(p) = v;
         }
+    }
+    // A partial's max or exp-sum, under the same rule.
+    static __device__ __forceinline__ void store_partial1(const DecodeArgs& a, float* p, float v) {
+        if (FUSED || a.write_through)
+            asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+        else
+            *p = v;
     }
 
     // Page id of token `tok` (0..31 within the step) from the step's ids.
@@ -675,8 +683,8 @@ struct MfmaKernel {
             }
             if (!direct && i < G && c == 0) {
                 const int64_t pr = (row0 + i) * NP + part;
-                a.max_logits[pr] = st.m;
-                a.exp_sums[pr] = out_bad ? nanv : lsum;
+                store_partial1(a, a.max_logits + pr, st.m);
+                store_partial1(a, a.exp_sums + pr, out_bad ? nanv : lsum);
             }
         } else if constexpr (W == 1) {
             const bool out_bad = poison || wave_bad;
@@ -689,8 +697,8 @@ struct MfmaKernel {
                     const int64_t pr = r * NP + part;
                     dst = a.tmp_out + pr * D;
                     if (c == 0) {
-                        a.max_logits[pr] = st.m;
-                        a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                        store_partial1(a, a.max_logits + pr, st.m);
+                        store_partial1(a, a.exp_sums + pr, out_bad ? __builtin_nanf("") : lsum);
                     }
                 }
 #pragma unroll
@@ -753,8 +761,8 @@ struct MfmaKernel {
                     const int64_t pr = r * NP + pb;
                     store_partial(a, a.tmp_out + pr * D + d, o);
                     if (d == 0) {
-                        a.max_logits[pr] = M;
-                        a.exp_sums[pr] = out_bad ? nanv : den;
+                        store_partial1(a, a.max_logits + pr, M);
+                        store_partial1(a, a.exp_sums + pr, out_bad ? nanv : den);
                     }
                 }
             }
@@ -770,19 +778,21 @@ struct MfmaKernel {
     // head.  Arrival is counted in counters[s * Hkv + g] with a device-scope
     // atomic increment that wraps to zero at n - 1: the last arrival sees
     // n - 1 and leaves the counter at zero for the next call.
-    // Ordering across XCDs (each has its own L2): every wave waits for its
-    // partial stores to be acknowledged, the barrier gathers the workgroup,
-    // then one lane releases at device scope (L2 write-back) before its
-    // increment; the last arrival acquires (L2 invalidate) before the
-    // barrier that lets its waves read the other partials.  One release per
-    // workgroup, one acquire per (sequence, KV head).
+    // Ordering across XCDs (each has its own L2): the partials were stored
+    // at device scope (written through L2), so once every wave has waited
+    // for its stores to be acknowledged they are visible to every XCD; the
+    // barrier gathers the workgroup and one lane increments.  No L2
+    // write-back per workgroup (that release, measured: 2-3x the launch time
+    // at thousands of workgroups).  The last arrival acquires (L2
+    // invalidate: its XCD may hold stale lines of these buffers from an
+    // earlier call) before the barrier that lets its waves read the other
+    // partials: one acquire per (sequence, KV head).
     static __device__ void merge_if_last(const DecodeArgs& a, int g, int s, int n, int64_t row0,
                                          int tid) {
         __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             const unsigned old = atomicInc(a.counters + (int64_t)s * a.num_kv_heads + g, (unsigned)(n - 1));
             const bool last = old == (unsigned)(n - 1);
             if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -793,6 +803,30 @@ struct MfmaKernel {
         const int NP = a.max_num_partitions;
         const int wave = tid >> 6, lane = tid & 63;
         constexpr int kChunks = D / merge::kDims;
+        if (n <= merge::kGroups) {
+            // Few partitions: NB pieces per wave with all their loads in flight.
+            constexpr int NB = 4;
+            for (int it0 = wave * NB; it0 < G * kChunks; it0 += W * NB) {
+                const float* ml[NB];
+                const float* es[NB];
+                const float4* to[NB];
+                float4* dst[NB];
+                bool ok[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int it = min(it0 + b, G * kChunks - 1);
+                    ok[b] = it0 + b < G * kChunks;
+                    const int h = it / kChunks, chunk = it % kChunks;
+                    const int64_t r = row0 + h;
+                    ml[b] = a.max_logits + r * NP;
+                    es[b] = a.exp_sums + r * NP;
+                    to[b] = reinterpret_cast<const float4*>(a.tmp_out + r * NP * D + chunk * merge::kDims);
+                    dst[b] = reinterpret_cast<float4*>(a.out + r * D + chunk * merge::kDims);
+                }
+                merge::merge_columns_few<NB>(ml, es, to, ok, D / 4, n, lane, dst);
+            }
+            return;
+        }
         for (int it = wave; it < G * kChunks; it += W) {
             const int h = it / kChunks, chunk = it % kChunks;
             const int64_t r = row0 + h;

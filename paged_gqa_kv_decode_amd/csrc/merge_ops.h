@@ -102,5 +102,52 @@ __device__ __forceinline__ void merge_columns(const float* ml, const float* es, 
         dst[lane] = make_float4(st.acc.x / st.l, st.acc.y / st.l, st.acc.z / st.l, st.acc.w / st.l);
 }
 
+// The same merge for NB pieces of work at once (one (sequence, head, 32 dims)
+// each, `ok[b]` false for an unused piece) when every piece has n <= kGroups
+// partitions: each lane holds at most one partition per piece, so all the
+// pieces' loads are issued before the first fold, where merge_columns would
+// wait for one piece's loads at a time.  Per piece the steps are those of
+// merge_columns (one fold of partition lane / kCols into the empty state,
+// then the same shuffle tree), so the results are bit-identical to it.
+template <int NB>
+__device__ __forceinline__ void merge_columns_few(const float* const (&ml)[NB],
+                                                  const float* const (&es)[NB],
+                                                  const float4* const (&to)[NB],
+                                                  const bool (&ok)[NB], int row4, int n, int lane,
+                                                  float4* const (&dst)[NB]) {
+    const int c = lane % kCols, grp = lane / kCols;
+    float m[NB], l[NB];
+    float4 o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const bool ld = ok[b] && grp < n;
+        m[b] = ld ? ml[b][grp] : -INFINITY;
+        l[b] = ld ? es[b][grp] : 0.f;
+        o[b] = ld ? to[b][(int64_t)grp * row4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        State st;
+        st.m = -INFINITY;
+        st.l = 0.f;
+        st.acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m[b] != -INFINITY) fold(st, m[b], l[b], o[b]);
+#pragma unroll
+        for (int off = kCols; off < 64; off <<= 1) {
+            State t;
+            t.m = __shfl_xor(st.m, off);
+            t.l = __shfl_xor(st.l, off);
+            t.acc.x = __shfl_xor(st.acc.x, off);
+            t.acc.y = __shfl_xor(st.acc.y, off);
+            t.acc.z = __shfl_xor(st.acc.z, off);
+            t.acc.w = __shfl_xor(st.acc.w, off);
+            fold_state(st, t);
+        }
+        if (ok[b] && lane < kCols)
+            dst[b][lane] = make_float4(st.acc.x / st.l, st.acc.y / st.l, st.acc.z / st.l,
+                                       st.acc.w / st.l);
+    }
+}
+
 }  // namespace merge
 }  // namespace vk

@@ -307,11 +307,11 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         // Longest-first work order when the split grid takes more than one
         // round of the wave slots, so the order decides the tail.  Measured on
         // MI355X at P = 512: 9-20% faster for 16-64 sequences of 2k-32k
-        // tokens with 16- and 32-token pages; with 8-token pages grid order
-        // was as fast or faster (up to 9%), so auto keeps grid order there.
+        // tokens with 16- and 32-token pages, 3% for 64 mixed-length
+        // sequences with 8-token pages.
         const bool lf_ok = partition_size > 0 && num_seqs <= 64;
         if (lf_ok && (t_order_choice == VK_ORDER_LONGEST_FIRST ||
-                      (t_order_choice == VK_ORDER_AUTO && wgs * waves > slots && block_size >= 16)))
+                      (t_order_choice == VK_ORDER_AUTO && wgs * waves > slots)))
             a.work_order = 1;
         // In longest-first order, waves of 8 steps (P / 128 waves per
         // partition) balanced best: 4 waves at P = 512, 2 at P = 256.
