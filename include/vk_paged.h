@@ -409,18 +409,16 @@ int32_t vk_select_work_order(int32_t order);
 
 /*
  * vk_select_varlen_kernel — A/B switch for this thread's later
- * vk_plan_varlen and vk_paged_gqa_varlen calls: VK_KERNEL_AUTO (tiles when
- * the longest query run of the batch is at least VK_VARLEN_TILE_MIN_Q
- * tokens, else columns: measured on MI355X, the tiles win from 4 query
- * tokens on for every admitted grouped geometry, the columns below, and
- * one token is the decode's own step), VK_KERNEL_VARLEN_COLUMNS or
- * VK_KERNEL_VARLEN_TILES.
+ * vk_plan_varlen and vk_paged_gqa_varlen calls: VK_KERNEL_AUTO (columns
+ * when the longest query run of the batch fits one 16-column tile, i.e. is
+ * at most 16 / G tokens for G = Hq / Hkv, so every K/V step is read once;
+ * tiles above that: measured on MI355X for G = 4, 6, 8),
+ * VK_KERNEL_VARLEN_COLUMNS or VK_KERNEL_VARLEN_TILES.
  * Both kernels compute the same rows to the same tolerance; the planner's
  * split rule depends on the kernel, so plan and launch under the same
  * setting.  Returns the previous setting, or -1 for an unknown value
  * (setting kept).
  */
-#define VK_VARLEN_TILE_MIN_Q 4
 int32_t vk_select_varlen_kernel(int32_t kernel);
 
 /* Human-readable name of a status code (static storage). */

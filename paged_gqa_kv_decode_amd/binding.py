@@ -24,7 +24,6 @@ DTYPE_F16, DTYPE_BF16, DTYPE_F32 = 0, 1, 2
 KERNEL_AUTO, KERNEL_DOT, KERNEL_MFMA = 0, 1, 2
 KERNEL_MFMA_W1, KERNEL_MFMA_W2, KERNEL_MFMA_W4, KERNEL_MFMA_W4P2 = 3, 4, 5, 6
 KERNEL_VARLEN_COLUMNS, KERNEL_VARLEN_TILES = 7, 8
-VARLEN_TILE_MIN_Q = 4
 ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",

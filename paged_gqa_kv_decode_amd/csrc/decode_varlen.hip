@@ -9,7 +9,9 @@
 //
 // The decode kernel's matrix-core step is reused unchanged (MfmaKernel in
 // decode_mfma_impl.h: 16-token steps, K as the A operand, V transposed in
-// registers).  What changes is the meaning of the 16 MFMA columns: in the
+// registers, the next step's K/V loaded straight into the wave's LDS slots
+// while the current one computes).  What changes is the meaning of the 16
+// MFMA columns: in the
 // decode they are the G heads of a KV group; here they are (query token,
 // head) pairs, 16 / G tokens x G heads per tile, so every K/V load of a step
 // serves that many queries.  Each column carries its own causal limit; the
@@ -31,6 +33,31 @@ struct VarlenKernel {
     static constexpr int TPT = 16 / G;    // query tokens per column tile
     static constexpr int NC = TPT * G;    // columns in use
     static constexpr int NKC = M::NKC, NDH = M::NDH, NPT = M::NPT, CH = M::CH;
+    static_assert(M::PF, "16-bit types: LDS prefetch");
+    static_assert(16 * D * 4 <= M::WAVE_LDS, "output staging fits the prefetch slots");
+
+    // Column col of the tile: its row, and whether and what it writes for
+    // this launch item (0 nothing, 1 zeros: unsplit and no visible key,
+    // 2 its result); `cbad` poisons a written result.
+    struct Col {
+        int64_t row;
+        int mode;
+        bool cbad;
+    };
+    static __device__ __forceinline__ Col column(const VarlenArgs& va, int col, int tile, int part,
+                                                 int g, int q0, int qlen, int L, int t_begin,
+                                                 bool wave_bad) {
+        const DecodeArgs& a = va.d;
+        const int P = a.partition_size, NP = a.max_num_partitions;
+        const int jt = tile * TPT + col / G;
+        const bool valid = col < NC && jt < qlen;
+        const int lim = valid ? L - qlen + jt + 1 : 0;
+        Col r;
+        r.row = ((int64_t)q0 + jt) * a.num_q_heads + g * G + col % G;
+        r.mode = !valid ? 0 : (P == 0 && lim <= 0) ? 1 : (lim <= t_begin) ? 0 : 2;
+        r.cbad = wave_bad || (P > 0 && part == NP - 1 && lim > t_begin + P);
+        return r;
+    }
 
     // QK of one 16-key step and the online-softmax update per column; `rem`
     // is how many of the step's keys this lane's column may see (<= 0: none).
@@ -88,11 +115,9 @@ struct VarlenKernel {
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) kv_end = max(kv_end, __shfl_xor(kv_end, off));
         int t_begin = 0, t_end = kv_end;
-        bool col_poison = false;
         if (P > 0) {
             t_begin = part * P;
             t_end = min(kv_end, t_begin + P);
-            if (part == NP - 1 && lim > t_begin + P) col_poison = true;   // beyond the grid
         }
         const int64_t row = ((int64_t)q0 + jt) * Hq + h;
         if (t_end <= t_begin || poison) {
@@ -121,6 +146,7 @@ struct VarlenKernel {
         }
         const int e_lim = min(lim, t_end);   // this column's last visible key + 1 here
 
+        __shared__ __attribute__((aligned(16))) char lds[M::WAVE_LDS];
         State st;
 #pragma unroll
         for (int t = 0; t < NPT; ++t) st.acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -138,48 +164,72 @@ struct VarlenKernel {
                     bad = true;
                 }
             }
-            int t0 = c0;
-            for (; t0 + 16 <= c1; t0 += 16) {
+            // Full 16-key steps, then at most one partial step; step k + 1
+            // is in flight to LDS while step k computes.
+            const int nfull = (c1 - c0) / 16;
+            const int tl = c0 + 16 * nfull;
+            if (nfull > 0)
+                M::template issue_lds<true>(a, lds, M::step_pages(pg, 0), g, 16, i, c);
+            else if (tl < c1)
+                M::template issue_lds<false>(a, lds, M::step_pages(pg, tl - c0), g, c1 - tl, i, c);
+            for (int k = 0; k < nfull; ++k) {
                 Buf b;
-                M::template issue<true>(a, b, pg, g, t0 - c0, 16, i, c);
+                M::wait_lds_loads();
+                M::template read_lds<true>(b, lds, 16, lane, i, c);
+                M::wait_lds_reads();
+                if (k + 1 < nfull)
+                    M::template issue_lds<true>(a, lds, M::step_pages(pg, 16 * (k + 1)), g, 16, i, c);
+                else if (tl < c1)
+                    M::template issue_lds<false>(a, lds, M::step_pages(pg, tl - c0), g, c1 - tl, i, c);
+                const int t0 = c0 + 16 * k;
                 M::pv(st, b, qk_softmax(a, st, b, qb, e_lim - t0, c));
             }
-            if (t0 < c1) {
+            if (tl < c1) {
                 Buf b;
-                M::template issue<false>(a, b, pg, g, t0 - c0, c1 - t0, i, c);
-                M::pv(st, b, qk_softmax(a, st, b, qb, min(e_lim, c1) - t0, c));
+                M::wait_lds_loads();
+                M::template read_lds<false>(b, lds, c1 - tl, lane, i, c);
+                M::wait_lds_reads();
+                M::pv(st, b, qk_softmax(a, st, b, qb, min(e_lim, c1) - tl, c));
             }
         }
         float lsum = st.l + __shfl_xor(st.l, 16);
         lsum += __shfl_xor(lsum, 32);
-        const bool out_bad = col_poison || __ballot(bad) != 0;
-        if (!valid) return;
-        if (P == 0 && lim <= 0) {   // a query that sees no key: zeros
-            float* o = a.out + row * D;
-            for (int d = 4 * c; d < D; d += 16) *reinterpret_cast<float4*>(o + d) = make_float4(0.f, 0.f, 0.f, 0.f);
-            return;
+        const bool wave_bad = __ballot(bad) != 0;
+
+        // The accumulator layout scatters a column's dims over the lanes; the
+        // normalised columns go through the (now idle) prefetch slots and
+        // leave as 16-byte stores, one row of D floats per column.
+        float* stage = reinterpret_cast<float*>(lds);
+        if (valid) {
+#pragma unroll
+            for (int dh = 0; dh < NDH; ++dh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        stage[i * D + 128 * dh + 8 * (4 * c + rr) + e] = st.acc[dh * 8 + e][rr] / lsum;
         }
-        if (lim <= t_begin) return;   // this column does not see this partition
-        float* dst;
-        if (P == 0) {
-            dst = a.out + row * D;
-        } else {
-            const int64_t pr = row * NP + part;
-            dst = a.tmp_out + pr * D;
-            if (c == 0) {
+        if (c == 0) {
+            const Col me = column(va, i, tile, part, g, q0, qlen, L, t_begin, wave_bad);
+            if (P > 0 && me.mode == 2) {
+                const int64_t pr = me.row * NP + part;
                 a.max_logits[pr] = st.m;
-                a.exp_sums[pr] = out_bad ? __builtin_nanf("") : lsum;
+                a.exp_sums[pr] = me.cbad ? __builtin_nanf("") : lsum;
             }
         }
-#pragma unroll
-        for (int dh = 0; dh < NDH; ++dh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int d = 128 * dh + 8 * (4 * c + rr) + e;
-                    dst[d] = out_bad ? __builtin_nanf("") : st.acc[dh * 8 + e][rr] / lsum;
-                }
+        __syncthreads();
+        const float nanv = __builtin_nanf("");
+        for (int e = lane; e < 16 * (D / 4); e += 64) {
+            const int col = e / (D / 4), d = 4 * (e % (D / 4));
+            const Col cl = column(va, col, tile, part, g, q0, qlen, L, t_begin, wave_bad);
+            if (cl.mode == 0) continue;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (cl.mode == 2)
+                o = cl.cbad ? make_float4(nanv, nanv, nanv, nanv)
+                            : *reinterpret_cast<const float4*>(stage + col * D + d);
+            float* dst = P == 0 ? a.out + cl.row * D : a.tmp_out + (cl.row * NP + part) * D;
+            *reinterpret_cast<float4*>(dst + d) = o;
+        }
     }
 };
 

@@ -22,10 +22,18 @@ thread_local int32_t t_kernel_choice = VK_KERNEL_AUTO;
 thread_local int32_t t_order_choice = VK_ORDER_AUTO;
 thread_local int32_t t_varlen_choice = VK_KERNEL_AUTO;
 
-// The multi-token kernel for a batch whose longest query run is max_q tokens.
-int32_t varlen_kernel(int64_t max_q) {
+// The multi-token kernel for a batch whose longest query run is max_q tokens,
+// G = `group` query heads per KV head.  Measured on MI355X (32 sequences of
+// 4k-16k tokens, G = 4, 6, 8): the column kernel is faster while one of its
+// 16-column tiles (16 / G tokens x G heads) holds every sequence's queries,
+// so each K/V step is read once and used straight from the prefetch slots
+// (G = 4, 4 tokens: 281 vs 344 us); with more tokens it reads the keys once
+// per tile and the LDS-tiled kernel, which shares them among 128 columns,
+// wins (G = 6, 4 tokens: 531 vs 365 us).
+int32_t varlen_kernel(int64_t max_q, int group) {
     if (t_varlen_choice != VK_KERNEL_AUTO) return t_varlen_choice;
-    return max_q >= VK_VARLEN_TILE_MIN_Q ? VK_KERNEL_VARLEN_TILES : VK_KERNEL_VARLEN_COLUMNS;
+    return max_q > vk::varlen_tokens_per_tile(group) ? VK_KERNEL_VARLEN_TILES
+                                                     : VK_KERNEL_VARLEN_COLUMNS;
 }
 
 struct Geometry {
@@ -410,8 +418,8 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     if (cap_tokens > INT32_MAX) return VK_ERR_BAD_DIM;
     int64_t max_q = 0;
     for (int32_t s = 0; s < num_seqs; ++s) max_q = std::max<int64_t>(max_q, q_lens_host[s]);
-    const int32_t kernel = varlen_kernel(max_q);
     const int group = num_q_heads / num_kv_heads;
+    const int32_t kernel = varlen_kernel(max_q, group);
     const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
     const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
     const int waves_per_tile = tiled ? vk::varlen_tile_threads(head_dim) / 64 : 1;
@@ -507,7 +515,7 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
         return VK_ERR_PARTITION;
     }
     const int group = num_q_heads / num_kv_heads;
-    const int32_t kernel = varlen_kernel(max_q_len);
+    const int32_t kernel = varlen_kernel(max_q_len, group);
     const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
     const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
     const int64_t tiles = (max_q_len + tpt - 1) / tpt;

@@ -250,11 +250,20 @@ def test_plan_varlen_scratch_cap():
     assert e.value.name == "SCRATCH_CAP"
 
 
+@pytest.mark.parametrize("geom,fits", [((32, 8, 128), 4), ((24, 4, 256), 2), ((16, 2, 128), 2),
+                                       ((16, 2, 256), 2), ((16, 16, 128), 16), ((16, 1, 128), 1)])
+def test_plan_varlen_kernel_choice_rule(geom, fits):
+    # The longest query run decides: while it fits one 16-column tile of the
+    # column kernel (16 / G tokens) -> columns, above -> LDS tiles.
+    C, T = vb.KERNEL_VARLEN_COLUMNS, vb.KERNEL_VARLEN_TILES
+    assert _pv([2000, 1500], [fits, 1], geom, cu=4).kernel == C
+    assert _pv([2000, 1500], [1, fits], geom, cu=4).kernel == C
+    assert _pv([2000, 1500], [fits + 1, 1], geom, cu=4).kernel == T
+
+
 def test_plan_varlen_kernel_choice():
-    # The longest query run decides: >= 4 tokens -> LDS tiles, else columns.
-    assert vb.VARLEN_TILE_MIN_Q == 4
     assert _pv([2000, 1500], [3, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS
-    assert _pv([2000, 1500], [4, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
+    assert _pv([2000, 1500], [5, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_TILES
     prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
     try:
         assert _pv([2000, 1500], [100, 1], (32, 8, 128), cu=4).kernel == vb.KERNEL_VARLEN_COLUMNS

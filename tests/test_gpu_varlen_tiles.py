@@ -40,12 +40,20 @@ def test_prefill_workload_picks_tiles_and_matches(orc):
 
 
 @pytest.mark.parametrize("P", [-1, 0, 512])
-def test_verify_workload_picks_tiles_and_matches(orc, P):
-    """Speculative-decode verification (4 query tokens): auto picks the tiled
-    kernel; the whole batch against the oracle."""
+def test_verify_workload_both_kernels_match(orc, P):
+    """Speculative-decode verification (4 query tokens at G = 4: one column
+    tile per sequence): auto picks the column kernel; both kernels on the
+    whole batch against the oracle."""
     wl = make_varlen("verify32_q4")
     ref = oracle_varlen(orc, wl)
     gpu, plan, _ = run_varlen(wl, P)
+    assert plan.kernel == vb.KERNEL_VARLEN_COLUMNS
+    assert_parity(gpu, ref, f"verify32_q4 columns P={plan.partition_size}")
+    prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_TILES)
+    try:
+        gpu, plan, _ = run_varlen(wl, P)
+    finally:
+        vb.select_varlen_kernel(prev)
     assert plan.kernel == vb.KERNEL_VARLEN_TILES
     say(f"[tiles] verify32_q4 P={plan.partition_size}")
     assert_parity(gpu, ref, f"verify32_q4 tiles P={plan.partition_size}")
