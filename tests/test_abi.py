@@ -311,6 +311,36 @@ def test_plan_varlen_auto_falls_back_under_the_scratch_cap():
     assert p.partition_size in (256, 512)
 
 
+def _varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, S=2, T=8, mq=4, Hq=32, Hkv=8,
+             D=128, bs=16, mb=8, nb=64, scale=0.088, P=256, NP=2, out=FAKE, ml=FAKE, es=FAKE,
+             to=FAKE)
+    a.update(kw)
+    return vb.lib().vk_paged_gqa_varlen(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["S"],
+                                        a["T"], a["mq"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                        a["mb"], a["nb"], a["scale"], a["P"], a["NP"], a["out"],
+                                        a["ml"], a["es"], a["to"], None)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("kw", [dict(q=FAKE + 8), dict(k=FAKE + 4), dict(v=FAKE + 2),
+                                dict(to=FAKE + 12), dict(P=0, NP=1, out=FAKE + 4),
+                                dict(cu=FAKE + 2), dict(bt=FAKE + 1), dict(ml=FAKE + 2)])
+def test_varlen_rejects_misaligned_pointers(kw):
+    assert _varlen(**kw) == CODES["ALIGN"]
+    assert _varlen(q=FAKE + 16, S=0) == CODES["BAD_DIM"]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+def test_varlen_reduce_rejects_misaligned_pointers():
+    R = vb.lib().vk_paged_gqa_varlen_reduce
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 32, 128, 256, 2, FAKE, None)
+    for pos, off in [(2, 4), (11, 8), (0, 2), (4, 1)]:
+        args = list(ok)
+        args[pos] = FAKE + off
+        assert R(*args) == CODES["ALIGN"], (pos, off)
+
+
 def test_varlen_dt_rejects_other_element_types():
     """fp32 (and unknown) element types are refused on the host, before any
     pointer is looked at or any HIP call is made."""
