@@ -274,6 +274,8 @@ def bench_varlen(args, wl, gen_s):
     stream = torch.cuda.current_stream()
     vb.select_varlen_kernel({"auto": vb.KERNEL_AUTO, "columns": vb.KERNEL_VARLEN_COLUMNS,
                              "tiles": vb.KERNEL_VARLEN_TILES}[args.varlen_kernel])
+    vb.select_work_order({"auto": vb.ORDER_AUTO, "grid": vb.ORDER_GRID,
+                          "longest": vb.ORDER_LONGEST_FIRST}[args.order])
     step0 = vb.VarlenStep(q, k, v, bt, sl, cu, wl.seq_lens, ql, wl.scale, P_req)
     kname = {vb.KERNEL_VARLEN_COLUMNS: "varlen_columns",
              vb.KERNEL_VARLEN_TILES: "varlen_tiles"}[step0.plan.kernel]
@@ -312,6 +314,7 @@ def bench_varlen(args, wl, gen_s):
         one_step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t
+    order_ran = vb.last_plan().work_order   # of the last launch
     dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     ms = wall * 1e3 / args.steps
@@ -340,7 +343,8 @@ def bench_varlen(args, wl, gen_s):
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "total_q": int(ql.sum()), "max_q_len": mq, "partition_size": P,
-                   "max_num_partitions": NP, "decode_kernel": kname},
+                   "max_num_partitions": NP, "decode_kernel": kname,
+                   "work_order": {1: "grid", 2: "longest_first"}.get(order_ran, str(order_ran))},
         "roofline": roof,
         "kernel_us": {"varlen_mean": round(float(dec_ms.mean()) * 1e3, 2),
                       "varlen_median": round(float(np.median(dec_ms)) * 1e3, 2),

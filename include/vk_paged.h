@@ -114,7 +114,9 @@ enum {
                                      LDS tiles shared by all of them */
 };
 
-/* Work order of the matrix-core decode; see vk_select_work_order. */
+/* Work order of the matrix-core decode (and of the multi-token column kernel
+ * when every sequence's queries fit one of its tiles); see
+ * vk_select_work_order. */
 enum {
     VK_ORDER_AUTO = 0,           /* longest first when the split grid over <= 64
                                     sequences takes more than one round of the
@@ -401,7 +403,10 @@ int32_t vk_select_decode_kernel(int32_t kernel);
  * vk_select_work_order — A/B switch for the order in which this thread's
  * later matrix-core decode launches hand out their (partition, KV head,
  * sequence) items.  Longest first applies only to split launches over at most
- * 64 sequences (others run in grid order whatever the setting); it changes
+ * 64 sequences (others run in grid order whatever the setting), and to the
+ * multi-token column kernel's split launches when one tile holds every
+ * sequence's queries (the same items; write-through partials come with it
+ * there); it changes
  * which workgroup computes which partial, never a result.  Returns the
  * previous setting, or -1 for an unknown value (setting kept).
  */

@@ -95,9 +95,19 @@ struct VarlenKernel {
     static __device__ void run(const VarlenArgs& va) {
         const DecodeArgs& a = va.d;
         const int lane = threadIdx.x, i = lane & 15, c = lane >> 4;
-        const int tile = (int)(blockIdx.x % (unsigned)va.tiles);
-        const int part = (int)(blockIdx.x / (unsigned)va.tiles);
-        const int g = blockIdx.y, s = blockIdx.z;
+        int tile, part, g, s;
+        if (a.work_order == 1) {
+            // One tile per sequence (the host's condition for this order):
+            // the items are the decode's (partition, KV head, sequence), so
+            // its longest-first mapping applies as it is.
+            if (!M::longest_first(a, part, g, s)) return;
+            tile = 0;
+        } else {
+            tile = (int)(blockIdx.x % (unsigned)va.tiles);
+            part = (int)(blockIdx.x / (unsigned)va.tiles);
+            g = blockIdx.y;
+            s = blockIdx.z;
+        }
         const int q0 = va.cu_q[s], qlen = va.cu_q[s + 1] - q0;
         if (qlen <= 0 || tile * TPT >= qlen) return;
         const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
@@ -213,8 +223,8 @@ struct VarlenKernel {
             const Col me = column(va, i, tile, part, g, q0, qlen, L, t_begin, wave_bad);
             if (P > 0 && me.mode == 2) {
                 const int64_t pr = me.row * NP + part;
-                a.max_logits[pr] = st.m;
-                a.exp_sums[pr] = me.cbad ? __builtin_nanf("") : lsum;
+                M::store_partial1(a, a.max_logits + pr, st.m);
+                M::store_partial1(a, a.exp_sums + pr, me.cbad ? __builtin_nanf("") : lsum);
             }
         }
         __syncthreads();
@@ -227,8 +237,10 @@ struct VarlenKernel {
             if (cl.mode == 2)
                 o = cl.cbad ? make_float4(nanv, nanv, nanv, nanv)
                             : *reinterpret_cast<const float4*>(stage + col * D + d);
-            float* dst = P == 0 ? a.out + cl.row * D : a.tmp_out + (cl.row * NP + part) * D;
-            *reinterpret_cast<float4*>(dst + d) = o;
+            if (P == 0)
+                *reinterpret_cast<float4*>(a.out + cl.row * D + d) = o;
+            else
+                M::store_partial(a, a.tmp_out + (cl.row * NP + part) * D + d, o);
         }
     }
 };

@@ -544,6 +544,18 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
     a.scale_log2e = (float)((double)scale * 1.4426950408889634073599246810019);
     a.work_order = 0;
     a.write_through = 0;
+    // The column kernel with one tile per sequence, split, over <= 64
+    // sequences has the decode's items: its longest-first order and
+    // write-through partials apply when the grid takes more than one round
+    // of the wave slots (measured on 32 sequences of 4k-16k tokens, 4 query
+    // tokens at G = 4).
+    if (!tiled && tiles == 1 && partition_size > 0 && num_seqs <= 64 &&
+        (t_order_choice == VK_ORDER_LONGEST_FIRST ||
+         (t_order_choice == VK_ORDER_AUTO &&
+          gx * num_kv_heads * (int64_t)num_seqs > wave_slots()))) {
+        a.work_order = 1;
+        a.write_through = 1;
+    }
     va.cu_q = cu_seqlens_q;
     va.tiles = (int32_t)tiles;
     const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);
@@ -565,7 +577,7 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
     p.grid[1] = (int32_t)grid.y;
     p.grid[2] = (int32_t)grid.z;
     p.block = tiled ? vk::varlen_tile_threads(head_dim) : 64;
-    p.work_order = VK_ORDER_GRID;
+    p.work_order = a.work_order ? VK_ORDER_LONGEST_FIRST : VK_ORDER_GRID;
     t_last_plan = p;
     return VK_OK;
 }

@@ -19,8 +19,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def column_kernel():
-    """These tests cover the column kernel (auto would pick the LDS-tiled one
-    from 4 query tokens on; that kernel has its own tests)."""
+    """These tests cover the column kernel (auto picks the LDS-tiled one when
+    a sequence has more than 16 / G query tokens; that kernel has its own
+    tests)."""
     prev = vb.select_varlen_kernel(vb.KERNEL_VARLEN_COLUMNS)
     yield
     vb.select_varlen_kernel(prev)
@@ -223,3 +224,29 @@ def test_varlen_argument_errors():
     with pytest.raises(vb.VkError) as e:
         vb.paged_gqa_varlen(q, k, v, bt, sl, cu, 4, wl.scale, 128, 1, out)
     assert e.value.name == "PARTITION"
+
+
+@pytest.mark.parametrize("P", [256, 512])
+def test_single_tile_longest_first_matches_grid_order(orc, P):
+    """Every sequence's queries fit one column tile (<= 16 / G tokens): the
+    split launch takes the decode's longest-first order over (partition,
+    KV head, sequence) when the grid takes several rounds, with its partials
+    written through L2.  Same partials as grid order, so bit-identical, and
+    both within the oracle's bar; rows with q_len = 0 and L = 1 included."""
+    lens = [4000, 9000, 300, 1, 7000, 2048, 513, 12000] * 4
+    qlens = [4, 1, 3, 1, 4, 2, 0, 4] * 4
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=16, seed=21, canaries=True)
+    ref = oracle_varlen(orc, wl)
+    outs = {}
+    for order in (vb.ORDER_GRID, vb.ORDER_LONGEST_FIRST):
+        prev = vb.select_work_order(order)
+        try:
+            outs[order], plan, _ = run_varlen(wl, P)
+            ran = vb.last_plan().work_order
+        finally:
+            vb.select_work_order(prev)
+        assert plan.kernel == vb.KERNEL_VARLEN_COLUMNS and ran == order
+        say(f"[columns] single tile P={P} order={order}")
+        assert_parity(outs[order], ref, f"single tile P{P} order {order}")
+    assert np.array_equal(outs[vb.ORDER_GRID], outs[vb.ORDER_LONGEST_FIRST])
