@@ -17,24 +17,23 @@
 // Workgroup = W wave64s per (partition, KV head, sequence) (vllm-metal
 // kernels page, cf-1.com/news/5525226, section "Metal 并行模型": all query
 // heads of the group share one pass over the group's K/V pages).  Each wave
-// takes every W-th step of T tokens (T = 32 for D = 128; T = 16 for D = 256,
-// which keeps a lane under 256 registers).  Per step and lane l (i = l % 16,
-// c = l / 16), shown for T = 32:
-//  * K: two 16-token tiles; lane l loads token i (and 16 + i), dims
-//    [32 kk + 8 c, +8) for kk < D/32: 16-byte loads that are exactly the MFMA
-//    A operand.  The B operand is Q^T: head i, the same dims (zero for
-//    i >= G), held in registers for the whole partition.
-//  * The QK output tile gives lane l head i and tokens 4c + r (r < 4); the two
-//    tiles give 8 tokens per lane.  That is exactly the B operand (P^T) of the
-//    PV product when k-slot j of lane group c is token (j < 4 ? 4c + j :
-//    16 + 4c + j - 4), so P needs no data movement, only fp16 packing.
-//  * V: lane l loads its 8 tokens' dims [128 dh + 8 i, +8) (whole 256-byte
-//    half-rows per 16 lanes) and transposes the 8x8 fp16 block in registers
-//    with v_perm_b32 into the PV A operands: tile (dh, e) holds
-//    d = 128 dh + 8 i + e for row i.
+// takes every W-th step of T = 16 tokens (32-token steps remain a
+// compile-time option, VK_MFMA_T128 / VK_MFMA_T256).  Per step and lane l
+// (i = l % 16, c = l / 16):
+//  * K: lane l holds token i, dims [32 kk + 8 c, +8) for kk < D/32: exactly
+//    the MFMA A operand.  16-bit types load it through the wave's LDS slots
+//    in whole 128-byte lines and read it back in this layout (issue_lds /
+//    read_lds); fp32 loads it directly.  The B operand is Q^T: head i, the
+//    same dims (zero for i >= G), held in registers for the whole partition.
+//  * The QK output tile gives lane l head i and tokens 4c + r (r < 4): that
+//    is exactly the B operand (P^T) of the 16x16x16 PV product, so P needs
+//    no data movement, only packing to the element type.
+//  * V: lane l loads its 4 tokens' dims [128 dh + 8 i, +8) (whole 256-byte
+//    half-rows per 16 lanes) and transposes the 4x8 block in registers with
+//    v_perm_b32 into the PV A operands: tile (dh, e) holds d = 128 dh + 8 i + e.
 //  * Online softmax in log2 space (section "GQA 解码内核的四个提速技巧",
-//    item 1): per head, max over the 32 tokens (in-lane, then across the 4
-//    lane groups), one rescale of the accumulators per step, exp2 of
+//    item 1): per head, max over the step's tokens (in-lane, then across the
+//    4 lane groups), one rescale of the accumulators per step, exp2 of
 //    x - max, per-lane partial exp-sums (summed once at the end).
 // Page ids: each wave holds up to 64 page ids of the current chunk in one
 // register (lane k = page k, one coalesced load) and reads the step's 1-4 ids
