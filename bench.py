@@ -404,7 +404,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print(f"bench.py: this path runs on one GPU only (asked for {max(args.gpus, world)}); "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+              "the library has no multi-GPU path",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
