@@ -446,6 +446,9 @@ def main():
         wl = make_varlen(args.workload, dtype=args.dtype)
         return bench_varlen(args, wl, time.time() - t0)
     else:
+        if args.dtype != "f16":
+            raise SystemExit("bench.py: the named decode workloads are fp16; "
+                             "use --shape S,Hq,Hkv,D,bs,lo,hi with --dtype bf16 or f32")
         wl = make_workload(args.workload)
     gen_s = time.time() - t0
     P_req = args.partition if args.partition is not None else wl.partition_sizes[0]
