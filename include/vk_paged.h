@@ -278,7 +278,8 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
  * tokens (0 <= q_len <= seq_len).  The kernel follows vk_select_varlen_kernel
  * and is reported in plan_out->kernel.  A tile holds T query tokens of one KV
  * head's G heads and runs on w waves: T = 16 / G, w = 1 for
- * VK_KERNEL_VARLEN_COLUMNS; T = 128 / G, w = 4 for VK_KERNEL_VARLEN_TILES.
+ * VK_KERNEL_VARLEN_COLUMNS; T = 128 / G, w = 4 at head_dim 128 and 8 at
+ * head_dim 256 for VK_KERNEL_VARLEN_TILES.
  * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
  * call is unsplit when the tiles alone give one wave per wave slot
  * (w * n >= 8 * cu_count), otherwise split at 512 when
