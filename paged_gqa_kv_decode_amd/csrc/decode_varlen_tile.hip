@@ -6,8 +6,8 @@
 // in decode_varlen.hip and of the decode).
 //
 // The column kernel gives each wave 16 (token, head) columns and streams the
-// keys through registers, so every 16 / G query tokens re-read the whole
-// context.  Here a workgroup of four waves owns 128 columns (BQ = 128 / G
+// keys through that wave's own prefetch slots, so every 16 / G query tokens
+// re-read the whole context.  Here a workgroup of four waves owns 128 columns (BQ = 128 / G
 // query tokens x G heads) and streams the keys through LDS in 32-key tiles:
 // each tile is fetched once per workgroup and serves all 128 columns.
 //
