@@ -1,5 +1,6 @@
 """GPU parity of the LDS-tiled multi-token kernel (VK_KERNEL_VARLEN_TILES:
-four waves per 128 (token, head) columns, K/V tiles shared through LDS)
+128 (token, head) columns per workgroup on four waves at D = 128 and eight
+at D = 256, K/V tiles shared through LDS)
 against the float64 oracle.
 
 Same tolerance as the decode: max |gpu - ref| <= 2e-3 and per-row relative
