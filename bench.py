@@ -95,15 +95,20 @@ def _bench_lib():
     L = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.vkb_stream_read.argtypes = [vp, i64, vp, i32, vp]
+    L.vkb_stream_read_nt.argtypes = [vp, i64, vp, i32, vp]
     L.vkb_page_read.argtypes = [vp, i64, vp, i64, i32, i64, vp, vp]
+    L.vkb_page_read_nt.argtypes = [vp, i64, vp, i64, i32, i64, vp, vp]
     L.vkb_fill.argtypes = [vp, i64, ctypes.c_uint32, vp]
     return L
 
 
 def ceilings(wl, dev, P, reps=10):
-    """Read-bandwidth ceilings of this machine for the workload's KV pools:
-    a streaming read of both pools, the exact page list of the decode
-    (partition-major, P/bs pages per workgroup), and the same pages sorted."""
+    """Read-bandwidth ceilings of this machine for the workload's KV pools: a
+    streaming read of both pools (16-byte loads, 8192 workgroups of 256
+    threads, 8 loads in flight per thread), with plain and with nontemporal
+    loads; the exact page list of the decode (partition-major, P/bs pages per
+    workgroup), in order and sorted, plain and nontemporal.  Each timed run
+    follows a 512 MiB read, so nothing is served from the caches."""
     import numpy as np
     import torch
     L = _bench_lib()
@@ -111,7 +116,7 @@ def ceilings(wl, dev, P, reps=10):
     st = torch.cuda.current_stream()
     h = st.cuda_stream
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    blocks = 256 * 16
+    blocks = 8192
     sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     bs, D, Hkv = wl.block_size, wl.head_dim, wl.num_kv_heads
     page_bytes = bs * D * 2
@@ -143,24 +148,31 @@ def ceilings(wl, dev, P, reps=10):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return float(np.median(ts))
 
-    pool_bytes = k.numel() * 2
-    t_stream = timed(lambda: (L.vkb_stream_read(k.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h),
-                              L.vkb_stream_read(v.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h)))
+    pool_bytes = k.numel() * k.element_size()
+
+    def stream(fn):
+        return timed(lambda: (fn(k.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h),
+                              fn(v.data_ptr(), pool_bytes, sink.data_ptr(), blocks, h)))
+
+    t_plain, t_nt = stream(L.vkb_stream_read), stream(L.vkb_stream_read_nt)
     page_total = 2 * len(ids) * page_bytes
 
-    def pages(idt):
-        L.vkb_page_read(k.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg, page_bytes,
-                        psink.data_ptr(), h)
-        L.vkb_page_read(v.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg, page_bytes,
-                        psink.data_ptr(), h)
+    def pages(fn, idt):
+        return timed(lambda: (fn(k.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg,
+                                 page_bytes, psink.data_ptr(), h),
+                              fn(v.data_ptr(), pool_pages, idt.data_ptr(), len(ids), ppg,
+                                 page_bytes, psink.data_ptr(), h)))
 
-    t_pages = timed(lambda: pages(ids_dev))
-    t_sorted = timed(lambda: pages(ids_sorted))
-    return {"stream_read_GBps": round(2 * pool_bytes / t_stream / 1e9, 1),
-            "page_read_GBps": round(page_total / t_pages / 1e9, 1),
-            "page_read_sorted_GBps": round(page_total / t_sorted / 1e9, 1),
-            "page_bytes": page_bytes, "pages_per_group": ppg,
-            "flushed": "512 MiB read before each timed run"}
+    gbs = {"stream_read_plain_GBps": 2 * pool_bytes / t_plain / 1e9,
+           "stream_read_nt_GBps": 2 * pool_bytes / t_nt / 1e9,
+           "page_read_GBps": page_total / pages(L.vkb_page_read, ids_dev) / 1e9,
+           "page_read_nt_GBps": page_total / pages(L.vkb_page_read_nt, ids_dev) / 1e9,
+           "page_read_sorted_GBps": page_total / pages(L.vkb_page_read, ids_sorted) / 1e9}
+    out = {k_: round(v_, 1) for k_, v_ in gbs.items()}
+    out["stream_read_GBps"] = max(out["stream_read_plain_GBps"], out["stream_read_nt_GBps"])
+    out.update({"page_bytes": page_bytes, "pages_per_group": ppg, "stream_blocks": blocks,
+                "flushed": "512 MiB read before each timed run"})
+    return out
 
 
 def cpu_model() -> str:
@@ -176,38 +188,37 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(wl, min_seconds: float = 10.0, max_seconds: float = 30.0):
-    """Time the float64 oracle, as it stands, on a bounded sample of the
-    workload: whole sequences, taken in order and cycling over the batch,
-    until at least `min_seconds` of wall time (a sequence is not started when
-    the estimate says it would end past `max_seconds`)."""
+    """Time the float64 oracle, as it stands, on whole steps of the workload
+    (every sequence and query head in one call, threaded over the (sequence,
+    head) rows): one warm-up step, then at least 3 timed steps, more while
+    the timed total stays under `min_seconds`; a step that alone takes longer
+    than `max_seconds` is timed once.  Reported: the median step."""
     import numpy as np
     import oracle
     from paged_gqa_kv_decode_amd.workloads import kv_read_bytes
     nthreads = oracle.default_threads()
-    done_tokens, done_bytes, runs, total = 0, 0, 0, 0.0
-    per_token = None
-    while total < min_seconds:
-        s = runs % wl.num_seqs
-        L = int(wl.seq_lens[s])
-        if per_token is not None and total + per_token * L > max_seconds:
-            break
+    dtype = wl.meta.get("dtype", "f16")
+
+    def step():
         t = time.perf_counter()
-        oracle.paged_attention_arrays(wl.q[s:s + 1], wl.k_cache, wl.v_cache,
-                                      wl.block_tables[s:s + 1], wl.seq_lens[s:s + 1], wl.scale,
-                                      nthreads=nthreads, dtype=wl.meta.get("dtype", "f16"))
-        dt = time.perf_counter() - t
-        total += dt
-        runs += 1
-        done_tokens += L
-        done_bytes += kv_read_bytes(wl.seq_lens[s:s + 1], wl.num_kv_heads, wl.head_dim,
-                                    4 if wl.meta.get("dtype") == "f32" else 2)
-        per_token = total / max(done_tokens, 1)
-    return {"value": round(done_bytes / total / 1e9, 4), "unit": "GB/s (KV-read)",
+        oracle.paged_attention_arrays(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.seq_lens,
+                                      wl.scale, nthreads=nthreads, dtype=dtype)
+        return time.perf_counter() - t
+
+    first = step()
+    ts = [first] if first > max_seconds else []
+    while not ts or (len(ts) < 3 or sum(ts) < min_seconds) and sum(ts) + first <= max_seconds:
+        ts.append(step())
+    med = float(np.median(ts))
+    kv = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim, 4 if dtype == "f32" else 2)
+    return {"value": round(kv / med / 1e9, 4), "unit": "GB/s (KV-read)",
             "cores": nthreads, "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": f"{runs} single-sequence oracle calls cycling over the {wl.num_seqs} "
-                      f"sequences ({done_tokens} tokens, all {wl.num_q_heads} q heads), "
-                      f"{total:.2f} s wall",
-            "seconds": round(total, 3)}
+            "ms_per_step": round(med * 1e3, 1),
+            "sample": f"whole steps ({wl.num_seqs} sequences, {int(wl.seq_lens.sum())} tokens, "
+                      f"all {wl.num_q_heads} q heads): median of {len(ts)} after "
+                      f"{'none' if first > max_seconds else 'one'} warm-up, "
+                      f"{sum(ts) + (0 if first > max_seconds else first):.2f} s wall in all",
+            "seconds": round(sum(ts), 3)}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
@@ -358,6 +369,189 @@ def bench_varlen(args, wl, gen_s):
     print(json.dumps(result), flush=True)
 
 
+ORDER_NAMES = {1: "grid", 2: "longest_first"}
+
+
+class DecodeBench:
+    """One decode workload on the device: inputs, rotated K/V pool copies,
+    scratch, and the step (host plan + decode + reduce, or the single launch)
+    timed with HIP events on the launch stream."""
+
+    def __init__(self, wl, P_req, max_copies, fused=False, append=False):
+        import numpy as np
+        import torch
+        from paged_gqa_kv_decode_amd import binding as vb
+        from paged_gqa_kv_decode_amd.workloads import kv_read_bytes
+        self.wl, self.P_req, self.fused, self.append = wl, P_req, fused, append
+        self.dev = vb.device_inputs(wl)
+        q, k, v, bt, sl = self.dev
+        self.dtype_code = {"f16": vb.DTYPE_F16, "bf16": vb.DTYPE_BF16,
+                           "f32": vb.DTYPE_F32}[wl.meta.get("dtype", "f16")]
+        self.kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim,
+                                      4 if self.dtype_code == vb.DTYPE_F32 else 2)
+        # Successive steps rotate over identical copies of the K/V pools so
+        # that at least 4x the 256 MB Infinity Cache is read between two reads
+        # of the same page: every step streams its KV from HBM, as a layer's
+        # decode does when the other layers' caches are read in between.
+        self.ncopies = max(2, min(max_copies, -(-(4 * MALL_BYTES) // self.kv_bytes)))
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(self.ncopies - 1)]
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        self.out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
+                               device="cuda")
+        # Scratch sized once from a first plan; every step plans again (host)
+        # and reuses it (the plan depends only on the host seq_lens).
+        self.step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=self.out,
+                                   fused=fused, dtype=self.dtype_code)
+        self.P, self.NP = self.step0.plan.partition_size, self.step0.plan.max_num_partitions
+        self.counter = 0
+        if append:
+            # the K/V rows at slot L-1 of the workload and their positions
+            self.last = torch.from_numpy((wl.seq_lens - 1).astype(np.int32)).cuda()
+            blk = wl.block_tables[np.arange(wl.num_seqs), (wl.seq_lens - 1) // wl.block_size]
+            slot = (wl.seq_lens - 1) % wl.block_size
+            self.k_new = torch.from_numpy(np.ascontiguousarray(wl.k_cache[blk, :, slot, :])).cuda()
+            self.v_new = torch.from_numpy(np.ascontiguousarray(wl.v_cache[blk, :, slot, :])).cuda()
+
+    def one_step(self, ev=None, stream=None):
+        from paged_gqa_kv_decode_amd import binding as vb
+        wl, P, NP, st0, out = self.wl, self.P, self.NP, self.step0, self.out
+        stream = stream if stream is not None else self.stream
+        q, _, _, bt, sl = self.dev
+        k, v = self.pools[self.counter % self.ncopies]
+        self.counter += 1
+        if self.append:
+            if ev is not None:
+                ev[3].record(stream)
+            vb.paged_kv_append(self.k_new, self.v_new, bt, self.last, k, v, 10000.0, stream)
+        plan = vb.plan_partitions(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                  wl.block_size, wl.max_blocks_per_seq, self.P_req, 0)
+        assert plan.partition_size == P and plan.max_num_partitions == NP
+        if ev is not None:
+            ev[0].record(stream)
+        if self.fused:
+            vb.paged_gqa_decode_fused(q, k, v, bt, sl, wl.scale, P, NP, out, st0.max_logits,
+                                      st0.exp_sums, st0.tmp_out, st0.counters, stream)
+            if ev is not None:
+                ev[1].record(stream)
+        elif self.dtype_code != vb.DTYPE_F16:
+            vb.paged_gqa_decode_dt(self.dtype_code, q, k, v, bt, sl, wl.scale, P, NP,
+                                   None if P else out, st0.max_logits, st0.exp_sums,
+                                   st0.tmp_out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            if P:
+                vb.paged_gqa_reduce(st0.max_logits, st0.exp_sums, st0.tmp_out, sl, P, out, stream)
+        elif P:
+            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, P, NP, None, st0.max_logits,
+                                st0.exp_sums, st0.tmp_out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            vb.paged_gqa_reduce(st0.max_logits, st0.exp_sums, st0.tmp_out, sl, P, out, stream)
+        else:
+            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, 0, 1, out, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def time(self, steps, warmup):
+        """W untimed steps, then K steps between two device synchronisations;
+        per-launch durations from HIP events recorded on the launch stream."""
+        import numpy as np
+        import torch
+        from paged_gqa_kv_decode_amd import binding as vb
+        for _ in range(warmup):
+            self.one_step()
+        torch.cuda.synchronize()
+        kernel_ran, order_ran = vb.last_plan().kernel, vb.last_plan().work_order
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(steps):
+            self.one_step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t
+        dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+        red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+        r = {"ms_per_step": wall * 1e3 / steps, "kernel": kernel_ran, "order": order_ran,
+             "achieved_GBps": self.kv_bytes / (float(dec_ms.mean()) * 1e-3) / 1e9,
+             "kernel_us": {"decode_mean": round(float(dec_ms.mean()) * 1e3, 2),
+                           "decode_median": round(float(np.median(dec_ms)) * 1e3, 2),
+                           "decode_p5": round(float(np.percentile(dec_ms, 5)) * 1e3, 2),
+                           "decode_p95": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
+                           "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)}}
+        if self.append:
+            app_ms = np.array([e[3].elapsed_time(e[0]) for e in events])
+            r["append_us_median"] = round(float(np.median(app_ms)) * 1e3, 2)
+        return r
+
+    def time_graph(self, steps):
+        """The step replayed from a captured HIP graph (one step per pool copy,
+        captured back to back), µs per step."""
+        import torch
+        cap = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(self.ncopies):
+                self.one_step(stream=cap)
+        reps = max(1, -(-steps // self.ncopies))
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t) * 1e6 / (reps * self.ncopies), 2)
+
+    def time_flushed(self):
+        """Median decode duration with a 512 MiB read before each step."""
+        import numpy as np
+        import torch
+        L = _bench_lib()
+        flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+        fsink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+        fl = []
+        for _ in range(20):
+            L.vkb_stream_read(flush.data_ptr(), flush.numel(), fsink.data_ptr(), 4096,
+                              self.stream.cuda_stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            self.one_step(ev)
+            torch.cuda.synchronize()
+            fl.append(ev[0].elapsed_time(ev[1]))
+        return round(float(np.median(fl)) * 1e3, 2)
+
+    def release(self):
+        import torch
+        torch.cuda.synchronize()
+        self.pools = None
+        self.step0 = None
+        self.out = None
+        torch.cuda.empty_cache()
+
+
+def cpu_single_thread():
+    """The float64 oracle on one thread for the two small decode workloads
+    (one sequence of 64 tokens; 8 sequences of up to 2048): median of 3 whole
+    steps after one warm-up, ms."""
+    import numpy as np
+    import oracle
+    from paged_gqa_kv_decode_amd.workloads import make_workload
+    res = {}
+    for name in ("tiny_1x64", "batch8_2k"):
+        wl = make_workload(name)
+        ts = []
+        for _ in range(4):
+            t = time.perf_counter()
+            oracle.paged_attention_arrays(wl.q, wl.k_cache, wl.v_cache, wl.block_tables,
+                                          wl.seq_lens, wl.scale, nthreads=1)
+            ts.append(time.perf_counter() - t)
+        res[name] = round(float(np.median(ts[1:])) * 1e3, 3)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,8 +586,11 @@ def main():
                          "(vk_paged_gqa_decode_fused) instead of decode + reduce")
     ap.add_argument("--max-copies", type=int, default=256,
                     help="cap on the rotated K/V pool copies")
-    ap.add_argument("--ceiling", action="store_true",
-                    help="also measure the box's read-bandwidth ceilings on the KV pools")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the box's read-bandwidth ceilings on the KV pools")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload: skip timing the other long-context workloads "
+                         "(long32_16k at P=256 and 512, mixed64_32k at 512)")
     ap.add_argument("--flush", action="store_true",
                     help="also time the decode with a 512 MiB cache flush before each run")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -459,109 +656,20 @@ def main():
     vb.select_work_order({"auto": vb.ORDER_AUTO, "grid": vb.ORDER_GRID,
                           "longest": vb.ORDER_LONGEST_FIRST}[args.order])
 
-    dev = vb.device_inputs(wl)
-    q, k, v, bt, sl = dev
-    dtype_code = {"f16": vb.DTYPE_F16, "bf16": vb.DTYPE_BF16,
-                  "f32": vb.DTYPE_F32}[wl.meta.get("dtype", "f16")]
-    kv_bytes = kv_read_bytes(wl.seq_lens, wl.num_kv_heads, wl.head_dim,
-                             4 if dtype_code == vb.DTYPE_F32 else 2)
-    # Successive steps rotate over identical copies of the K/V pools so that at
-    # least 4x the 256 MB Infinity Cache is read between two reads of the same
-    # page: every step streams its KV from HBM, as a layer's decode does when
-    # the other layers' caches are read in between.
-    ncopies = max(2, min(args.max_copies, -(-(4 * MALL_BYTES) // kv_bytes)))
-    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(ncopies - 1)]
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
-
-    # Scratch sized once from a first plan; every step plans again (host) and
-    # reuses it (the plan depends only on the host seq_lens).
-    step0 = vb.DecodeStep(q, k, v, bt, sl, wl.seq_lens, wl.scale, P_req, out=out,
-                          fused=args.fused, dtype=dtype_code)
-    P, NP = step0.plan.partition_size, step0.plan.max_num_partitions
-
-    counter = [0]
-    if args.append:
-        # the K/V rows at slot L-1 of the workload and their positions
-        last = torch.from_numpy((wl.seq_lens - 1).astype(np.int32)).cuda()
-        blk = wl.block_tables[np.arange(wl.num_seqs), (wl.seq_lens - 1) // wl.block_size]
-        slot = (wl.seq_lens - 1) % wl.block_size
-        k_new = torch.from_numpy(np.ascontiguousarray(wl.k_cache[blk, :, slot, :])).cuda()
-        v_new = torch.from_numpy(np.ascontiguousarray(wl.v_cache[blk, :, slot, :])).cuda()
-
-    def one_step(ev=None, stream=stream):
-        k, v = pools[counter[0] % ncopies]
-        counter[0] += 1
-        if args.append:
-            if ev is not None:
-                ev[3].record(stream)
-            vb.paged_kv_append(k_new, v_new, bt, last, k, v, 10000.0, stream)
-        plan = vb.plan_partitions(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                  wl.block_size, wl.max_blocks_per_seq, P_req, 0)
-        assert plan.partition_size == P and plan.max_num_partitions == NP
-        if ev is not None:
-            ev[0].record(stream)
-        if args.fused:
-            vb.paged_gqa_decode_fused(q, k, v, bt, sl, wl.scale, P, NP, out, step0.max_logits,
-                                      step0.exp_sums, step0.tmp_out, step0.counters, stream)
-            if ev is not None:
-                ev[1].record(stream)
-        elif dtype_code != vb.DTYPE_F16:
-            vb.paged_gqa_decode_dt(dtype_code, q, k, v, bt, sl, wl.scale, P, NP,
-                                   None if P else out, step0.max_logits, step0.exp_sums,
-                                   step0.tmp_out, stream)
-            if ev is not None:
-                ev[1].record(stream)
-            if P:
-                vb.paged_gqa_reduce(step0.max_logits, step0.exp_sums, step0.tmp_out, sl, P, out,
-                                    stream)
-        elif P:
-            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, P, NP, None, step0.max_logits,
-                                step0.exp_sums, step0.tmp_out, stream)
-            if ev is not None:
-                ev[1].record(stream)
-            vb.paged_gqa_reduce(step0.max_logits, step0.exp_sums, step0.tmp_out, sl, P, out,
-                                stream)
-        else:
-            vb.paged_gqa_decode(q, k, v, bt, sl, wl.scale, 0, 1, out, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
-    kernel_ran = vb.last_plan().kernel
-    order_ran = vb.last_plan().work_order
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for i in range(args.steps):
-        one_step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t
-
-    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    app_ms = np.array([e[3].elapsed_time(e[0]) for e in events]) if args.append else None
-    ms_per_step = wall * 1e3 / args.steps
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_mean_s = float(dec_ms.mean()) * 1e-3
-    achieved = kv_bytes / dec_mean_s / 1e9
-    traffic = load_traffic(args.workload, P, kernel_ran, args.fused)
+    db = DecodeBench(wl, P_req, args.max_copies, fused=args.fused, append=args.append)
+    tm = db.time(args.steps, args.warmup)
+    P, NP, kv_bytes, ncopies = db.P, db.NP, db.kv_bytes, db.ncopies
+    traffic = load_traffic(args.workload, P, tm["kernel"], args.fused)
 
     result = {
         "metric": "decode-attention µs/step and KV-read HBM GB/s (% of MI355X peak)",
-        "value": round(value, 2),
+        "value": round(kv_bytes / (tm["ms_per_step"] * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
+        "ms_per_step": round(tm["ms_per_step"], 5),
+        "us_per_step": round(tm["ms_per_step"] * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -572,57 +680,59 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "sum_seq_len": int(wl.seq_lens.sum()),
                    "partition_size": P, "max_num_partitions": NP,
-                   "decode_kernel": KERNEL_NAMES.get(kernel_ran, str(kernel_ran)),
-                   "work_order": {1: "grid", 2: "longest_first"}.get(order_ran, str(order_ran)),
+                   "decode_kernel": KERNEL_NAMES.get(tm["kernel"], str(tm["kernel"])),
+                   "work_order": ORDER_NAMES.get(tm["order"], str(tm["order"])),
                    "single_launch": bool(args.fused), "with_append": bool(args.append)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "kernel_us": {"decode_mean": round(float(dec_ms.mean()) * 1e3, 2),
-                      "decode_median": round(float(np.median(dec_ms)) * 1e3, 2),
-                      "decode_p5": round(float(np.percentile(dec_ms, 5)) * 1e3, 2),
-                      "decode_p95": round(float(np.percentile(dec_ms, 95)) * 1e3, 2),
-                      "reduce_median": round(float(np.median(red_ms)) * 1e3, 2)},
-        **({"append_us_median": round(float(np.median(app_ms)) * 1e3, 2)} if args.append else {}),
+        "roofline": {"bound": "hbm", "achieved": round(tm["achieved_GBps"], 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(tm["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "traffic_source": (None if traffic is None else
+                           f"stored: profiles/decode_{args.workload}_P{P}"
+                           f"{'_fused' if args.fused else ''}_traffic.txt (rocprofv3 FETCH_SIZE + "
+                           "WRITE_SIZE per launch, calibrated; used only while the kernel "
+                           "sources hash to the value recorded there)"),
+        "kernel_us": tm["kernel_us"],
+        **({"append_us_median": tm["append_us_median"]} if args.append else {}),
         "kv_read_bytes": kv_bytes,
         "kv_pool_copies": ncopies,
         "bytes_read_between_reuse": (ncopies - 1) * kv_bytes,
         "input_gen_s": round(gen_s, 1),
     }
     if args.graph:
-        # One step per pool copy captured back to back; replayed until K steps.
-        cap = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=cap):
-            for _ in range(ncopies):
-                one_step(stream=cap)
-        reps = max(1, -(-args.steps // ncopies))
-        for _ in range(2):
-            graph.replay()
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        result["us_per_step_graph"] = round((time.perf_counter() - t) * 1e6 / (reps * ncopies), 2)
-    if args.ceiling:
-        result["ceiling"] = ceilings(wl, dev, P)
+        result["us_per_step_graph"] = db.time_graph(args.steps)
     if args.flush:
-        L = _bench_lib()
-        flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-        fsink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
-        fl = []
-        for _ in range(20):
-            L.vkb_stream_read(flush.data_ptr(), flush.numel(), fsink.data_ptr(), 4096,
-                              stream.cuda_stream)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            one_step(ev)
-            torch.cuda.synchronize()
-            fl.append(ev[0].elapsed_time(ev[1]))
-        result["kernel_us"]["decode_median_flushed"] = round(float(np.median(fl)) * 1e3, 2)
+        result["kernel_us"]["decode_median_flushed"] = db.time_flushed()
+    if not args.no_ceiling:
+        result["ceiling"] = ceilings(wl, db.dev, P)
+    db.release()
+    if (not args.no_configs and not args.shape and not args.fused and not args.append
+            and args.workload == "long4_128k" and args.partition is None):
+        # The other long-context workloads, timed the same way in this run.
+        configs = {}
+        for name, p_req in (("long32_16k", 256), ("long32_16k", 512), ("mixed64_32k", 512)):
+            wl2 = make_workload(name)
+            db2 = DecodeBench(wl2, p_req, args.max_copies)
+            t2 = db2.time(args.steps, args.warmup)
+            configs[f"{name}_P{p_req}"] = {
+                "partition_size": db2.P, "kv_read_bytes": db2.kv_bytes,
+                "decode_us_mean": t2["kernel_us"]["decode_mean"],
+                "decode_us_median": t2["kernel_us"]["decode_median"],
+                "reduce_us_median": t2["kernel_us"]["reduce_median"],
+                "us_per_step": round(t2["ms_per_step"] * 1e3, 2),
+                "kv_TBps": round(t2["achieved_GBps"] / 1e3, 3),
+                "frac": round(t2["achieved_GBps"] / HBM_PEAK_GBS, 4),
+                "decode_kernel": KERNEL_NAMES.get(t2["kernel"], str(t2["kernel"])),
+                "work_order": ORDER_NAMES.get(t2["order"], str(t2["order"]))}
+            db2.release()
+            del wl2
+            print(f"bench: {name} P={p_req}: decode {t2['kernel_us']['decode_mean']} us "
+                  f"({configs[f'{name}_P{p_req}']['frac']:.3f} of peak)", file=sys.stderr,
+                  flush=True)
+        result["configs"] = configs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, 3 * args.cpu_seconds)
+        if args.workload == "long4_128k" and not args.shape:
+            result["cpu_baseline"]["single_thread_ms"] = cpu_single_thread()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -256,9 +256,11 @@ vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums,
  *   directly and leaves its scratch rows untouched.  L <= 0 writes zeros.
  * The merge is done by one workgroup per (s, KV head), so the form suits few
  * partitions per sequence (short and medium contexts, where the second
- * launch is a large share of the step); for very long contexts the separate
- * reduce spreads the merge over more workgroups.  Always runs the matrix-core
- * family (VK_KERNEL_DOT selects the automatic choice here).  Errors and
+ * launch is a large share of the step).  With max_num_partitions > 8 the
+ * call enqueues vk_paged_gqa_decode and vk_paged_gqa_reduce instead (two
+ * launches, the same partials and the same output; counters untouched), since
+ * the separate reduce spreads the merge over more workgroups.  Always runs
+ * the matrix-core family (VK_KERNEL_DOT selects the automatic choice here).  Errors and
  * device-side guards are those of vk_paged_gqa_decode; additionally
  * VK_ERR_NULL_ARG if out is NULL, or counters is NULL with partition_size > 0.
  */
@@ -394,14 +396,18 @@ vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t
 
 /*
  * vk_select_decode_kernel — A/B switch for this thread's later decode calls
- * (the pages describe an equivalent switch back to a former path for A/B
- * comparison).  VK_KERNEL_AUTO picks the fastest family for the geometry.
- * Returns the previous setting, or -1 for an unknown value (setting kept).
+ * (vllm-metal kernels page, cf-1.com/news/5525226, section "上手实践：如何验证
+ * 内核生效": an environment switch sends eligible requests back to the
+ * classic path so the two can be compared; here the switch is a call, per
+ * thread, and selects a kernel family or a wave count).  VK_KERNEL_AUTO
+ * picks the fastest family for the geometry.  Returns the previous setting,
+ * or -1 for an unknown value (setting kept).
  */
 int32_t vk_select_decode_kernel(int32_t kernel);
 
 /*
- * vk_select_work_order — A/B switch for the order in which this thread's
+ * vk_select_work_order — A/B switch (as vk_select_decode_kernel: vllm-metal
+ * kernels page, section "上手实践：如何验证内核生效") for the order in which this thread's
  * later matrix-core decode launches hand out their (partition, KV head,
  * sequence) items.  Longest first applies only to split launches over at most
  * 64 sequences (others run in grid order whatever the setting), and to the
@@ -414,7 +420,8 @@ int32_t vk_select_decode_kernel(int32_t kernel);
 int32_t vk_select_work_order(int32_t order);
 
 /*
- * vk_select_varlen_kernel — A/B switch for this thread's later
+ * vk_select_varlen_kernel — A/B switch (as vk_select_decode_kernel: vllm-metal
+ * kernels page, section "上手实践：如何验证内核生效") for this thread's later
  * vk_plan_varlen and vk_paged_gqa_varlen calls: VK_KERNEL_AUTO (columns
  * when the longest query run of the batch fits one 16-column tile, i.e. is
  * at most 16 / G tokens for G = Hq / Hkv, so every K/V step is read once;
@@ -433,9 +440,15 @@ const char* vk_status_string(vk_status s);
 /* HIP error code of this thread's last VK_ERR_HIP (0 if none). */
 int32_t vk_last_hip_error(void);
 
-/* This thread's last plan: from vk_plan_partitions, or the launch shape of
- * the last vk_paged_gqa_decode (mirrors the pages' "last dispatch"
- * diagnostics).  Returns VK_ERR_NULL_ARG if out is NULL. */
+/* This thread's last plan: from vk_plan_partitions or vk_plan_varlen, or
+ * the launch shape of the last decode or multi-token launch (vllm-metal
+ * kernels page, section "上手实践：如何验证内核生效": after a request the
+ * runtime reports which path the last dispatch took and the partition size,
+ * 256 or 512, it actually ran; here partition_size, kernel, grid, block and
+ * work_order).  Copied into *out, a caller-owned host struct; returns
+ * VK_ERR_NULL_ARG if out is NULL (the status return keeps every call of this
+ * ABI on one error convention).  Before any plan or launch on this thread,
+ * *out is all zero. */
 vk_status vk_last_plan(vk_plan* out);
 
 #ifdef __cplusplus

@@ -17,8 +17,7 @@
 // Workgroup = W wave64s per (partition, KV head, sequence) (vllm-metal
 // kernels page, cf-1.com/news/5525226, section "Metal 并行模型": all query
 // heads of the group share one pass over the group's K/V pages).  Each wave
-// takes every W-th step of T = 16 tokens (32-token steps remain a
-// compile-time option, VK_MFMA_T128 / VK_MFMA_T256).  Per step and lane l
+// takes every W-th step of T = 16 tokens.  Per step and lane l
 // (i = l % 16, c = l / 16):
 //  * K: lane l holds token i, dims [32 kk + 8 c, +8) for kk < D/32: exactly
 //    the MFMA A operand.  16-bit types load it through the wave's LDS slots
@@ -27,7 +26,10 @@
 //    same dims (zero for i >= G), held in registers for the whole partition.
 //  * The QK output tile gives lane l head i and tokens 4c + r (r < 4): that
 //    is exactly the B operand (P^T) of the 16x16x16 PV product, so P needs
-//    no data movement, only packing to the element type.
+//    no data movement, only packing to the element type.  16-bit types take
+//    each weight as a rounded value plus its rounded residual (two PV
+//    products), so the weights keep ~2^-22 (fp16) or ~2^-16 (bf16) relative
+//    precision instead of the operand format's 2^-11 or 2^-8.
 //  * V: lane l loads its 4 tokens' dims [128 dh + 8 i, +8) (whole 256-byte
 //    half-rows per 16 lanes) and transposes the 4x8 block in registers with
 //    v_perm_b32 into the PV A operands: tile (dh, e) holds d = 128 dh + 8 i + e.
@@ -48,12 +50,6 @@
 #include "vk_kernels.h"
 
 // Compile-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef VK_MFMA_T128
-#define VK_MFMA_T128 16          // tokens per wave step, D = 128
-#endif
-#ifndef VK_MFMA_T256
-#define VK_MFMA_T256 16          // tokens per wave step, D = 256
-#endif
 #ifndef VK_MFMA_WAVES_PER_EU
 #define VK_MFMA_WAVES_PER_EU 2   // minimum resident waves per SIMD
 #endif
@@ -80,8 +76,7 @@ using namespace mfma;
 // then holds dims 16t + 4c + r.
 template <int D, int G, int BS, int W, int WP, int T, bool FUSED, int DT = 0>
 struct MfmaKernel {
-    static_assert(T == 16 || T == 32, "16 or 32 tokens per wave step");
-    static_assert(DT == 0 || T == 16, "bf16 and fp32 run 16-token steps");
+    static_assert(T == 16, "16 tokens per wave step");
     // WP waves share one partition; a workgroup covers PPW = W / WP
     // consecutive partitions (split launches only, not the single launch).
     static constexpr int PPW = W / WP;
@@ -93,6 +88,13 @@ struct MfmaKernel {
     static constexpr int NPT = D / 16;    // PV output tiles (16 dims each)
     static constexpr int CHP = 64;        // page ids per chunk (one per lane)
     static constexpr int CH = CHP * BS;   // tokens per chunk
+    // fp16 weights are computed as 2^15 * 2^(x - m): the largest is 2^15, so
+    // the residual of each weight's fp16 rounding stays a normal fp16 number
+    // (pack_half2_split).  The exp-sums carry the same factor (a power of
+    // two: exact), the normalised outputs cancel it, and the stored
+    // partials' exp-sums are divided by it.
+    static constexpr float kPScale = DT == 0 ? 32768.f : 1.f;
+    static constexpr float kInvPScale = 1.f / kPScale;
 
     struct State {
         floatx4 acc[NPT];
@@ -294,23 +296,14 @@ struct MfmaKernel {
         float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            p[j] = exp2_fast(x[j] - mref);
+            p[j] = exp2_fast(x[j] - mref) * kPScale;
             ps += p[j];
         }
         st.l = st.l * alpha + ps;
         st.m = mnew;
 #pragma unroll
         for (int t = 0; t < NPT; ++t) st.acc[t] *= alpha;
-        uint4 pb;
-        if constexpr (T == 32) {
-            pb.x = pack_half2(p[0], p[1]);
-            pb.y = pack_half2(p[2], p[3]);
-            pb.z = pack_half2(p[4], p[5]);
-            pb.w = pack_half2(p[6], p[7]);
-        } else {
-            pb = pack_weights(p[0], p[1], p[2], p[3]);
-        }
-        return pb;
+        return pack_weights(p[0], p[1], p[2], p[3]);
     }
 
     // S = K Q^T product of one 32-dim chunk in the element type.
@@ -321,8 +314,8 @@ struct MfmaKernel {
             return mfma32(a, b, c);
     }
 
-    // Four weights of a 16-token step as the PV B operand: fp16 in .x/.y; for
-    // bf16 the rounded pairs in .x/.y and their residuals in .z/.w.
+    // Four weights of a 16-token step as the PV B operand: for 16-bit types
+    // the rounded pairs in .x/.y and their residuals in .z/.w.
     static __device__ __forceinline__ uint4 pack_weights(float p0, float p1, float p2, float p3) {
         uint4 pb;
         if constexpr (DT == 2) {   // fp32 weights as they are
@@ -332,15 +325,14 @@ struct MfmaKernel {
             pack_bf16_split(p0, p1, pb.x, pb.z);
             pack_bf16_split(p2, p3, pb.y, pb.w);
         } else {
-            pb.x = pack_half2(p0, p1);
-            pb.y = pack_half2(p2, p3);
-            pb.z = pb.w = 0;
+            pack_half2_split(p0, p1, pb.x, pb.z);
+            pack_half2_split(p2, p3, pb.y, pb.w);
         }
         return pb;
     }
 
     // One 16-dim PV output tile of a 16-token step (dims e of the lane
-    // group's 4 tokens); bf16 adds the residual weights' product.
+    // group's 4 tokens): the rounded weights' product, then the residuals'.
     template <int E>
     static __device__ __forceinline__ void pv16(floatx4& acc, const uint4 (&v)[4], const uint4& pb) {
         const uint2 a = vt_operand4<E>(v);
@@ -349,6 +341,7 @@ struct MfmaKernel {
             acc = mfma16_bf16(a, make_uint2(pb.z, pb.w), acc);
         } else {
             acc = mfma16(a, make_uint2(pb.x, pb.y), acc);
+            acc = mfma16(a, make_uint2(pb.z, pb.w), acc);
         }
     }
 
@@ -367,30 +360,16 @@ struct MfmaKernel {
             return;
         }
         const auto& vr = b.vr;
-        if constexpr (T == 32) {
 #pragma unroll
-            for (int dh = 0; dh < NDH; ++dh) {
-                st.acc[dh * 8 + 0] = mfma32(vt_operand<0>(vr[dh]), pb, st.acc[dh * 8 + 0]);
-                st.acc[dh * 8 + 1] = mfma32(vt_operand<1>(vr[dh]), pb, st.acc[dh * 8 + 1]);
-                st.acc[dh * 8 + 2] = mfma32(vt_operand<2>(vr[dh]), pb, st.acc[dh * 8 + 2]);
-                st.acc[dh * 8 + 3] = mfma32(vt_operand<3>(vr[dh]), pb, st.acc[dh * 8 + 3]);
-                st.acc[dh * 8 + 4] = mfma32(vt_operand<4>(vr[dh]), pb, st.acc[dh * 8 + 4]);
-                st.acc[dh * 8 + 5] = mfma32(vt_operand<5>(vr[dh]), pb, st.acc[dh * 8 + 5]);
-                st.acc[dh * 8 + 6] = mfma32(vt_operand<6>(vr[dh]), pb, st.acc[dh * 8 + 6]);
-                st.acc[dh * 8 + 7] = mfma32(vt_operand<7>(vr[dh]), pb, st.acc[dh * 8 + 7]);
-            }
-        } else {
-#pragma unroll
-            for (int dh = 0; dh < NDH; ++dh) {
-                pv16<0>(st.acc[dh * 8 + 0], vr[dh], pb);
-                pv16<1>(st.acc[dh * 8 + 1], vr[dh], pb);
-                pv16<2>(st.acc[dh * 8 + 2], vr[dh], pb);
-                pv16<3>(st.acc[dh * 8 + 3], vr[dh], pb);
-                pv16<4>(st.acc[dh * 8 + 4], vr[dh], pb);
-                pv16<5>(st.acc[dh * 8 + 5], vr[dh], pb);
-                pv16<6>(st.acc[dh * 8 + 6], vr[dh], pb);
-                pv16<7>(st.acc[dh * 8 + 7], vr[dh], pb);
-            }
+        for (int dh = 0; dh < NDH; ++dh) {
+            pv16<0>(st.acc[dh * 8 + 0], vr[dh], pb);
+            pv16<1>(st.acc[dh * 8 + 1], vr[dh], pb);
+            pv16<2>(st.acc[dh * 8 + 2], vr[dh], pb);
+            pv16<3>(st.acc[dh * 8 + 3], vr[dh], pb);
+            pv16<4>(st.acc[dh * 8 + 4], vr[dh], pb);
+            pv16<5>(st.acc[dh * 8 + 5], vr[dh], pb);
+            pv16<6>(st.acc[dh * 8 + 6], vr[dh], pb);
+            pv16<7>(st.acc[dh * 8 + 7], vr[dh], pb);
         }
     }
 
@@ -683,9 +662,12 @@ struct MfmaKernel {
             if (!direct && i < G && c == 0) {
                 const int64_t pr = (row0 + i) * NP + part;
                 store_partial1(a, a.max_logits + pr, st.m);
-                store_partial1(a, a.exp_sums + pr, out_bad ? nanv : lsum);
+                store_partial1(a, a.exp_sums + pr, out_bad ? nanv : lsum * kInvPScale);
             }
         } else if constexpr (W == 1) {
+            // (fp32, or built without the LDS prefetch.)  Plain stores: the
+            // single launch's release needs every partial at device scope.
+            static_assert(!FUSED, "the single launch stages its partials through the prefetch slots");
             const bool out_bad = poison || wave_bad;
             if (i < G) {
                 const int64_t r = row0 + i;
@@ -697,7 +679,7 @@ struct MfmaKernel {
                     dst = a.tmp_out + pr * D;
                     if (c == 0) {
                         store_partial1(a, a.max_logits + pr, st.m);
-                        store_partial1(a, a.exp_sums + pr, out_bad ? __builtin_nanf("") : lsum);
+                        store_partial1(a, a.exp_sums + pr, out_bad ? __builtin_nanf("") : lsum * kInvPScale);
                     }
                 }
 #pragma unroll
@@ -761,7 +743,7 @@ struct MfmaKernel {
                     store_partial(a, a.tmp_out + pr * D + d, o);
                     if (d == 0) {
                         store_partial1(a, a.max_logits + pr, M);
-                        store_partial1(a, a.exp_sums + pr, out_bad ? nanv : den);
+                        store_partial1(a, a.exp_sums + pr, out_bad ? nanv : den * kInvPScale);
                     }
                 }
             }
@@ -923,7 +905,7 @@ template <int D, int G, int BS, int W, int WP, bool FUSED, int DT>
 __global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu((DT == 2 && D == 256) ? 1 : VK_MFMA_WAVES_PER_EU)))
 void decode_mfma_kernel(DecodeArgs a) {
-    MfmaKernel<D, G, BS, W, WP, (D == 256 ? VK_MFMA_T256 : VK_MFMA_T128), FUSED, DT>::run(a);
+    MfmaKernel<D, G, BS, W, WP, 16, FUSED, DT>::run(a);
 }
 
 template <int D, int G, int W, int WP, bool FUSED, int DT>

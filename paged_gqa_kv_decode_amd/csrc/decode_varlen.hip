@@ -82,7 +82,7 @@ struct VarlenKernel {
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = exp2_fast(x[r] - mref);
+            p[r] = exp2_fast(x[r] - mref) * M::kPScale;
             ps += p[r];
         }
         st.l = st.l * alpha + ps;
@@ -224,7 +224,7 @@ struct VarlenKernel {
             if (P > 0 && me.mode == 2) {
                 const int64_t pr = me.row * NP + part;
                 M::store_partial1(a, a.max_logits + pr, st.m);
-                M::store_partial1(a, a.exp_sums + pr, me.cbad ? __builtin_nanf("") : lsum);
+                M::store_partial1(a, a.exp_sums + pr, me.cbad ? __builtin_nanf("") : lsum * M::kInvPScale);
             }
         }
         __syncthreads();

@@ -39,6 +39,9 @@
 #ifndef VK_TILE_D256_ONE_BLOCK
 #define VK_TILE_D256_ONE_BLOCK 1   // D = 256: eight waves of one column block
 #endif
+#ifndef VK_TILE_SPLIT_WEIGHTS
+#define VK_TILE_SPLIT_WEIGHTS 1    // fp16: weights as value + residual (two PV products)
+#endif
 
 namespace vk {
 namespace {
@@ -88,6 +91,13 @@ struct TileKernel {
     // by more than kTau, so after the first tiles of a row the rescale is
     // skipped; the weights stay <= 2^kTau, well inside fp16.
     static constexpr float kTau = 8.f;
+    // fp16 with split weights: each weight is 2^7 * 2^(score - r) <= 2^15 and
+    // enters PV as its fp16 rounding plus the fp16 rounding of the residual
+    // (pack_half2_split), so the residual stays a normal fp16 number down to
+    // weights 2^-25 below the largest.  l carries the same power-of-two
+    // factor (exact); the stored exp-sum is divided by it.
+    static constexpr bool kSplit = DT == 1 || VK_TILE_SPLIT_WEIGHTS;
+    static constexpr float kPScale = (DT == 0 && kSplit) ? 128.f : 1.f;
     struct Col {
         floatx4 acc[NACC];
         float m, r, l;
@@ -268,7 +278,7 @@ struct TileKernel {
             float ps = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                p[j] = exp2_fast(x[j] - rref);
+                p[j] = exp2_fast(x[j] - rref) * kPScale;
                 ps += p[j];
             }
             st[cb].l += ps;
@@ -277,6 +287,11 @@ struct TileKernel {
                 pack_bf16_split(p[2], p[3], pb[cb].y, pl[cb].y);
                 pack_bf16_split(p[4], p[5], pb[cb].z, pl[cb].z);
                 pack_bf16_split(p[6], p[7], pb[cb].w, pl[cb].w);
+            } else if constexpr (kSplit) {
+                pack_half2_split(p[0], p[1], pb[cb].x, pl[cb].x);
+                pack_half2_split(p[2], p[3], pb[cb].y, pl[cb].y);
+                pack_half2_split(p[4], p[5], pb[cb].z, pl[cb].z);
+                pack_half2_split(p[6], p[7], pb[cb].w, pl[cb].w);
             } else {
                 pb[cb].x = pack_half2(p[0], p[1]);
                 pb[cb].y = pack_half2(p[2], p[3]);
@@ -298,6 +313,9 @@ struct TileKernel {
                 if constexpr (DT == 1) {
                     st[cb].acc[m] = mfma32_bf16(av, pb[cb], st[cb].acc[m]);
                     st[cb].acc[m] = mfma32_bf16(av, pl[cb], st[cb].acc[m]);
+                } else if constexpr (kSplit) {
+                    st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
+                    st[cb].acc[m] = mfma32(av, pl[cb], st[cb].acc[m]);
                 } else {
                     st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
                 }
@@ -499,7 +517,8 @@ struct TileKernel {
             float lsum = st[cb].l + __shfl_xor(st[cb].l, 16);
             lsum += __shfl_xor(lsum, 32);
             // the partial's exp-sum is taken against the max itself
-            const float lmax = st[cb].r == -INFINITY ? lsum : lsum * exp2_fast(st[cb].r - st[cb].m);
+            const float lmax = (st[cb].r == -INFINITY ? lsum : lsum * exp2_fast(st[cb].r - st[cb].m)) *
+                               (1.f / kPScale);
             if (!valid[cb]) continue;
             if (P == 0 && lim[cb] <= 0) {   // a query that sees no key: zeros
                 float* o = a.out + row[cb] * D;

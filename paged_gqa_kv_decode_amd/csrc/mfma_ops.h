@@ -50,6 +50,23 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Two weights as an fp16 pair (round to nearest even) and the fp16 pair of
+// what that rounding left.  a - fp16(a) is exact in fp32 (the two are within
+// a factor 2), so hi + lo is within 2^-22 relative of the weight, or 2^-25
+// absolute where the residual falls below fp16's normal range (2^-14; 2^-14
+// if subnormal operands were flushed).  Callers scale the weights so that
+// the largest is between 2^7 and 2^15 (the fp16 range ends at 65504), which
+// makes that absolute term negligible next to the largest.  A PV product in
+// fp16 takes both pairs (two matrix products): one fp16 weight alone is off
+// by up to 2^-11 relative.
+__device__ __forceinline__ void pack_half2_split(float a, float b, uint32_t& hi, uint32_t& lo) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    const half2_t h = {(_Float16)a, (_Float16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const half2_t l = {(_Float16)(a - (float)h.x), (_Float16)(b - (float)h.y)};
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // fp32 element type: one k-slot per lane group.
 __device__ __forceinline__ floatx4 mfma4_f32(uint32_t a, uint32_t b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a),
@@ -86,19 +103,6 @@ __device__ __forceinline__ void pack_bf16_split(float a, float b, uint32_t& hi, 
     const float bh = __builtin_bit_cast(float, hi & 0xFFFF0000u);
     const bf2_t l = {(__bf16)(a - ah), (__bf16)(b - bh)};
     lo = __builtin_bit_cast(uint32_t, l);
-}
-
-// 8x8 fp16 transpose step: dims e of tokens 0..7 (lane group's k-slots) out of
-// 8 rows of 8 dims each.
-template <int E>
-__device__ __forceinline__ uint4 vt_operand(const uint4 (&v)[8]) {
-    constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-    uint4 a;
-    a.x = __builtin_amdgcn_perm(word<E / 2>(v[1]), word<E / 2>(v[0]), sel);
-    a.y = __builtin_amdgcn_perm(word<E / 2>(v[3]), word<E / 2>(v[2]), sel);
-    a.z = __builtin_amdgcn_perm(word<E / 2>(v[5]), word<E / 2>(v[4]), sel);
-    a.w = __builtin_amdgcn_perm(word<E / 2>(v[7]), word<E / 2>(v[6]), sel);
-    return a;
 }
 
 // 4x8 fp16 transpose step for the 16x16x16 product: dim e of the lane

@@ -83,6 +83,10 @@ vk_status hip_fail(hipError_t e) {
 // Resident wave slots of the current device for the matrix-core decode:
 // CUs x 4 SIMDs x 2 waves (its register budget allows two waves per SIMD).
 // The CU count is queried once per device; 2048 (256 CUs) if the query fails.
+// Largest partition count per sequence that the single-launch form merges in
+// place (the merge's few-partition path: all loads of a piece in flight).
+constexpr int32_t kFusedMaxPartitions = 8;
+
 int64_t wave_slots() {
     static std::atomic<int> cached[64] = {};
     int dev = 0;
@@ -258,6 +262,19 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         return VK_ERR_PARTITION;
     }
 
+    // The single launch merges the partials of a (sequence, KV head) in the
+    // workgroup that finishes last.  With more than kFusedMaxPartitions
+    // partitions that one workgroup folds them alone and becomes the launch's
+    // tail (measured on MI355X: 4 sequences of 131072 tokens at P = 512,
+    // 256 partitions, 483.8 us against 183.3 us for decode + reduce), so the
+    // call then enqueues the decode and the reduce instead: same kernels,
+    // same partials, the counters untouched.
+    const bool fused_split = fused && partition_size > 0 && max_num_partitions > kFusedMaxPartitions;
+    if (fused_split) {
+        fused = false;
+        counters = nullptr;
+    }
+
     vk::DecodeArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_cache);
@@ -290,8 +307,10 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     // other element types exist only in the matrix-core family; two
     // partitions per workgroup need an fp16 split without the in-place merge.
     const bool mhq = group == 1 || group == 16;
-    if (kernel == VK_KERNEL_DOT && (fused || mhq || dtype != VK_DTYPE_F16)) kernel = VK_KERNEL_AUTO;
-    if (kernel == VK_KERNEL_MFMA_W4P2 && (fused || partition_size == 0 || dtype != VK_DTYPE_F16))
+    if (kernel == VK_KERNEL_DOT && (fused || fused_split || mhq || dtype != VK_DTYPE_F16))
+        kernel = VK_KERNEL_AUTO;
+    if (kernel == VK_KERNEL_MFMA_W4P2 &&
+        (fused || fused_split || partition_size == 0 || dtype != VK_DTYPE_F16))
         kernel = VK_KERNEL_MFMA_W4;
     const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
     const int64_t slots = kernel == VK_KERNEL_DOT ? 0 : wave_slots();
@@ -338,6 +357,12 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     }
     if (!ok) return VK_ERR_GEOMETRY;
     if (e != hipSuccess) return hip_fail(e);
+    if (fused_split) {
+        const vk_status rs = vk_paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, num_seqs,
+                                                 num_q_heads, head_dim, partition_size,
+                                                 max_num_partitions, out, stream);
+        if (rs != VK_OK) return rs;
+    }
 
     vk_plan p = {};
     p.partition_size = partition_size;

@@ -14,6 +14,16 @@ from paged_gqa_kv_decode_amd.workloads import make_workload
 ATOL = 2e-3          # max over all elements of |gpu - ref|
 RTOL_ROW = 1e-2      # per (s, h) row: ||gpu - ref||_2 / max(||ref||_2, 1e-6)
 
+# Achieved-error bounds per element type of q/K/V, (max abs, max row-relative):
+# about 10x the largest error measured on MI355X over the whole GPU suite, so
+# that a loss of precision far below the stated tolerance still fails.
+# Measured maxima: fp16 2.4e-6 on the named workloads (4.4e-6 on the split
+# partials, 3.2e-6 on multi-token mixed batches), row-relative 3.1e-6; bf16
+# 1.8e-5 / 7.3e-6 (bf16 weights as value + residual carry ~2^-16); fp32
+# 3.9e-6 / 3.4e-6.  (Before the softmax weights entered the fp16 PV product
+# as value + residual, fp16 reached 1.3e-4, and 5.7e-4 on multi-token rows.)
+ACHIEVED = {"f16": (3e-5, 3e-5), "bf16": (2e-4, 1e-4), "f32": (4e-5, 4e-5)}
+
 
 def say(msg: str) -> None:
     print(msg, flush=True)
@@ -90,9 +100,13 @@ def err_stats(gpu, ref):
     return max_abs, row_rel, frac
 
 
-def assert_parity(gpu, ref, what):
+def assert_parity(gpu, ref, what, dtype="f16"):
+    """The stated tolerance, then the achieved-error bound of the element type."""
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
     max_abs, row_rel, frac = err_stats(gpu, ref)
     say(f"  {what}: max_abs={max_abs:.3e} max_row_rel={row_rel:.3e} allclose_frac={frac:.6f}")
     assert max_abs <= ATOL, f"{what}: max abs err {max_abs:.3e} > {ATOL}"
     assert row_rel <= RTOL_ROW, f"{what}: row rel err {row_rel:.3e} > {RTOL_ROW}"
+    a_abs, a_rel = ACHIEVED[dtype]
+    assert max_abs <= a_abs, f"{what}: max abs err {max_abs:.3e} above the {dtype} bound {a_abs}"
+    assert row_rel <= a_rel, f"{what}: row rel err {row_rel:.3e} above the {dtype} bound {a_rel}"

@@ -68,7 +68,7 @@ def test_element_types_decode(orc, geom, bs, kernel, dtype):
     ref = orc.paged_attention(wl)
     for P in (0, 512):
         gpu, _, last, _ = run_hip(wl, P, kernel=kernel)
-        assert_parity(gpu, ref, f"{dtype} {geom} P{P} kernel {last.kernel}")
+        assert_parity(gpu, ref, f"{dtype} {geom} P{P} kernel {last.kernel}", dtype=dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -80,7 +80,7 @@ def test_element_types_long_sequences(orc, dtype):
     ref = orc.paged_attention(wl)
     gpu, plan, _, _ = run_hip(wl, -1)
     say(f"  {dtype} long: P={plan.partition_size}")
-    assert_parity(gpu, ref, f"{dtype} long")
+    assert_parity(gpu, ref, f"{dtype} long", dtype=dtype)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -62,7 +62,7 @@ def test_bf16_mixed_batch(orc, geom, bs, kernel):
     for P in (0, 256):
         gpu = run(wl, kernel, P)
         say(f"[bf16 varlen] {geom} bs{bs} kernel {kernel} P{P}")
-        assert_parity(gpu, ref, f"bf16 {geom} bs{bs} k{kernel} P{P}")
+        assert_parity(gpu, ref, f"bf16 {geom} bs{bs} k{kernel} P{P}", dtype="bf16")
 
 
 def test_bf16_is_not_the_fp16_result(orc):
@@ -72,7 +72,7 @@ def test_bf16_is_not_the_fp16_result(orc):
                             head_dim=128, block_size=16, seed=5, dtype="bf16")
     ref = oracle_bf16(orc, wl)
     gpu = run(wl, vb.KERNEL_VARLEN_TILES, 0)
-    assert_parity(gpu, ref, "bf16 tiles")
+    assert_parity(gpu, ref, "bf16 tiles", dtype="bf16")
     as_f16 = orc.paged_varlen_arrays(wl.q.view(np.float16), wl.k_cache.view(np.float16),
                                      wl.v_cache.view(np.float16), wl.block_tables, wl.seq_lens,
                                      wl.meta["cu_q"], wl.scale)
