@@ -30,6 +30,13 @@
 #define VK_NUM_BLOCK_SIZES 3
 #define VK_BLOCK_SIZE_LIST {8, 16, 32}
 
+/* Size of the device array that holds the split-KV partials of
+ * vk_paged_gqa_decode_noalloc (one per GPU, for the life of the process):
+ * 64 MiB, enough for num_seqs * num_q_heads * max_num_partitions * (head_dim
+ * + 2) * 4 bytes of scratch up to about 16 M floats (e.g. 32 sequences of 16k
+ * tokens at (24, 4, 256) and partition 256: 51 MB). */
+#define VK_NOALLOC_SCRATCH_BYTES (64ull * 1024ull * 1024ull)
+
 /* A KV page id outside [0, num_blocks), or a device seq_len the page table
  * cannot hold, never reaches memory: the kernel reads page 0 instead and the
  * affected (sequence, head) results become NaN. */

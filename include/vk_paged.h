@@ -274,6 +274,38 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
                                     float* tmp_out, uint32_t* counters, void* stream);
 
 /*
+ * vk_paged_gqa_decode_noalloc — vk_paged_gqa_decode followed by
+ * vk_paged_gqa_reduce (same kernels, same launch choices, same result bit for
+ * bit) with the split-KV partials held in a device array of the library
+ * instead of caller buffers, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The call allocates and frees nothing.
+ *
+ * Arguments are those of vk_paged_gqa_decode without the three scratch
+ * pointers; `out` (fp32 [num_seqs, num_q_heads, head_dim]) is always required
+ * and receives the final normalised result.  partition_size 0 runs the
+ * unsplit decode into out (no scratch); 256 or 512 writes the partials into
+ * the array and merges them into out.  The partials (num_seqs * num_q_heads *
+ * max_num_partitions * (head_dim + 2) * 4 bytes, plus alignment) must fit
+ * VK_NOALLOC_SCRATCH_BYTES (64 MiB, vk_constants.h): larger calls return
+ * VK_ERR_SCRATCH_CAP before any HIP call.
+ * The array is one per GPU, held until the process ends, and shared by every
+ * call on that GPU: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be serialised by the caller.  Nothing in
+ * it needs clearing between calls (every partial the merge reads is written
+ * by the same call).  The first call on a device looks up that device's copy
+ * (VK_ERR_HIP if the lookup fails).  Other errors and device-side guards are
+ * those of vk_paged_gqa_decode and vk_paged_gqa_reduce.
+ */
+vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                      int32_t partition_size, int32_t max_num_partitions,
+                                      float* out, void* stream);
+
+/*
  * vk_plan_varlen — plan a vk_paged_gqa_varlen call (host only; no HIP call
  * when cu_count > 0).  seq_lens_host[s] (>= 1, within the page table) counts
  * all of sequence s's cached tokens including its q_lens_host[s] new query

@@ -30,7 +30,8 @@ EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fu
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
             "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
             "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce",
-            "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel", "vk_paged_gqa_varlen_dt")
+            "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel", "vk_paged_gqa_varlen_dt",
+            "vk_paged_gqa_decode_noalloc")
 
 
 class VkError(RuntimeError):
@@ -100,6 +101,9 @@ def lib() -> ctypes.CDLL:
     L.vk_paged_gqa_decode_fused.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             i64, ctypes.c_float, i32, i32, vp, vp, vp, vp, vp, vp]
     L.vk_paged_gqa_decode_fused.restype = i32
+    L.vk_paged_gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                              i64, ctypes.c_float, i32, i32, vp, vp]
+    L.vk_paged_gqa_decode_noalloc.restype = i32
     L.vk_plan_varlen.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, u64,
                                  ctypes.POINTER(_Plan)]
     L.vk_plan_varlen.restype = i32
@@ -289,6 +293,20 @@ def paged_gqa_decode_fused(q, k_cache, v_cache, block_tables, seq_lens, scale: f
     _check("vk_paged_gqa_decode_fused",
            lib().vk_paged_gqa_decode_fused(*args, _ptr(counters) if partition_size else None,
                                            _stream_handle(stream)))
+
+
+def paged_gqa_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                             partition_size: int, max_num_partitions: int, out,
+                             stream=None) -> None:
+    """Enqueue decode + reduce into out [S,Hq,D] fp32 with the split partials
+    in the library's own device array (no scratch arguments; calls on one GPU
+    must not overlap in time)."""
+    if out is None:
+        raise ValueError("out is required")
+    args = _decode_args(q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                        max_num_partitions, out, None, None, None)
+    _check("vk_paged_gqa_decode_noalloc",
+           lib().vk_paged_gqa_decode_noalloc(*args[:16], _stream_handle(stream)))
 
 
 def paged_gqa_reduce(max_logits, exp_sums, tmp_out, seq_lens, partition_size: int, out,

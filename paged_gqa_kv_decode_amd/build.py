@@ -27,7 +27,7 @@ ARCH = "gfx950"
 SOURCES = ["vk_host.cpp", "decode_dot.hip", "decode_mfma.hip", "decode_mfma_mhq.hip",
            "decode_mfma_bf16.hip", "decode_mfma_f32.hip", "decode_varlen.hip",
            "decode_varlen_tile.hip", "reduce.hip",
-           "kv_append.hip"]
+           "kv_append.hip", "noalloc.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

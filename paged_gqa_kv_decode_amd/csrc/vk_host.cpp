@@ -702,6 +702,55 @@ vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t
     return VK_OK;
 }
 
+vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                      int32_t partition_size, int32_t max_num_partitions,
+                                      float* out, void* stream) {
+    // Host checks of the sizes first (decode_impl repeats the rest before
+    // its launch): the partials must fit the library's array.
+    if (!out) return VK_ERR_NULL_ARG;
+    if (num_seqs <= 0 || num_seqs > 65535) return VK_ERR_BAD_DIM;
+    vk_status gs = geometry_status(num_q_heads, num_kv_heads, head_dim);
+    if (gs != VK_OK) return gs;
+    if (partition_size == 0) {
+        return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                           scale, 0, max_num_partitions, out, nullptr, nullptr, nullptr, nullptr,
+                           false, VK_DTYPE_F16, stream);
+    }
+    if (partition_size != VK_PARTITION_SMALL && partition_size != VK_PARTITION_LARGE)
+        return VK_ERR_PARTITION;
+    if (max_num_partitions < 1 ||
+        (int64_t)max_num_partitions * partition_size > (int64_t)INT32_MAX)
+        return VK_ERR_PARTITION;
+    // Layout in the array: max_logits, exp_sums, tmp_out, each at a 256-byte
+    // boundary (at most 2^16 * 32 * 2^23 * 258 * 4 bytes: no overflow).
+    const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_num_partitions;
+    const uint64_t vec = (rows * 4u + 255u) & ~(uint64_t)255u;
+    const uint64_t need = 2u * vec + rows * (uint64_t)head_dim * 4u;
+    if (need > VK_NOALLOC_SCRATCH_BYTES) return VK_ERR_SCRATCH_CAP;
+    void* base = nullptr;
+    hipError_t e = vk::noalloc_scratch(&base);
+    if (e != hipSuccess) return hip_fail(e);
+    char* b = static_cast<char*>(base);
+    float* ml = reinterpret_cast<float*>(b);
+    float* es = reinterpret_cast<float*>(b + vec);
+    float* to = reinterpret_cast<float*>(b + 2u * vec);
+    vk_status st = decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                               num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                               scale, partition_size, max_num_partitions, nullptr, ml, es, to,
+                               nullptr, false, VK_DTYPE_F16, stream);
+    if (st != VK_OK) return st;
+    const vk_plan launched = t_last_plan;   // the decode's launch shape, reported afterwards
+    st = vk_paged_gqa_reduce(ml, es, to, seq_lens, num_seqs, num_q_heads, head_dim,
+                             partition_size, max_num_partitions, out, stream);
+    if (st == VK_OK) t_last_plan = launched;
+    return st;
+}
+
 vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums, const float* tmp_out,
                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                               int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,

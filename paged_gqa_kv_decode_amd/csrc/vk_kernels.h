@@ -65,6 +65,10 @@ struct AppendArgs {
     double rope_theta;            // <= 0: no rotary embedding
 };
 
+// Device address of this device's copy of the library-held scratch array
+// (VK_NOALLOC_SCRATCH_BYTES; noalloc.hip), looked up once per device.
+hipError_t noalloc_scratch(void** out);
+
 // Each launcher returns hipSuccess or the launch error; `geometry_ok` is
 // false when no specialisation exists for the shape (host code checks first).
 hipError_t launch_decode_dot(const DecodeArgs& a, int group, int head_dim, int block_size,

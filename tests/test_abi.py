@@ -185,6 +185,59 @@ def test_reduce_validation():
     assert R(FAKE + 2, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
 
 
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=2, Hq=32, Hkv=8, D=128, bs=16, mb=8,
+             nb=64, scale=0.088, P=512, NP=1, out=FAKE)
+    a.update(kw)
+    return vb.lib().vk_paged_gqa_decode_noalloc(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"],
+                                                a["Hq"], a["Hkv"], a["D"], a["bs"], a["mb"],
+                                                a["nb"], a["scale"], a["P"], a["NP"], a["out"],
+                                                None)
+
+
+NOALLOC_BYTES = 64 << 20   # VK_NOALLOC_SCRATCH_BYTES
+
+
+def _noalloc_need(S, Hq, D, NP):
+    rows = S * Hq * NP
+    vec = (rows * 4 + 255) // 256 * 256
+    return 2 * vec + rows * D * 4
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), "NULL_ARG"), (dict(P=0, NP=1, out=None), "NULL_ARG"),
+    (dict(S=0), "BAD_DIM"), (dict(S=70000), "BAD_DIM"),
+    (dict(Hq=24, Hkv=8), "GEOMETRY"), (dict(P=128), "PARTITION"), (dict(NP=0), "PARTITION"),
+    (dict(NP=5_000_000), "PARTITION"),
+    # partials over the library's 64 MiB array: 2 x 32 x 3000 x 130 x 4 bytes = 99.8 MB
+    (dict(NP=3000), "SCRATCH_CAP"),
+    (dict(S=32, Hq=24, Hkv=4, D=256, bs=32, P=256, NP=100), "SCRATCH_CAP"),
+    # unsplit: the decode's own checks
+    (dict(P=0, NP=2), "PARTITION"), (dict(P=0, NP=1, q=None), "NULL_ARG"),
+])
+def test_noalloc_validation(kw, code):
+    """The no-allocation entry point refuses, on the host, what the decode
+    refuses and any split call whose partials exceed its array."""
+    assert _noalloc(**kw) == CODES[code]
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
+def test_noalloc_cap_boundary():
+    """The largest partition count whose partials fit passes the size check
+    (and then fails only at the device lookup, there being no GPU here); one
+    more is refused."""
+    S, Hq, D = 2, 32, 128
+    np_fit = max(n for n in range(1, 5000) if _noalloc_need(S, Hq, D, n) <= NOALLOC_BYTES)
+    assert _noalloc_need(S, Hq, D, np_fit + 1) > NOALLOC_BYTES
+    assert _noalloc(S=S, Hq=Hq, D=D, NP=np_fit + 1) == CODES["SCRATCH_CAP"]
+    assert _noalloc(S=S, Hq=Hq, D=D, NP=np_fit) == CODES["HIP"]
+    # every named long-context workload's partials fit: (S, Hq, D, P, max L)
+    for S_, Hq_, D_, P_, Lmax in ((32, 24, 256, 256, 16384), (64, 16, 128, 512, 32768),
+                                   (4, 16, 256, 512, 131072), (8, 32, 128, 512, 2048)):
+        assert _noalloc_need(S_, Hq_, D_, -(-Lmax // P_)) <= NOALLOC_BYTES
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="needs a machine without a GPU")
 def test_planner_device_query_without_gpu_is_hip_error():
     code = _c_plan([100], 32, 8, 128, 16, 8, -1, 0)
