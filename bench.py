@@ -170,6 +170,8 @@ def ceilings(wl, dev, P, reps=10):
            "page_read_sorted_GBps": page_total / pages(L.vkb_page_read, ids_sorted) / 1e9}
     out = {k_: round(v_, 1) for k_, v_ in gbs.items()}
     out["stream_read_GBps"] = max(out["stream_read_plain_GBps"], out["stream_read_nt_GBps"])
+    best = max(gbs, key=gbs.get)
+    out["read_ceiling_GBps"], out["read_ceiling_kernel"] = out[best], best.replace("_GBps", "")
     out.update({"page_bytes": page_bytes, "pages_per_group": ppg, "stream_blocks": blocks,
                 "flushed": "512 MiB read before each timed run"})
     return out
@@ -552,6 +554,90 @@ def cpu_single_thread():
     return res
 
 
+def planner_sweep(args):
+    """The data behind the partition planner's budget: for the four
+    grouped-query geometries and a range of batches, decode + reduce at P =
+    256 against P = 512 (HIP events on the launch stream, 10 steps per
+    segment in ABBA order, K/V pools rotated as in the timed step), beside
+    the full-partition work W(512) = Hq * sum_s floor(L_s / 512) per CU that
+    the planner compares with its budget (33 per CU: P = 512 when W(512) >=
+    33 * CUs).  Inputs are random fp16 drawn on the device (timing only)."""
+    import numpy as np
+    import torch
+    from paged_gqa_kv_decode_amd import binding as vb
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    geoms = [((32, 8, 128), 16), ((24, 4, 256), 32), ((16, 2, 128), 8), ((16, 2, 256), 32)]
+    rng = np.random.default_rng(5)
+    batches = [(f"{S}x32768", [32768] * S) for S in (1, 2, 3, 4, 6, 8, 10, 12, 16, 24)]
+    batches += [(f"{S}xU[1,32768]", list(rng.integers(1, 32769, S))) for S in (8, 16, 32, 64)]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for (Hq, Hkv, D), bs in geoms:
+        for name, lens in batches:
+            lens = np.asarray(lens, dtype=np.int32)
+            S = len(lens)
+            pages = [-(-int(L) // bs) for L in lens]
+            pool = int(sum(pages))
+            perm = rng.permutation(pool).astype(np.int32)
+            bt = np.zeros((S, max(pages)), dtype=np.int32)
+            o = 0
+            for i, n in enumerate(pages):
+                bt[i, :n] = perm[o:o + n]
+                o += n
+            kv_bytes = 4 * Hkv * D * int(lens.sum())
+            ncopies = max(2, min(16, -(-(4 * MALL_BYTES) // kv_bytes)))
+            q = torch.randn((S, Hq, D), device="cuda").half()
+            pools = [(torch.randn((pool, Hkv, bs, D), device="cuda").half(),
+                      torch.randn((pool, Hkv, bs, D), device="cuda").half()) for _ in range(ncopies)]
+            btd, sld = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+            steps = {P: vb.DecodeStep(q, pools[0][0], pools[0][1], btd, sld, lens, D ** -0.5, P)
+                     for P in (256, 512)}
+            times = {256: [], 512: []}
+            ctr = [0]
+
+            def seg(P, n, record):
+                st = steps[P]
+                for _ in range(n):
+                    k, v = pools[ctr[0] % ncopies]
+                    ctr[0] += 1
+                    st.args = (q, k, v, btd, sld)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    st.run()
+                    e1.record(stream)
+                    if record:
+                        times[P].append((e0, e1))
+            for P in (256, 512):
+                seg(P, 3, False)
+            for P in (256, 512, 512, 256):
+                seg(P, 10, True)
+            torch.cuda.synchronize()
+            us = {P: float(np.mean([a.elapsed_time(b) for a, b in times[P]])) * 1e3 for P in times}
+            w512 = Hq * int((lens // 512).sum())
+            plan = vb.plan_partitions(lens, Hq, Hkv, D, bs, bt.shape[1], -1, cu)
+            r = {"geometry": [Hq, Hkv, D], "block_size": bs, "batch": name,
+                 "w512_per_cu": round(w512 / cu, 2), "us_P256": round(us[256], 2),
+                 "us_P512": round(us[512], 2), "faster": 256 if us[256] < us[512] else 512,
+                 "planner": plan.partition_size}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+            del pools, steps, q
+            torch.cuda.empty_cache()
+    # the budget per CU that the data favour: the threshold on W(512)/CU
+    # that picks the faster size for the most batches (ties: the smallest
+    # loss in us)
+    cands = sorted({r["w512_per_cu"] for r in rows} | {33.0})
+    def score(b):
+        wrong = [r for r in rows if (512 if r["w512_per_cu"] >= b else 256) != r["faster"]]
+        loss = sum(abs(r["us_P256"] - r["us_P512"]) for r in wrong)
+        return (len(wrong), loss)
+    best = min(cands, key=score)
+    print(json.dumps({"planner_sweep": "summary", "cu_count": cu, "configs": len(rows),
+                      "budget_33_wrong": score(33.0)[0], "budget_33_loss_us": round(score(33.0)[1], 2),
+                      "best_threshold_per_cu": best, "best_wrong": score(best)[0],
+                      "best_loss_us": round(score(best)[1], 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -593,6 +679,9 @@ def main():
                          "(long32_16k at P=256 and 512, mixed64_32k at 512)")
     ap.add_argument("--flush", action="store_true",
                     help="also time the decode with a 512 MiB cache flush before each run")
+    ap.add_argument("--planner-sweep", action="store_true",
+                    help="time P=256 against P=512 over geometries and batches (the data "
+                         "behind the planner's budget); prints one JSON line per batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, --steps times (the "
                          "known-size reference for the HBM byte counters)")
@@ -609,6 +698,8 @@ def main():
     import torch
     from paged_gqa_kv_decode_amd import binding as vb
 
+    if args.planner_sweep:
+        return planner_sweep(args)
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")

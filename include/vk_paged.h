@@ -317,8 +317,11 @@ vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const 
  * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
  * call is unsplit when the tiles alone give one wave per wave slot
  * (w * n >= 8 * cu_count), otherwise split at 512 when
- * n * floor(L / 512) summed per sequence >= 33 * cu_count, else 256; when
- * that split's scratch would exceed the cap, 512, and failing that unsplit.
+ * Hq * ceil(q_len / T) * floor(L / 512) summed per sequence >= 33 * cu_count
+ * (vk_plan_partitions' rule, whose unit is a (query head, full partition)
+ * pair, counted for every tile; with one query token per sequence the two
+ * planners agree), else 256; when that split's scratch would exceed the
+ * cap, 512, and failing that unsplit.
  * NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
  * against the cap (an explicit partition request over it is an error).  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
  * q_len outside [0, seq_len]; VK_ERR_BAD_DIM if a q_len exceeds 65535.

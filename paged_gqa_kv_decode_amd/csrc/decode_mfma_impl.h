@@ -71,9 +71,10 @@ using namespace mfma;
 // kk the k-slot of lane group c is dim c * D/4 + kk, so lane (token i, c)
 // reads D/4 contiguous floats of its K row and the Q^T operand the same dims
 // of head i; the QK output (lane: head i, tokens 4c + r) is again the PV B
-// operand, one fp32 weight per product r, against V[token 4c + r][dim] read
-// one float per lane (16 lanes = 64 contiguous bytes).  Accumulator tile t
-// then holds dims 16t + 4c + r.
+// operand, one fp32 weight per product r.  In PV the A-operand row of lane i
+// is dim 64 t' + 4 i + e in tile 4 t' + e, so one 16-byte read of V[token
+// 4c + r][64 t' + 4 i, +4) feeds four products; accumulator tile 4 t' + e
+// then holds dims 64 t' + 16 c + 4 rr + e in row rr of lane group c.
 template <int D, int G, int BS, int W, int WP, int T, bool FUSED, int DT = 0>
 struct MfmaKernel {
     static_assert(T == 16, "16 tokens per wave step");
@@ -144,13 +145,13 @@ struct MfmaKernel {
 
     // K/V registers of one step.
     static constexpr int KQ = DT == 2 ? D / 16 : NKC;   // uint4 of K per token tile, and of Q
-    static constexpr int NF = DT == 2 ? D / 16 : 1;     // fp32: V floats per token per lane
+    static constexpr int NVQ = DT == 2 ? D / 64 : 1;    // fp32: uint4 of V per token per lane
     using QReg = uint4[KQ];
 
     // Dim of accumulator tile t, row rr, for lane group c.
     static __device__ __forceinline__ int acc_dim(int t, int c, int rr) {
         if constexpr (DT == 2)
-            return 16 * t + 4 * c + rr;
+            return 64 * (t / 4) + 16 * c + 4 * rr + t % 4;
         else
             return 128 * (t / 8) + 8 * (4 * c + rr) + t % 8;
     }
@@ -158,7 +159,7 @@ struct MfmaKernel {
     struct Buf {
         uint4 kr[NT][KQ];
         uint4 vr[NDH][NJ];
-        float vf[4][NF];
+        uint4 vq[4][NVQ];   // fp32: V[4c + r][64 t' + 4 i, +4)
     };
 
     // Page ids of the step at chunk offset `off`, read from the chunk's page
@@ -219,11 +220,12 @@ struct MfmaKernel {
             for (int r = 0; r < 4; ++r) {
                 const int tok = 4 * c + r;
                 const bool ok = FULL || tok < remain;
-                const float* vp = vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
-                                  (int64_t)((sp.off_slot + tok) % BS) * D;
+                const uint4* vp = reinterpret_cast<const uint4*>(
+                    vbase + (int64_t)page_of(tok, sp.pid) * page_stride +
+                    (int64_t)((sp.off_slot + tok) % BS) * D);
 #pragma unroll
-                for (int t = 0; t < NF; ++t)
-                    b.vf[r][t] = ok ? __builtin_nontemporal_load(vp + 16 * t + i) : 0.f;
+                for (int t = 0; t < NVQ; ++t)
+                    b.vq[r][t] = ok ? load_stream(vp + 16 * t + i) : make_uint4(0, 0, 0, 0);
             }
             return;
         }
@@ -348,15 +350,16 @@ struct MfmaKernel {
     // ---- O^T += V^T P^T on the matrix cores ----
     static __device__ __forceinline__ void pv(State& st, const Buf& b, const uint4& pb) {
         if constexpr (DT == 2) {
-            const float p0 = __builtin_bit_cast(float, pb.x), p1 = __builtin_bit_cast(float, pb.y);
-            const float p2 = __builtin_bit_cast(float, pb.z), p3 = __builtin_bit_cast(float, pb.w);
+            const uint32_t pw[4] = {pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-            for (int t = 0; t < NPT; ++t) {
-                st.acc[t] = mfma4_f32(b.vf[0][t], p0, st.acc[t]);
-                st.acc[t] = mfma4_f32(b.vf[1][t], p1, st.acc[t]);
-                st.acc[t] = mfma4_f32(b.vf[2][t], p2, st.acc[t]);
-                st.acc[t] = mfma4_f32(b.vf[3][t], p3, st.acc[t]);
-            }
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < NVQ; ++t) {
+                    st.acc[4 * t + 0] = mfma4_f32(b.vq[r][t].x, pw[r], st.acc[4 * t + 0]);
+                    st.acc[4 * t + 1] = mfma4_f32(b.vq[r][t].y, pw[r], st.acc[4 * t + 1]);
+                    st.acc[4 * t + 2] = mfma4_f32(b.vq[r][t].z, pw[r], st.acc[4 * t + 2]);
+                    st.acc[4 * t + 3] = mfma4_f32(b.vq[r][t].w, pw[r], st.acc[4 * t + 3]);
+                }
             return;
         }
         const auto& vr = b.vr;
@@ -400,8 +403,19 @@ struct MfmaKernel {
     // puts the 16 lanes of one read (rows 0..15, same piece) on 16 distinct
     // 16-byte bank groups.  Registers end up holding exactly the operands of
     // the direct loads.
-    static constexpr bool PF = VK_MFMA_LDS_PF && DT != 2 && T == 16;
-    static constexpr int SLOTS = NT * NKC + NDH * NJ;    // 16-byte registers of a Buf
+    //
+    // fp32 rows are 4D bytes (one or two rows per 1 KiB slot): K and V land
+    // in whole rows, K rows in slots 0 .. F_KSL - 1, V rows after them.  Lane
+    // l of a slot load takes row r = slot * F_RPS + l / F_LPR and piece
+    // (l % F_LPR) ^ (r % 16) of it, so piece p of row r sits at position
+    // (r % F_RPS) * F_LPR + (p ^ (r % 16)) of slot r / F_RPS: the 16 lanes of
+    // each read-back (16 rows at one piece for K, 16 pieces of one row for V)
+    // fall on 16 distinct 16-byte bank groups.
+    static constexpr bool PF = VK_MFMA_LDS_PF && T == 16;
+    static constexpr int F_RPS = DT == 2 ? 1024 / (4 * D) : 1;   // fp32: rows per slot
+    static constexpr int F_LPR = 64 / F_RPS;                     // fp32: 16-byte pieces per row
+    static constexpr int F_KSL = 16 / F_RPS;                     // fp32: slots of the K rows
+    static constexpr int SLOTS = DT == 2 ? 2 * F_KSL : NT * NKC + NDH * NJ;   // 1 KiB slots per wave
     static constexpr int WAVE_LDS = PF ? SLOTS * 64 * 16 : 0;   // bytes per wave
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -410,6 +424,25 @@ struct MfmaKernel {
                                                      const StepPages& sp, int g, int remain, int i,
                                                      int c) {
         const int64_t page_stride = (int64_t)a.num_kv_heads * BS * D;   // elements
+        if constexpr (DT == 2) {
+            static_assert(F_RPS * 4 * D == 1024 && F_LPR * 4 == D, "fp32 rows fill the slots");
+            const float* kbase = reinterpret_cast<const float*>(a.k) + (int64_t)g * BS * D;
+            const float* vbase = reinterpret_cast<const float*>(a.v) + (int64_t)g * BS * D;
+            const int l = i + 16 * c;
+#pragma unroll
+            for (int sl = 0; sl < F_KSL; ++sl) {
+                const int row = sl * F_RPS + l / F_LPR;
+                const int tok = FULL ? row : min(row, remain - 1);
+                const int64_t off = (int64_t)page_of(tok, sp.pid) * page_stride +
+                                    (int64_t)((sp.off_slot + tok) % BS) * D;
+                const int piece = (l % F_LPR) ^ (row & 15);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(kbase + off) + piece,
+                                                 (lds_ptr_t)(lds + sl * 1024), 16, 0, 2);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(vbase + off) + piece,
+                                                 (lds_ptr_t)(lds + (F_KSL + sl) * 1024), 16, 0, 2);
+            }
+            return;
+        }
         const uint16_t* kbase = a.k + (int64_t)g * BS * D;
         const uint16_t* vbase = a.v + (int64_t)g * BS * D;
         static_assert(NT == 1 && NKC % 2 == 0, "LDS prefetch: 16-token steps, whole K lines");
@@ -448,6 +481,27 @@ struct MfmaKernel {
     static __device__ __forceinline__ void read_lds(Buf& b, const char* lds, int remain, int lane,
                                                     int i, int c) {
         const uint4 z = make_uint4(0, 0, 0, 0);
+        if constexpr (DT == 2) {
+            // K: row i, pieces c KQ + u (dims [c D/4 + 4u, +4)).
+#pragma unroll
+            for (int u = 0; u < KQ; ++u) {
+                const int pos = (i % F_RPS) * F_LPR + ((c * KQ + u) ^ (i & 15));
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + (i / F_RPS) * 1024 + 16 * pos);
+                b.kr[0][u] = (FULL || i < remain) ? v : z;
+            }
+            // V: row 4c + r, pieces 16 t + i (dims [64 t + 4 i, +4)).
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < NVQ; ++t) {
+                    const int row = 4 * c + r;
+                    const int pos = (row % F_RPS) * F_LPR + ((16 * t + i) ^ (row & 15));
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        lds + (F_KSL + row / F_RPS) * 1024 + 16 * pos);
+                    b.vq[r][t] = (FULL || row < remain) ? v : z;
+                }
+            return;
+        }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll

@@ -482,13 +482,16 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     };
     if (P == -1) {
         // Unsplit when the (tile, KV head) workgroups fill the wave slots
-        // once (8 per CU); otherwise the decode's rule over (tile, full
-        // partition) units.  Many query rows can make the partials outgrow
-        // the cap: then 512, and failing that unsplit (which needs none).
+        // once (8 per CU); otherwise the decode's rule, its unit a (query
+        // head, full partition) pair, counted for every tile: W(P) =
+        // Hq * sum_s tiles_s * floor(L_s / P), which is the decode's W(P)
+        // when each sequence brings one query token.  Many query rows can
+        // make the partials outgrow the cap: then 512, and failing that
+        // unsplit (which needs none).
         if ((int64_t)waves_per_tile * num_kv_heads * tiles >= 8 * (int64_t)cu_count)
             P = 0;
         else
-            P = ((int64_t)num_kv_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
+            P = ((int64_t)num_q_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
         if (P == VK_PARTITION_SMALL && scratch_at(P) > cap) P = VK_PARTITION_LARGE;
         if (P == VK_PARTITION_LARGE && scratch_at(P) > cap) P = 0;
     }
@@ -498,7 +501,7 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
         p.work_full_parts = (int64_t)num_kv_heads * tiles;
     } else {
         p.max_num_partitions = (int32_t)((max_len + P - 1) / P);
-        p.work_full_parts = (int64_t)num_kv_heads * (P == VK_PARTITION_LARGE ? full512 : full256);
+        p.work_full_parts = (int64_t)num_q_heads * (P == VK_PARTITION_LARGE ? full512 : full256);
         p.scratch_bytes = scratch_at(P);
         if (p.scratch_bytes > cap) return VK_ERR_SCRATCH_CAP;
     }

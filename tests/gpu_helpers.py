@@ -22,7 +22,8 @@ RTOL_ROW = 1e-2      # per (s, h) row: ||gpu - ref||_2 / max(||ref||_2, 1e-6)
 # 1.8e-5 / 7.3e-6 (bf16 weights as value + residual carry ~2^-16); fp32
 # 3.9e-6 / 3.4e-6.  (Before the softmax weights entered the fp16 PV product
 # as value + residual, fp16 reached 1.3e-4, and 5.7e-4 on multi-token rows.)
-ACHIEVED = {"f16": (3e-5, 3e-5), "bf16": (2e-4, 1e-4), "f32": (4e-5, 4e-5)}
+ACHIEVED = {"f16": (3e-5, 3e-5), "bf16": (2e-4, 1e-4), "f32": (4e-5, 4e-5),
+            "f16_tiles": (2e-3, 1e-2)}
 
 
 def say(msg: str) -> None:

@@ -262,7 +262,7 @@ def _pv(lens, qlens, geom, bs=16, P=-1, cu=256, cap=0, mb=None):
 
 def test_plan_varlen_split_small_work(columns):
     # G = 4: 4 query tokens per tile; tiles 1 + 1, units 8 * 2 = 16 < 8 * 4.
-    # Full-512 work 8 * (1 + 1) = 16 < 33 * 4 -> 256; NP = ceil(1000 / 256) = 4.
+    # Full-512 work 32 * (1 + 1) = 64 < 33 * 4 -> 256; NP = ceil(1000 / 256) = 4.
     p = _pv([1000, 600], [4, 1], (32, 8, 128), cu=4)
     assert (p.partition_size, p.max_num_partitions) == (256, 4)
     assert p.scratch_bytes == 5 * 32 * 4 * 130 * 4
@@ -277,12 +277,26 @@ def test_plan_varlen_unsplit_when_tiles_fill_the_slots(columns):
 
 
 def test_plan_varlen_large_partition_at_the_budget(columns):
-    # G = 8, tiles 1 + 1 -> units 4 < 8.  Full-512 units: 2 * (16 + 8) = 48 >= 33.
+    # G = 8, tiles 1 + 1 -> units 4 < 8.  Full-512 units: 16 * (16 + 8) = 384 >= 33.
     p = _pv([8192, 4096], [2, 2], (16, 2, 256), bs=32, cu=1)
     assert (p.partition_size, p.max_num_partitions) == (512, 16)
-    # 2 * (8 + 4) = 24 < 33 -> 256
+    # 16 * (1 + 1) = 32 < 33 -> 256
+    p = _pv([1023, 600], [2, 2], (16, 2, 256), bs=32, cu=1)
+    assert (p.partition_size, p.max_num_partitions) == (256, 4)
+    # both sides of W(512) = budget: 16 CUs, budget 528 = 16 heads * 33 full partitions
+    p = _pv([33 * 512], [2], (16, 2, 256), bs=32, cu=16)
+    assert (p.partition_size, p.work_full_parts, p.budget) == (512, 528, 528)
+    p = _pv([33 * 512 - 1], [2], (16, 2, 256), bs=32, cu=16)
+    assert (p.partition_size, p.work_full_parts) == (256, 16 * 65)
+    # one query token per sequence: the decode planner's choice
+    for lens in ([8192, 4096], [1023, 600], [33 * 512], [33 * 512 - 1]):
+        for cu in (1, 16):
+            a = _pv(lens, [1] * len(lens), (16, 2, 256), bs=32, cu=cu)
+            d = vb.plan_partitions(np.array(lens, dtype=np.int32), 16, 2, 256, 32, 600, -1, cu)
+            assert (a.partition_size, a.work_full_parts) == (d.partition_size, d.work_full_parts)
+    # 2 * (8 + 4) full partitions of 512 tokens, 24 (tile, head) units
     p = _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, cu=1)
-    assert (p.partition_size, p.max_num_partitions) == (256, 16)
+    assert (p.partition_size, p.max_num_partitions) == (512, 8)
     # forced sizes and unsplit
     assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=512, cu=1).max_num_partitions == 8
     assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=0, cu=1).partition_size == 0

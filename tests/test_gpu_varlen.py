@@ -100,7 +100,8 @@ def test_prefill_workload_sampled_parity(orc, P):
     say(f"[varlen] prefill4_chunk1k P={plan.partition_size}")
     assert np.all(np.isfinite(gpu))
     rows, ref = sampled_rows_ref(orc, wl, 48, seed=5)
-    assert_parity(gpu[rows], ref, f"prefill4_chunk1k P={plan.partition_size} ({len(rows)} rows)")
+    assert_parity(gpu[rows], ref, f"prefill4_chunk1k P={plan.partition_size} ({len(rows)} rows)",
+                  dtype="f16_tiles")
 
 
 SWEEP = [((32, 8, 128), 8), ((32, 8, 128), 16), ((32, 8, 128), 32),
@@ -123,7 +124,7 @@ def test_all_specialisations_mixed_batch(orc, geom, bs):
     ref = oracle_varlen(orc, wl)
     for P in (0, 256, 512):
         gpu, _, _ = run_varlen(wl, P)
-        assert_parity(gpu, ref, f"{geom} bs{bs} P{P}")
+        assert_parity(gpu, ref, f"{geom} bs{bs} P{P}", dtype="f16_tiles")
 
 
 @pytest.mark.parametrize("P", [0, 512])

@@ -37,7 +37,7 @@ def test_prefill_workload_picks_tiles_and_matches(orc):
     assert vb.last_plan().kernel == vb.KERNEL_VARLEN_TILES
     assert np.all(np.isfinite(gpu))
     rows, ref = sampled_rows_ref(orc, wl, 64, seed=9)
-    assert_parity(gpu[rows], ref, f"prefill4_chunk1k tiles ({len(rows)} rows)")
+    assert_parity(gpu[rows], ref, f"prefill4_chunk1k tiles ({len(rows)} rows)", dtype="f16_tiles")
 
 
 @pytest.mark.parametrize("P", [-1, 0, 512])
@@ -57,7 +57,7 @@ def test_verify_workload_both_kernels_match(orc, P):
         vb.select_varlen_kernel(prev)
     assert plan.kernel == vb.KERNEL_VARLEN_TILES
     say(f"[tiles] verify32_q4 P={plan.partition_size}")
-    assert_parity(gpu, ref, f"verify32_q4 tiles P={plan.partition_size}")
+    assert_parity(gpu, ref, f"verify32_q4 tiles P={plan.partition_size}", dtype="f16_tiles")
 
 
 GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256), (16, 16, 128), (8, 8, 256),
@@ -79,7 +79,7 @@ def test_tiles_all_specialisations(orc, tiles, geom, bs):
     for P in (0, 256, 512):
         gpu, plan, _ = run_varlen(wl, P)
         assert plan.kernel == vb.KERNEL_VARLEN_TILES
-        assert_parity(gpu, ref, f"tiles {geom} bs{bs} P{P}")
+        assert_parity(gpu, ref, f"tiles {geom} bs{bs} P{P}", dtype="f16_tiles")
 
 
 def test_tiles_whole_prompt_and_long_chunks(orc, tiles):
@@ -90,7 +90,7 @@ def test_tiles_whole_prompt_and_long_chunks(orc, tiles):
     ref = oracle_varlen(orc, wl)
     for P in (0, 512):
         gpu, _, _ = run_varlen(wl, P)
-        assert_parity(gpu, ref, f"tiles prompt/chunks P{P}")
+        assert_parity(gpu, ref, f"tiles prompt/chunks P{P}", dtype="f16_tiles")
 
 
 def test_tiles_agree_with_columns(orc):
@@ -106,7 +106,7 @@ def test_tiles_agree_with_columns(orc):
         finally:
             vb.select_varlen_kernel(prev)
         assert plan.kernel == k
-        assert_parity(out[k], ref, f"kernel {k}")
+        assert_parity(out[k], ref, f"kernel {k}", dtype="f16_tiles")
     assert np.max(np.abs(out[vb.KERNEL_VARLEN_COLUMNS] - out[vb.KERNEL_VARLEN_TILES])) <= 2e-3
 
 
