@@ -40,7 +40,7 @@
 #define VK_TILE_D256_ONE_BLOCK 1   // D = 256: eight waves of one column block
 #endif
 #ifndef VK_TILE_SPLIT_WEIGHTS
-#define VK_TILE_SPLIT_WEIGHTS 1    // fp16: weights as value + residual (two PV products)
+#define VK_TILE_SPLIT_WEIGHTS 0    // fp16 residual PV product: 0 never, 1 on heavy tiles, 2 always
 #endif
 
 namespace vk {
@@ -91,13 +91,30 @@ struct TileKernel {
     // by more than kTau, so after the first tiles of a row the rescale is
     // skipped; the weights stay <= 2^kTau, well inside fp16.
     static constexpr float kTau = 8.f;
-    // fp16 with split weights: each weight is 2^7 * 2^(score - r) <= 2^15 and
-    // enters PV as its fp16 rounding plus the fp16 rounding of the residual
-    // (pack_half2_split), so the residual stays a normal fp16 number down to
-    // weights 2^-25 below the largest.  l carries the same power-of-two
-    // factor (exact); the stored exp-sum is divided by it.
-    static constexpr bool kSplit = DT == 1 || VK_TILE_SPLIT_WEIGHTS;
-    static constexpr float kPScale = (DT == 0 && kSplit) ? 128.f : 1.f;
+    // fp16 weights.  By default PV takes each weight's fp16 rounding alone
+    // and l sums exactly those rounded values, so every output is the convex
+    // combination sum_t w'_t v_t / sum_t w'_t of V rows with weights w'_t
+    // within 2^-11 relative of the softmax's: the error is at most 2^-11
+    // times the largest |v_t - o| of the row, and in practice far less where
+    // many keys share the weight (their rounding errors average out; a row
+    // dominated by one key is exact).  Measured on MI355X: 2.8e-5 max abs on
+    // the chunked-prefill workload, up to 5.6e-4 on rows of mixed test
+    // batches that see few keys or a peaked softmax.
+    // Two build options take the rounded residual through a second PV
+    // product as well (weights 2^7 * 2^(score - r) <= 2^15, so the residual
+    // stays a normal fp16 number; l and the stored exp-sum carry the same
+    // power of two), which brings the weights to ~2^-22:
+    //  * VK_TILE_SPLIT_WEIGHTS 2, on every tile: largest error ~1e-6, chunked
+    //    prefill 1528 us against 1270 us (the products are this kernel's
+    //    critical path);
+    //  * VK_TILE_SPLIT_WEIGHTS 1, only on tiles where some lane's share of
+    //    the tile's weights is at least 1/16 of that lane's exp-sum so far (a
+    //    row's first tiles, a tile that brings a new dominant key): largest
+    //    error 2.9e-5, 1410 us.  The waves of a workgroup meet at a barrier
+    //    on every tile, so one wave's extra pass holds all eight.
+    static constexpr int kSplitMode = DT == 1 ? 2 : VK_TILE_SPLIT_WEIGHTS;
+    static constexpr float kSplitShare = 1.f / 16.f;
+    static constexpr float kPScale = (DT == 0 && kSplitMode > 0) ? 128.f : 1.f;
     struct Col {
         floatx4 acc[NACC];
         float m, r, l;
@@ -246,7 +263,9 @@ struct TileKernel {
                 sc[cb][1] = qk_mma(k1, qb[cb][kk], sc[cb][1]);
             }
         }
-        uint4 pb[CB], pl[CB];   // weights (bf16: and their residuals)
+        uint4 pb[CB], pl[CB];   // weights and their residuals
+        float s_hi[CB], s_full[CB];   // fp16: the lane's sum of the rounded / exact weights
+        bool heavy = false;           // fp16: some column block of this lane needs the residual
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             float x[8];
@@ -260,8 +279,7 @@ struct TileKernel {
             float mx = x[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_rows4(mx);
             const float mnew = fmaxf(st[cb].m, mx);
             st[cb].m = mnew;
             const bool grow = mnew > st[cb].r + kTau;
@@ -275,33 +293,69 @@ struct TileKernel {
             }
             const float rref = (st[cb].r == -INFINITY) ? 0.f : st[cb].r;
             float p[8];
-            float ps = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = exp2_fast(x[j] - rref) * kPScale;
-                ps += p[j];
-            }
-            st[cb].l += ps;
+            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(x[j] - rref) * kPScale;
             if constexpr (DT == 1) {
+                float ps = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ps += p[j];
+                st[cb].l += ps;
                 pack_bf16_split(p[0], p[1], pb[cb].x, pl[cb].x);
                 pack_bf16_split(p[2], p[3], pb[cb].y, pl[cb].y);
                 pack_bf16_split(p[4], p[5], pb[cb].z, pl[cb].z);
                 pack_bf16_split(p[6], p[7], pb[cb].w, pl[cb].w);
-            } else if constexpr (kSplit) {
-                pack_half2_split(p[0], p[1], pb[cb].x, pl[cb].x);
-                pack_half2_split(p[2], p[3], pb[cb].y, pl[cb].y);
-                pack_half2_split(p[4], p[5], pb[cb].z, pl[cb].z);
-                pack_half2_split(p[6], p[7], pb[cb].w, pl[cb].w);
             } else {
-                pb[cb].x = pack_half2(p[0], p[1]);
-                pb[cb].y = pack_half2(p[2], p[3]);
-                pb[cb].z = pack_half2(p[4], p[5]);
-                pb[cb].w = pack_half2(p[6], p[7]);
-                pl[cb] = pb[cb];
+                // the rounded weights, their sum and (unless never taken) the
+                // rounded residuals
+                float h[8];
+                float hs = 0.f, fs = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    h[j] = (float)(_Float16)p[j];
+                    hs += h[j];
+                    fs += p[j];
+                }
+                pb[cb].x = pack_half2(h[0], h[1]);
+                pb[cb].y = pack_half2(h[2], h[3]);
+                pb[cb].z = pack_half2(h[4], h[5]);
+                pb[cb].w = pack_half2(h[6], h[7]);
+                if constexpr (kSplitMode > 0) {
+                    pl[cb].x = pack_half2(p[0] - h[0], p[1] - h[1]);
+                    pl[cb].y = pack_half2(p[2] - h[2], p[3] - h[3]);
+                    pl[cb].z = pack_half2(p[4] - h[4], p[5] - h[5]);
+                    pl[cb].w = pack_half2(p[6] - h[6], p[7] - h[7]);
+                    heavy = heavy || hs >= kSplitShare * (st[cb].l + hs);
+                }
+                s_hi[cb] = hs;
+                s_full[cb] = fs;
             }
         }
+        // fp16: one decision per wave (the products are the wave's).
+        bool split = DT == 1 || kSplitMode == 2;
+        if constexpr (DT == 0 && kSplitMode == 1) split = __ballot(heavy) != 0;
+        if constexpr (DT == 0) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) st[cb].l += split ? s_full[cb] : s_hi[cb];
+        }
         // O^T += V^T P^T, 16 dims at a time: k-slots of lane group c are keys
-        // 4c + e, then 16 + 4c + e (the order of the weights in pb).
+        // 4c + e, then 16 + 4c + e (the order of the weights in pb).  fp16:
+        // the residual weights' product, on the tiles that need it, is a
+        // second pass over V (its own loop: a branch among the products would
+        // keep the compiler from scheduling them together).
+        if constexpr (DT == 1 || kSplitMode == 2) {
+            pv<2>(st, lb, pb, pl, voff);
+        } else {
+            pv<0>(st, lb, pb, pl, voff);
+            if constexpr (kSplitMode == 1) {
+                if (split) pv<1>(st, lb, pb, pl, voff);
+            }
+        }
+    }
+
+    // PV of one tile: W = 0 the rounded weights, 1 the residuals, 2 both.
+    template <int W>
+    static __device__ __forceinline__ void pv(Col (&st)[CB], const char* lb, const uint4 (&pb)[CB],
+                                              const uint4 (&pl)[CB], const int (&voff)[8]) {
         const char* vb = lb + KSLOTS * 1024;
 #pragma unroll
         for (int m = 0; m < NACC; ++m) {
@@ -313,11 +367,9 @@ struct TileKernel {
                 if constexpr (DT == 1) {
                     st[cb].acc[m] = mfma32_bf16(av, pb[cb], st[cb].acc[m]);
                     st[cb].acc[m] = mfma32_bf16(av, pl[cb], st[cb].acc[m]);
-                } else if constexpr (kSplit) {
-                    st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
-                    st[cb].acc[m] = mfma32(av, pl[cb], st[cb].acc[m]);
                 } else {
-                    st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
+                    if constexpr (W != 1) st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
+                    if constexpr (W != 0) st[cb].acc[m] = mfma32(av, pl[cb], st[cb].acc[m]);
                 }
             }
         }
@@ -360,15 +412,41 @@ struct TileKernel {
             wait_vm<0>();
     }
 
+    // Workgroup order across the XCDs.  Workgroups are dealt to the eight
+    // XCDs in turn by linear id, each XCD with its own L2, and the query tiles
+    // of one (sequence, KV head) stream the same key tiles.  Here each XCD
+    // takes runs of 8 consecutive items (8 query tiles of one (sequence, KV
+    // head), read through one L2) while the runs are still dealt round-robin,
+    // so every XCD keeps a share of every sequence (contiguous quarters of
+    // the launch per XCD unbalanced the XCDs: 10% slower).  Measured on the
+    // chunked prefill: L2 hit rate 75% -> 83%, bytes fetched past L2
+    // 1.49 -> 1.00 GB, 1.8% faster.  A bijection of the ids (the tail of
+    // fewer than 64 keeps its order), so only the speed depends on it.
+    static __device__ __forceinline__ void xcd_order(unsigned& bx, unsigned& by, unsigned& bz) {
+        constexpr uint64_t kXcds = 8, kRun = 8;
+        const uint64_t gx = gridDim.x, gy = gridDim.y;
+        const uint64_t n = gx * gy * gridDim.z;
+        uint64_t i = blockIdx.x + gx * (blockIdx.y + gy * (uint64_t)blockIdx.z);
+        if (i < n / (kXcds * kRun) * (kXcds * kRun)) {
+            const uint64_t x = i % kXcds, slot = i / kXcds;
+            i = ((slot / kRun) * kXcds + x) * kRun + slot % kRun;
+        }
+        bx = (unsigned)(i % gx);
+        by = (unsigned)((i / gx) % gy);
+        bz = (unsigned)(i / (gx * gy));
+    }
+
     static __device__ void run(const VarlenArgs& va) {
         __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF];
         __shared__ int ring[NW][NBUF][64];   // per wave: page ids of tile u in slot u % NBUF
         const DecodeArgs& a = va.d;
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, c = lane >> 4;
+        unsigned bx, by, bz;
+        xcd_order(bx, by, bz);
         // Later tiles see more keys: they start first.
-        const int tile = va.tiles - 1 - (int)(blockIdx.x % (unsigned)va.tiles);
-        const int part = (int)(blockIdx.x / (unsigned)va.tiles);
-        const int g = blockIdx.y, s = blockIdx.z;
+        const int tile = va.tiles - 1 - (int)(bx % (unsigned)va.tiles);
+        const int part = (int)(bx / (unsigned)va.tiles);
+        const int g = (int)by, s = (int)bz;
         const int q0 = va.cu_q[s], qlen = va.cu_q[s + 1] - q0;
         if (qlen <= 0 || tile * BQ >= qlen) return;
         const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;

@@ -67,6 +67,20 @@ __device__ __forceinline__ void pack_half2_split(float a, float b, uint32_t& hi,
     lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// Max over the four 16-lane rows of a wave (lanes i, i + 16, i + 32, i + 48:
+// one matrix-core column), with gfx950's row-swapping permutes: VALU only, no
+// LDS round trip as for a shuffle.  permlane32_swap(v, v) leaves lane l with
+// v[l] in one result and v[l ^ 32] in the other (rows 0-1 and 2-3 swapped),
+// permlane16_swap the same for l ^ 16 (rows 0 and 1, 2 and 3).
+__device__ __forceinline__ float max_rows4(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const float m = fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
+    const uint32_t mb = __builtin_bit_cast(uint32_t, m);
+    const auto q = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);
+    return fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
+}
+
 // fp32 element type: one k-slot per lane group.
 __device__ __forceinline__ floatx4 mfma4_f32(uint32_t a, uint32_t b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a),

@@ -22,8 +22,13 @@ RTOL_ROW = 1e-2      # per (s, h) row: ||gpu - ref||_2 / max(||ref||_2, 1e-6)
 # 1.8e-5 / 7.3e-6 (bf16 weights as value + residual carry ~2^-16); fp32
 # 3.9e-6 / 3.4e-6.  (Before the softmax weights entered the fp16 PV product
 # as value + residual, fp16 reached 1.3e-4, and 5.7e-4 on multi-token rows.)
+# The LDS-tiled multi-token kernel takes each fp16 weight through PV as its
+# fp16 rounding alone (with the exp-sum of exactly those values): measured
+# 5.6e-4 / 4.4e-4 on mixed batches with rows that see few keys or a peaked
+# softmax, 2.8e-5 on the chunked-prefill workload; its bound is the stated
+# absolute tolerance and 10x the measured row-relative error.
 ACHIEVED = {"f16": (3e-5, 3e-5), "bf16": (2e-4, 1e-4), "f32": (4e-5, 4e-5),
-            "f16_tiles": (2e-3, 1e-2)}
+            "f16_tiles": (2e-3, 5e-3)}
 
 
 def say(msg: str) -> None:
