@@ -16,6 +16,12 @@
 
 #define VK_PARTITION_LARGE 512
 #define VK_PARTITION_SMALL 256
+/* Multi-token calls only (vk_plan_varlen, vk_paged_gqa_varlen*): a third,
+ * larger partition, which the planner picks for verification-shaped batches
+ * (several query tokens per sequence, one column tile each) when its full
+ * partitions alone reach the work budget.  An MI355X addition: half the
+ * partials of 512 and half the (partition, KV head) launch items. */
+#define VK_PARTITION_XLARGE 1024
 
 #define VK_DEFAULT_BUDGET_PER_CU 33
 #define VK_DEFAULT_SCRATCH_CAP (512ull * 1024ull * 1024ull)

@@ -128,7 +128,7 @@ enum {
 };
 
 typedef struct vk_plan {
-    int32_t  partition_size;     /* 0 = unsplit, else 256 or 512 */
+    int32_t  partition_size;     /* 0 = unsplit, else 256 or 512 (multi-token calls: or 1024) */
     int32_t  max_num_partitions; /* NP = ceil(max_s L_s / P); 1 when unsplit */
     int64_t  work_full_parts;    /* W(P) = Hq * sum_s floor(L_s / P) at the chosen P */
     int64_t  budget;             /* budget_per_cu * cu_count */
@@ -316,12 +316,16 @@ vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const 
  * head_dim 256 for VK_KERNEL_VARLEN_TILES.
  * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
  * call is unsplit when the tiles alone give one wave per wave slot
- * (w * n >= 8 * cu_count), otherwise split at 512 when
- * Hq * ceil(q_len / T) * floor(L / 512) summed per sequence >= 33 * cu_count
- * (vk_plan_partitions' rule, whose unit is a (query head, full partition)
- * pair, counted for every tile; with one query token per sequence the two
- * planners agree), else 256; when that split's scratch would exceed the
- * cap, 512, and failing that unsplit.
+ * (w * n >= 8 * cu_count), otherwise split at the largest P whose full-
+ * partition work W(P) = Hq * sum_s ceil(q_len_s / T) * floor(L_s / P)
+ * reaches 33 * cu_count, else at 256 (vk_plan_partitions' rule, whose unit
+ * is a (query head, full partition) pair, counted for every tile).  The
+ * sizes tried are 512 and, for column tiles when some sequence brings more
+ * than one query token, first VK_PARTITION_XLARGE = 1024 (an MI355X
+ * addition: half the partials of 512); with one query token per sequence
+ * the two planners agree.  When that split's scratch would exceed the cap,
+ * the next larger size, and failing that unsplit.  partition_request may
+ * force 256, 512 or 1024.
  * NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes
  * against the cap (an explicit partition request over it is an error).  Errors: those of vk_plan_partitions; VK_ERR_SEQ_LEN for a
  * q_len outside [0, seq_len]; VK_ERR_BAD_DIM if a q_len exceeds 65535.
@@ -353,8 +357,9 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
  *                  [total_q, Hq, NP, D] (split), as for vk_paged_gqa_decode
  * Query j of sequence s attends to tokens t < L_s - q_len_s + j + 1 with the
  * decode's scores and log2-space softmax; a row that sees no token is zeros.
- * Split: partition i of row j is written for i < ceil((L - q_len + j + 1) / P)
- * and merged by vk_paged_gqa_varlen_reduce on the same stream.  Geometries,
+ * Split (partition_size 256, 512 or 1024): partition i of row j is written
+ * for i < ceil((L - q_len + j + 1) / P) and merged by
+ * vk_paged_gqa_varlen_reduce on the same stream.  Geometries,
  * block sizes, errors and device-side guards as for vk_paged_gqa_decode (a
  * sequence longer than the page table gives NaN rows and reads nothing);
  * VK_ERR_BAD_DIM for total_q or max_q_len outside [1, 65535] or max_q_len >
@@ -392,7 +397,8 @@ vk_status vk_paged_gqa_varlen_dt(int32_t dtype, const void* q, const void* k_cac
  * vk_paged_gqa_varlen_reduce — the merge of vk_paged_gqa_reduce for
  * variable-length rows: row cu_seqlens_q[s] + j merges its
  * n = min(ceil((L - q_len + j + 1) / P), NP) partitions into out
- * [total_q, Hq, D]; a row that sees no token is zeros.
+ * [total_q, Hq, D]; a row that sees no token is zeros.  P is 256, 512 or
+ * 1024 (VK_ERR_PARTITION otherwise).
  */
 vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_sums,
                                      const float* tmp_out, const int32_t* seq_lens,

@@ -39,6 +39,9 @@
 #ifndef VK_TILE_D256_ONE_BLOCK
 #define VK_TILE_D256_ONE_BLOCK 1   // D = 256: eight waves of one column block
 #endif
+#ifndef VK_TILE_PV_AHEAD
+#define VK_TILE_PV_AHEAD 4         // PV: V reads kept this many products ahead (0: compiler's order)
+#endif
 #ifndef VK_TILE_SPLIT_WEIGHTS
 #define VK_TILE_SPLIT_WEIGHTS 0    // fp16 residual PV product: 0 never, 1 on heavy tiles, 2 always
 #endif
@@ -244,6 +247,25 @@ struct TileKernel {
         return *reinterpret_cast<const uint4*>(lb + slot * 1024 + 16 * lane);
     }
 
+    // Instruction order of a run of STEPS matrix-product steps fed from LDS
+    // (READS operand reads and MFMAS products per step): the reads of the
+    // first AH steps, then per step its products and the reads of the step
+    // AH later.  Left to itself the compiler issued the PV product's V reads
+    // just one product ahead, so every product waited out the LDS latency.
+    template <int STEPS, int READS, int MFMAS, int AHEAD>
+    static __device__ __forceinline__ void lds_ahead() {
+        constexpr int AH = AHEAD < STEPS ? AHEAD : STEPS;
+        if constexpr (AH > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, AH * READS, 0);   // LDS reads
+#pragma unroll
+            for (int j = 0; j < STEPS - AH; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);    // matrix products
+                __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AH * MFMAS, 0);
+        }
+    }
+
     // One tile for this wave's two column blocks; rem[cb]: keys of the tile
     // the lane's column sees (MASK: some column sees fewer than 32).
     template <bool MASK>
@@ -373,6 +395,7 @@ struct TileKernel {
                 }
             }
         }
+        lds_ahead<NACC, 2, CB * ((DT == 1 || W == 2) ? 2 : 1), VK_TILE_PV_AHEAD>();
     }
 
     // Page ids of the tile at k0 into a 256-byte LDS slot: lane k holds page

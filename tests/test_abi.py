@@ -150,7 +150,7 @@ def _decode(**kw):
     (dict(Hq=24, Hkv=8), "GEOMETRY"), (dict(Hq=16, Hkv=2, D=64), "GEOMETRY"),
     (dict(bs=64), "BLOCK_SIZE"), (dict(P=128), "PARTITION"), (dict(P=512, NP=0), "PARTITION"),
     (dict(P=0, NP=2), "PARTITION"), (dict(P=512, NP=5_000_000), "PARTITION"),
-    (dict(mb=200_000_000), "BAD_DIM"),
+    (dict(mb=200_000_000), "BAD_DIM"), (dict(P=1024), "PARTITION"),
 ])
 def test_decode_validation(kw, code):
     assert _decode(**kw) == CODES[code]
@@ -180,6 +180,7 @@ def test_reduce_validation():
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 96, 512, 4, FAKE, None) == CODES["GEOMETRY"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 0, 4, FAKE, None) == CODES["PARTITION"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 0, FAKE, None) == CODES["PARTITION"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 1024, 4, FAKE, None) == CODES["PARTITION"]
     assert R(FAKE, FAKE, FAKE + 4, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE + 8, None) == CODES["ALIGN"]
     assert R(FAKE + 2, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
@@ -277,9 +278,10 @@ def test_plan_varlen_unsplit_when_tiles_fill_the_slots(columns):
 
 
 def test_plan_varlen_large_partition_at_the_budget(columns):
-    # G = 8, tiles 1 + 1 -> units 4 < 8.  Full-512 units: 16 * (16 + 8) = 384 >= 33.
+    # G = 8, tiles 1 + 1 -> units 4 < 8.  Two query tokens: full-1024 units
+    # 16 * (8 + 4) = 192 >= 33 -> 1024.
     p = _pv([8192, 4096], [2, 2], (16, 2, 256), bs=32, cu=1)
-    assert (p.partition_size, p.max_num_partitions) == (512, 16)
+    assert (p.partition_size, p.max_num_partitions) == (1024, 8)
     # 16 * (1 + 1) = 32 < 33 -> 256
     p = _pv([1023, 600], [2, 2], (16, 2, 256), bs=32, cu=1)
     assert (p.partition_size, p.max_num_partitions) == (256, 4)
@@ -294,12 +296,49 @@ def test_plan_varlen_large_partition_at_the_budget(columns):
             a = _pv(lens, [1] * len(lens), (16, 2, 256), bs=32, cu=cu)
             d = vb.plan_partitions(np.array(lens, dtype=np.int32), 16, 2, 256, 32, 600, -1, cu)
             assert (a.partition_size, a.work_full_parts) == (d.partition_size, d.work_full_parts)
-    # 2 * (8 + 4) full partitions of 512 tokens, 24 (tile, head) units
+    # 16 * (4 + 2) = 96 full 1024-token units >= 33
     p = _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, cu=1)
-    assert (p.partition_size, p.max_num_partitions) == (512, 8)
+    assert (p.partition_size, p.max_num_partitions) == (1024, 4)
     # forced sizes and unsplit
     assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=512, cu=1).max_num_partitions == 8
     assert _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, P=0, cu=1).partition_size == 0
+
+
+def test_plan_varlen_xlarge_partition_rule(columns):
+    # Column tiles with several query tokens try 1024 first, under the same
+    # budget rule: both sides of W(1024) = budget (16 CUs: 528 = 16 heads x
+    # 33 full 1024-token partitions).
+    p = _pv([33 * 1024], [2], (16, 2, 256), bs=32, cu=16)
+    assert (p.partition_size, p.work_full_parts, p.max_num_partitions) == (1024, 528, 33)
+    assert p.scratch_bytes == 2 * 16 * 33 * 258 * 4
+    p = _pv([33 * 1024 - 1], [2], (16, 2, 256), bs=32, cu=16)
+    assert (p.partition_size, p.work_full_parts) == (512, 16 * 65)
+    # one query token per sequence: the decode planner's sizes only
+    p = _pv([33 * 1024], [1], (16, 2, 256), bs=32, cu=16)
+    d = vb.plan_partitions(np.array([33 * 1024], dtype=np.int32), 16, 2, 256, 32, 1100, -1, 16)
+    assert p.partition_size == d.partition_size == 512
+    # the verification shape: 32 x 4 tokens (32, 8, 128) on 4k-16k contexts
+    lens = [4096 + 384 * k for k in range(32)]
+    p = _pv(lens, [4] * 32, (32, 8, 128), cu=256)
+    full1024 = sum(L // 1024 for L in lens)
+    assert 32 * full1024 >= 33 * 256 and p.partition_size == 1024
+    assert p.max_num_partitions == -(-max(lens) // 1024)
+    # forced 1024, and its scratch
+    p = _pv([5000, 3000], [4, 4], (32, 8, 128), P=1024, cu=4)
+    assert (p.partition_size, p.max_num_partitions) == (1024, 5)
+    assert p.scratch_bytes == 8 * 32 * 5 * 130 * 4
+    # 3 CUs (budget 99): full-1024 units 32 * 2 = 64 < 99, full-512 units
+    # 32 * 4 = 128 >= 99 -> 512; with the cap one byte under its scratch
+    # (8 rows x 32 heads x 3 partitions) the next size up, 1024, before unsplit
+    assert _pv([1500, 1500], [4, 4], (32, 8, 128), cu=3).partition_size == 512
+    p = _pv([1500, 1500], [4, 4], (32, 8, 128), cu=3, cap=8 * 32 * 3 * 130 * 4 - 1)
+    assert (p.partition_size, p.max_num_partitions) == (1024, 2)
+    p = _pv([1500, 1500], [4, 4], (32, 8, 128), cu=3, cap=8 * 32 * 2 * 130 * 4 - 1)
+    assert p.partition_size == 0
+    # the decode planner does not take it
+    with pytest.raises(vb.VkError) as e:
+        vb.plan_partitions(np.array([4096], dtype=np.int32), 32, 8, 128, 16, 256, 1024, 4)
+    assert e.value.name == "PARTITION"
 
 
 @pytest.mark.parametrize("lens,qlens,name", [([100, 50], [101, 1], "SEQ_LEN"),
@@ -353,9 +392,14 @@ def test_plan_varlen_tiles_split_rule():
     assert (p.partition_size, p.max_num_partitions) == (256, 8)
     assert p.scratch_bytes == 164 * 32 * 8 * 130 * 4
     # one 16k sequence, 64 query tokens: 2 tiles, 64 waves < 8 * 10 -> split;
-    # full-512 units 8 * 2 * 32 = 512 >= 33 * 10 -> 512
+    # full-512 units 8 * 2 * 32 = 512 >= 33 * 10 -> 512; LDS tiles never
+    # take 1024
     p = _pv([16384], [64], (32, 8, 128), cu=10)
     assert (p.partition_size, p.max_num_partitions) == (512, 32)
+    # a 64k context: full-1024 units 32 * 2 * 64 = 4096 >= 330, yet 512
+    p = _pv([65536], [64], (32, 8, 128), cu=10)
+    assert p.kernel == vb.KERNEL_VARLEN_TILES
+    assert (p.partition_size, p.max_num_partitions) == (512, 128)
     # G = 6, D = 256: 21 tokens per tile; 4 chunks of 1024 -> 4 * 4 * 49 = 784
     # workgroups, 3136 waves >= 8 * 256: the chunked-prefill shape runs unsplit.
     p = _pv([3000, 5000, 8000, 2048], [1024] * 4, (24, 4, 256), bs=32, cu=256)

@@ -74,7 +74,7 @@ def sampled_rows_ref(orc, wl, rows_per_seq, seed):
     return np.array(rows), ref
 
 
-@pytest.mark.parametrize("P", [-1, 0, 256, 512])
+@pytest.mark.parametrize("P", [-1, 0, 256, 512, 1024])
 def test_verify_workload_parity(orc, P):
     wl = make_varlen("verify32_q4")
     ref = oracle_varlen(orc, wl)
@@ -114,7 +114,7 @@ SWEEP = [((32, 8, 128), 8), ((32, 8, 128), 16), ((32, 8, 128), 32),
 def test_all_specialisations_mixed_batch(orc, geom, bs):
     """Decode rows, verification rows, prefill chunks, a whole prompt (q_len =
     L) and an empty sequence in one batch, around page / step / partition
-    boundaries; unsplit and both partition sizes; canaries on."""
+    boundaries; unsplit and every partition size; canaries on."""
     Hq, Hkv, D = geom
     lens = [1, 17, 300, 513, 1030, 257, 64, 2100, 40]
     qlens = [1, 1, 3, 8, 300, 257, 0, 5, 40]
@@ -122,7 +122,7 @@ def test_all_specialisations_mixed_batch(orc, geom, bs):
                             head_dim=D, block_size=bs, seed=Hq * 100 + D + bs, pool_factor=1.5,
                             canaries=True, sigma_k=2.0)
     ref = oracle_varlen(orc, wl)
-    for P in (0, 256, 512):
+    for P in (0, 256, 512, 1024):
         gpu, _, _ = run_varlen(wl, P)
         assert_parity(gpu, ref, f"{geom} bs{bs} P{P}", dtype="f16_tiles")
 
@@ -227,7 +227,7 @@ def test_varlen_argument_errors():
     assert e.value.name == "PARTITION"
 
 
-@pytest.mark.parametrize("P", [256, 512])
+@pytest.mark.parametrize("P", [256, 512, 1024])
 def test_single_tile_longest_first_matches_grid_order(orc, P):
     """Every sequence's queries fit one column tile (<= 16 / G tokens): the
     split launch takes the decode's longest-first order over (partition,
