@@ -251,3 +251,30 @@ def test_single_tile_longest_first_matches_grid_order(orc, P):
         say(f"[columns] single tile P={P} order={order}")
         assert_parity(outs[order], ref, f"single tile P{P} order {order}")
     assert np.array_equal(outs[vb.ORDER_GRID], outs[vb.ORDER_LONGEST_FIRST])
+
+
+def test_varlen_reduce_row_and_chunk_merges_bit_identical(orc):
+    """The variable-length reduce merges one row per wave when there are many
+    rows of few partitions, and 32 dims per wave otherwise; per dim both take
+    the same fold steps in the same order, so the same partials give
+    bit-identical rows.  max_q_len (an upper bound that only sizes the grid)
+    picks the mode here: 4 -> 8 x 4 x 32 = 1024 rows (32 dims per wave),
+    8 -> 2048 rows (one row per wave); P = 1024, at most 7 partitions."""
+    import torch
+    lens = [3000, 5000, 1200, 7000, 4100, 2500, 6000, 800]
+    qlens = [4, 4, 3, 4, 1, 4, 2, 4]
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=16, seed=31)
+    q, k, v, bt, sl, cu = _dev(wl)
+    step = vb.VarlenStep(q, k, v, bt, sl, cu, wl.seq_lens, wl.meta["q_lens"], wl.scale, 1024)
+    assert (step.plan.partition_size, step.plan.max_num_partitions) == (1024, 7)
+    step.run()
+    outs = []
+    for mq in (4, 8):
+        o = torch.full_like(step.out, float("nan"))
+        vb.paged_gqa_varlen_reduce(step.max_logits, step.exp_sums, step.tmp_out, sl, cu, mq, 1024, o)
+        torch.cuda.synchronize()
+        outs.append(o.cpu().numpy())
+    say("[varlen] reduce row vs chunk merge, P=1024")
+    assert np.array_equal(outs[0], outs[1])
+    assert_parity(outs[1].astype(np.float64), oracle_varlen(orc, wl), "reduce row merge P1024")
