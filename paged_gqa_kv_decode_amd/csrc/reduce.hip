@@ -9,6 +9,76 @@
 #include "vk_kernels.h"
 
 namespace vk {
+namespace merge {
+
+// All NCH * 32 dims of one row in one wave: per 32-dim chunk the lanes,
+// partition order and fold steps of merge_columns (so the same results),
+// with each partition's (max, exp-sum) loaded once for the whole row and the
+// loads of every chunk in flight together (merge_columns over the chunks in
+// turn would wait for one chunk's loads at a time).
+template <int NCH>
+__device__ __forceinline__ void merge_row(const float* ml, const float* es, const float4* to,
+                                          int row4, int n, int lane, float4* dst) {
+    constexpr int KB = 16 / NCH > 0 ? 16 / NCH : 1;   // partitions per lane loaded ahead
+    const int c = lane % kCols, grp = lane / kCols;
+    if (n == 1) {
+        if (lane < kCols) {
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) dst[ch * kCols + lane] = to[ch * kCols + lane];
+        }
+        return;
+    }
+    State st[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        st[ch].m = -INFINITY;
+        st[ch].l = 0.f;
+        st[ch].acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int i0 = grp; i0 < n; i0 += KB * kGroups) {
+        float m[KB], l[KB];
+        float4 o[KB][NCH];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int i = i0 + k * kGroups;
+            const bool ok = i < n;
+            m[k] = ok ? ml[i] : -INFINITY;
+            l[k] = ok ? es[i] : 0.f;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch)
+                o[k][ch] = ok ? to[(int64_t)i * row4 + ch * kCols + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+            if (m[k] != -INFINITY) {
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) fold(st[ch], m[k], l[k], o[k][ch]);
+            }
+    }
+#pragma unroll
+    for (int off = kCols; off < 64; off <<= 1) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            State t;
+            t.m = __shfl_xor(st[ch].m, off);
+            t.l = __shfl_xor(st[ch].l, off);
+            t.acc.x = __shfl_xor(st[ch].acc.x, off);
+            t.acc.y = __shfl_xor(st[ch].acc.y, off);
+            t.acc.z = __shfl_xor(st[ch].acc.z, off);
+            t.acc.w = __shfl_xor(st[ch].acc.w, off);
+            fold_state(st[ch], t);
+        }
+    }
+    if (lane < kCols) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+            dst[ch * kCols + lane] = make_float4(st[ch].acc.x / st[ch].l, st[ch].acc.y / st[ch].l,
+                                                 st[ch].acc.z / st[ch].l, st[ch].acc.w / st[ch].l);
+    }
+}
+
+}  // namespace merge
+
 namespace {
 
 template <int D>
