@@ -481,6 +481,18 @@ const char* vk_status_string(vk_status s);
 /* HIP error code of this thread's last VK_ERR_HIP (0 if none). */
 int32_t vk_last_hip_error(void);
 
+/* 1 when the environment variable VK_TRACE is set (and not "0") and a
+ * roctx library could be loaded, else 0.  Then every entry point that enqueues
+ * work (the decode, reduce, multi-token and append calls) opens a roctx range
+ * named after itself for the length of the call, which rocprofv3
+ * --marker-trace records beside the kernels (the vllm-metal kernels page,
+ * section "上手实践：如何验证内核生效": confirm in a trace which kernels a
+ * request ran).  The library does not link a roctx library: the
+ * rocprofiler-sdk one (librocprofiler-sdk-roctx.so.1), else libroctx64, is
+ * loaded at the first call, and without either tracing stays off (VK_LOG
+ * reports that once).  The setting is read once per process. */
+int32_t vk_trace_enabled(void);
+
 /* This thread's last plan: from vk_plan_partitions or vk_plan_varlen, or
  * the launch shape of the last decode or multi-token launch (vllm-metal
  * kernels page, section "上手实践：如何验证内核生效": after a request the

@@ -28,7 +28,8 @@ ORDER_AUTO, ORDER_GRID, ORDER_LONGEST_FIRST = 0, 1, 2
 
 EXPORTED = ("vk_plan_partitions", "vk_paged_gqa_decode", "vk_paged_gqa_decode_fused",
             "vk_paged_gqa_reduce", "vk_paged_kv_append", "vk_select_decode_kernel",
-            "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_last_plan",
+            "vk_select_work_order", "vk_status_string", "vk_last_hip_error", "vk_trace_enabled",
+            "vk_last_plan",
             "vk_plan_varlen", "vk_paged_gqa_varlen", "vk_paged_gqa_varlen_reduce",
             "vk_paged_gqa_decode_dt", "vk_select_varlen_kernel", "vk_paged_gqa_varlen_dt",
             "vk_paged_gqa_decode_noalloc")
@@ -130,6 +131,8 @@ def lib() -> ctypes.CDLL:
     L.vk_status_string.restype = ctypes.c_char_p
     L.vk_last_hip_error.argtypes = []
     L.vk_last_hip_error.restype = i32
+    L.vk_trace_enabled.argtypes = []
+    L.vk_trace_enabled.restype = i32
     L.vk_last_plan.argtypes = [ctypes.POINTER(_Plan)]
     L.vk_last_plan.restype = i32
     _lib = L

@@ -1,6 +1,7 @@
 // C-ABI entry points of libvkpaged: validation, partition planning and kernel
 // dispatch.  Everything here is host code; it launches on the caller's stream
 // and never synchronises.  Validation is complete before the first HIP call.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -49,6 +50,53 @@ bool log_enabled() {
     }();
     return on;
 }
+
+// VK_TRACE=1: every entry point that enqueues work opens a roctx range named
+// after itself for the length of the call (rocprofv3 --marker-trace lists the
+// ranges beside the kernels they launched).  The roctx library is looked up
+// at the first call, so the library has no link-time dependency on it; if it cannot
+// be loaded, tracing stays off (and VK_LOG says so once).
+struct Roctx {
+    int (*push)(const char*) = nullptr;
+    int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+    static const Roctx r = [] {
+        Roctx x;
+        const char* e = std::getenv("VK_TRACE");
+        if (!e || !e[0] || e[0] == '0') return x;
+        // rocprofv3 records the rocprofiler-sdk roctx library's ranges; the
+        // older libroctx64 (same two functions) serves older tools.
+        void* h = nullptr;
+        for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so",
+                                "libroctx64.so.4", "libroctx64.so"})
+            if (!h) h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
+        if (h) {
+            x.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+            x.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+            if (!x.push || !x.pop) x = Roctx();
+        }
+        if (!x.push && log_enabled()) std::fprintf(stderr, "[vk] VK_TRACE: no roctx library found, tracing off\n");
+        return x;
+    }();
+    return r;
+}
+
+class TraceRange {
+public:
+    explicit TraceRange(const char* name) : on_(roctx().push != nullptr) {
+        if (on_) roctx().push(name);
+    }
+    ~TraceRange() {
+        if (on_) roctx().pop();
+    }
+    TraceRange(const TraceRange&) = delete;
+    TraceRange& operator=(const TraceRange&) = delete;
+
+private:
+    bool on_;
+};
 
 // Null pointers pass (their own checks decide whether they are allowed).
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
@@ -123,6 +171,8 @@ const char* vk_status_string(vk_status s) {
 }
 
 int32_t vk_last_hip_error(void) { return t_last_hip_error; }
+
+int32_t vk_trace_enabled(void) { return roctx().push != nullptr ? 1 : 0; }
 
 vk_status vk_last_plan(vk_plan* out) {
     if (!out) return VK_ERR_NULL_ARG;
@@ -391,6 +441,7 @@ vk_status vk_paged_gqa_decode(const void* q, const void* k_cache, const void* v_
                               int64_t num_blocks, float scale, int32_t partition_size,
                               int32_t max_num_partitions, float* out, float* max_logits,
                               float* exp_sums, float* tmp_out, void* stream) {
+    TraceRange trace("vk_paged_gqa_decode");
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
@@ -405,6 +456,7 @@ vk_status vk_paged_gqa_decode_dt(int32_t dtype, const void* q, const void* k_cac
                                  int32_t partition_size, int32_t max_num_partitions, float* out,
                                  float* max_logits, float* exp_sums, float* tmp_out,
                                  void* stream) {
+    TraceRange trace("vk_paged_gqa_decode_dt");
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
@@ -419,6 +471,7 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
                                     int32_t partition_size, int32_t max_num_partitions,
                                     float* out, float* max_logits, float* exp_sums,
                                     float* tmp_out, uint32_t* counters, void* stream) {
+    TraceRange trace("vk_paged_gqa_decode_fused");
     return decode_impl(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_num_partitions, out, max_logits, exp_sums, tmp_out,
@@ -630,6 +683,7 @@ vk_status vk_paged_gqa_varlen(const void* q, const void* k_cache, const void* v_
                               int64_t num_blocks, float scale, int32_t partition_size,
                               int32_t max_num_partitions, float* out, float* max_logits,
                               float* exp_sums, float* tmp_out, void* stream) {
+    TraceRange trace("vk_paged_gqa_varlen");
     return varlen_impl(VK_DTYPE_F16, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q,
                        num_seqs, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
@@ -645,6 +699,7 @@ vk_status vk_paged_gqa_varlen_dt(int32_t dtype, const void* q, const void* k_cac
                                  float scale, int32_t partition_size, int32_t max_num_partitions,
                                  float* out, float* max_logits, float* exp_sums, float* tmp_out,
                                  void* stream) {
+    TraceRange trace("vk_paged_gqa_varlen_dt");
     return varlen_impl(dtype, q, k_cache, v_cache, block_tables, seq_lens, cu_seqlens_q, num_seqs,
                        total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks, scale, partition_size, max_num_partitions,
@@ -657,6 +712,7 @@ vk_status vk_paged_gqa_varlen_reduce(const float* max_logits, const float* exp_s
                                      int32_t max_q_len, int32_t num_q_heads, int32_t head_dim,
                                      int32_t partition_size, int32_t max_num_partitions,
                                      float* out, void* stream) {
+    TraceRange trace("vk_paged_gqa_varlen_reduce");
     if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !cu_seqlens_q || !out)
         return VK_ERR_NULL_ARG;
     if (!vectors_aligned({tmp_out, out}, {max_logits, exp_sums, seq_lens, cu_seqlens_q}))
@@ -691,6 +747,7 @@ vk_status vk_paged_kv_append(const void* k_new, const void* v_new, const int32_t
                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                              int64_t num_blocks, double rope_theta, void* k_cache, void* v_cache,
                              void* stream) {
+    TraceRange trace("vk_paged_kv_append");
     if (!k_new || !v_new || !block_tables || !positions || !k_cache || !v_cache)
         return VK_ERR_NULL_ARG;
     if (num_seqs <= 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
@@ -725,6 +782,7 @@ vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const 
                                       int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                       int32_t partition_size, int32_t max_num_partitions,
                                       float* out, void* stream) {
+    TraceRange trace("vk_paged_gqa_decode_noalloc");
     // Host checks of the sizes first (decode_impl repeats the rest before
     // its launch): the partials must fit the library's array.
     if (!out) return VK_ERR_NULL_ARG;
@@ -771,6 +829,7 @@ vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums, co
                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                               int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,
                               float* out, void* stream) {
+    TraceRange trace("vk_paged_gqa_reduce");
     if (!max_logits || !exp_sums || !tmp_out || !seq_lens || !out) return VK_ERR_NULL_ARG;
     if (!vectors_aligned({tmp_out, out}, {max_logits, exp_sums, seq_lens})) return VK_ERR_ALIGN;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_seqs > 65535) return VK_ERR_BAD_DIM;

@@ -460,3 +460,29 @@ def test_varlen_dt_rejects_other_element_types():
         code = L.vk_paged_gqa_varlen_dt(dtype, None, None, None, None, None, None, 1, 1, 1, 32, 8,
                                         128, 16, 1, 1, 1.0, 0, 1, None, None, None, None, None)
         assert vb.STATUS_NAMES[code] == "DTYPE"
+
+
+def test_trace_switch_loads_roctx():
+    """VK_TRACE=1 turns on roctx ranges around the entry points that enqueue
+    work (a roctx library loaded at the first call); unset or "0", tracing is off.
+    A traced call still validates and returns as usual (checked on a call
+    refused on the host)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from paged_gqa_kv_decode_amd import binding as vb\n"
+            "L = vb.lib()\n"
+            "r = L.vk_paged_gqa_reduce(None, None, None, None, 1, 32, 128, 512, 4, None, None)\n"
+            "print(L.vk_trace_enabled(), r)\n") % ROOT
+    outs = {}
+    for val in ("1", "0", None):
+        env = {k: v for k, v in os.environ.items() if k != "VK_TRACE"}
+        if val is not None:
+            env["VK_TRACE"] = val
+        p = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=120)
+        assert p.returncode == 0, p.stderr
+        outs[val] = p.stdout.split()
+    null_arg = str(CODES["NULL_ARG"])
+    assert outs["1"] == ["1", null_arg]
+    assert outs["0"] == ["0", null_arg] and outs[None] == ["0", null_arg]
