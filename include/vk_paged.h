@@ -310,14 +310,17 @@ vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const 
  * when cu_count > 0).  seq_lens_host[s] (>= 1, within the page table) counts
  * all of sequence s's cached tokens including its q_lens_host[s] new query
  * tokens (0 <= q_len <= seq_len).  The kernel follows vk_select_varlen_kernel
- * and is reported in plan_out->kernel.  A tile holds T query tokens of one KV
- * head's G heads and runs on w waves: T = 16 / G, w = 1 for
- * VK_KERNEL_VARLEN_COLUMNS; T = 128 / G, w = 4 at head_dim 128 and 8 at
- * head_dim 256 for VK_KERNEL_VARLEN_TILES.
- * With n = Hkv * sum ceil(q_len / T) tiles and partition_request == -1 the
+ * and is reported in plan_out->kernel.  A tile covers (query token, head)
+ * columns of one KV head's G heads and runs on w waves: for
+ * VK_KERNEL_VARLEN_COLUMNS T = 16 / G whole tokens, w = 1, so a sequence has
+ * t_s = ceil(q_len / T) tiles; for VK_KERNEL_VARLEN_TILES 128 consecutive
+ * columns in token-major order (across token boundaries where G does not
+ * divide 128), w = 4 at head_dim 128 and 8 at head_dim 256, so
+ * t_s = ceil(q_len * G / 128).
+ * With n = Hkv * sum t_s tiles and partition_request == -1 the
  * call is unsplit when the tiles alone give one wave per wave slot
  * (w * n >= 8 * cu_count), otherwise split at the largest P whose full-
- * partition work W(P) = Hq * sum_s ceil(q_len_s / T) * floor(L_s / P)
+ * partition work W(P) = Hq * sum_s t_s * floor(L_s / P)
  * reaches 33 * cu_count, else at 256 (vk_plan_partitions' rule, whose unit
  * is a (query head, full partition) pair, counted for every tile).  The
  * sizes tried are 512 and, for column tiles when some sequence brings more

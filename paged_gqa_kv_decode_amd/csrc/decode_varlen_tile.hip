@@ -7,9 +7,15 @@
 //
 // The column kernel gives each wave 16 (token, head) columns and streams the
 // keys through that wave's own prefetch slots, so every 16 / G query tokens
-// re-read the whole context.  Here a workgroup of four waves owns 128 columns (BQ = 128 / G
-// query tokens x G heads) and streams the keys through LDS in 32-key tiles:
-// each tile is fetched once per workgroup and serves all 128 columns.
+// re-read the whole context.  Here a workgroup owns 128 consecutive columns
+// of one (sequence, KV head) — columns are (token, head) pairs in token-major
+// order, so a workgroup covers 128 / G query tokens and, where G does not
+// divide 128, runs across token boundaries — and streams the keys through LDS
+// in 32-key tiles: each tile is fetched once per workgroup and serves all 128
+// columns.  At G = 6, 1024 query tokens are then exactly 48 workgroups (whole
+// tokens per workgroup would take 49, the last one partial; on the chunked
+// prefill of 4 x 1024 tokens that is 768 workgroups, three full rounds of the
+// 256 CUs, instead of 784).
 //
 //  * Loads: the tile's K and V go straight from the paged cache into LDS
 //    (global_load_lds_dwordx4: lane l's 16 bytes land at slot base + 16 l),
@@ -67,8 +73,7 @@ template <int D, int G, int BS, int DT>
 struct TileKernel {
     static constexpr int CB = tile_blocks(D);    // 16-column blocks per wave
     static constexpr int NW = tile_waves(D);     // waves per workgroup
-    static constexpr int BQ = NW * CB * 16 / G;  // query tokens per workgroup
-    static constexpr int NCOL = BQ * G;          // columns in use
+    static constexpr int NC = NW * CB * 16;      // columns per workgroup (128)
     static constexpr int KT = 32;                // keys per tile
     static constexpr int NKC = D / 32;           // QK k-chunks of 32 dims
     static constexpr int NDH = D / 128;          // 128-dim halves of a V row
@@ -471,29 +476,30 @@ struct TileKernel {
         const int part = (int)(bx / (unsigned)va.tiles);
         const int g = (int)by, s = (int)bz;
         const int q0 = va.cu_q[s], qlen = va.cu_q[s + 1] - q0;
-        if (qlen <= 0 || tile * BQ >= qlen) return;
+        if (qlen <= 0 || tile * NC >= qlen * G) return;
         const int Hq = a.num_q_heads, P = a.partition_size, NP = a.max_num_partitions;
         const int L = a.seq_lens[s];
         const bool poison = L > a.max_blocks_per_seq * BS;
         // The workgroup's key range ends where its last query token's does.
-        const int kv_end = L - qlen + min(qlen, (tile + 1) * BQ);
+        const int kv_end = L - qlen + min(qlen, (tile * NC + NC - 1) / G + 1);
         int t_begin = 0, t_end = kv_end;
         if (P > 0) {
             t_begin = part * P;
             t_end = min(kv_end, t_begin + P);
         }
 
-        // Columns: lane column i of block cb is workgroup column 32 wave + 16 cb + i.
+        // Columns: lane column i of block cb is workgroup column 16 (CB wave + cb) + i,
+        // column tile * NC + that of the (sequence, KV head): token / G, head % G.
         bool valid[CB], col_poison[CB];
         int lim[CB];
         int64_t row[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const int cw = 16 * CB * wave + 16 * cb + i;
-            const int jt = tile * BQ + cw / G;
-            valid[cb] = cw < NCOL && jt < qlen;
+            const int cg = tile * NC + 16 * CB * wave + 16 * cb + i;
+            const int jt = cg / G;
+            valid[cb] = jt < qlen;
             lim[cb] = valid[cb] ? L - qlen + jt + 1 : 0;
-            row[cb] = ((int64_t)q0 + jt) * Hq + g * G + cw % G;
+            row[cb] = ((int64_t)q0 + jt) * Hq + g * G + cg % G;
             col_poison[cb] = P > 0 && part == NP - 1 && lim[cb] > t_begin + P;
         }
         if (t_end <= t_begin || poison) {   // uniform over the workgroup
@@ -679,7 +685,7 @@ hipError_t launch_bs(const VarlenArgs& a, int dtype, int bs, dim3 grid, hipStrea
 
 }  // namespace
 
-int varlen_tile_tokens(int group) { return group > 0 && group <= 16 ? 128 / group : 0; }
+int64_t varlen_tile_count(int64_t q_len, int group) { return (q_len * group + 127) / 128; }
 int varlen_tile_threads(int head_dim) { return 64 * tile_waves(head_dim); }
 
 hipError_t launch_varlen_tile(const VarlenArgs& a, int dtype, int group, int head_dim,

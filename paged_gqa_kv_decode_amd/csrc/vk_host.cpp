@@ -499,7 +499,7 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
     const int group = num_q_heads / num_kv_heads;
     const int32_t kernel = varlen_kernel(max_q, group);
     const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
-    const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
+    const int tpt = vk::varlen_tokens_per_tile(group);   // column kernel
     const int waves_per_tile = tiled ? vk::varlen_tile_threads(head_dim) / 64 : 1;
     int64_t max_len = 0, total_q = 0, tiles = 0, full1024 = 0, full512 = 0, full256 = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
@@ -508,7 +508,7 @@ vk_status vk_plan_varlen(const int32_t* seq_lens_host, const int32_t* q_lens_hos
         if (ql < 0 || ql > L) return VK_ERR_SEQ_LEN;
         if (L > max_len) max_len = L;
         total_q += ql;
-        const int64_t t = (ql + tpt - 1) / tpt;
+        const int64_t t = tiled ? vk::varlen_tile_count(ql, group) : (ql + tpt - 1) / tpt;
         tiles += t;
         full1024 += t * (L / VK_PARTITION_XLARGE);
         full512 += t * (L / VK_PARTITION_LARGE);
@@ -610,8 +610,8 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
     const int group = num_q_heads / num_kv_heads;
     const int32_t kernel = varlen_kernel(max_q_len, group);
     const bool tiled = kernel == VK_KERNEL_VARLEN_TILES;
-    const int tpt = tiled ? vk::varlen_tile_tokens(group) : vk::varlen_tokens_per_tile(group);
-    const int64_t tiles = (max_q_len + tpt - 1) / tpt;
+    const int tpt = vk::varlen_tokens_per_tile(group);
+    const int64_t tiles = tiled ? vk::varlen_tile_count(max_q_len, group) : (max_q_len + tpt - 1) / tpt;
     const int64_t gx = tiles * (partition_size == 0 ? 1 : max_num_partitions);
     if (gx > INT32_MAX) return VK_ERR_BAD_DIM;
 

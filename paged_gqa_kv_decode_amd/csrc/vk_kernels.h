@@ -96,11 +96,11 @@ hipError_t launch_decode_mfma_f32(const DecodeArgs& a, bool mhq, int group, int 
 hipError_t launch_decode_varlen(const VarlenArgs& a, int dtype, int group, int head_dim,
                                 int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok);
 int varlen_tokens_per_tile(int group);
-// Four waves per workgroup of 128 / G query tokens; grid (tiles * max(NP, 1),
-// Hkv, S) with tiles = ceil(max_q_len / varlen_tile_tokens(G)).
+// Workgroups of 128 consecutive (token, head) columns; grid (tiles * max(NP, 1),
+// Hkv, S) with tiles = varlen_tile_count(max_q_len, G) = ceil(max_q_len * G / 128).
 hipError_t launch_varlen_tile(const VarlenArgs& a, int dtype, int group, int head_dim,
                               int block_size, dim3 grid, hipStream_t stream, bool* geometry_ok);
-int varlen_tile_tokens(int group);
+int64_t varlen_tile_count(int64_t q_len, int group);
 int varlen_tile_threads(int head_dim);
 hipError_t launch_kv_append(const AppendArgs& a, int num_seqs, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, dim3 grid, hipStream_t stream,

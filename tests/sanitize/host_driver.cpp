@@ -55,7 +55,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int, int, int, int
     ++g_launches; *ok = true; *block = 64 * waves; return hipSuccess;
 }
 int varlen_tokens_per_tile(int group) { return group > 0 && group <= 16 ? 16 / group : 0; }
-int varlen_tile_tokens(int group) { return group > 0 && group <= 16 ? 128 / group : 0; }
+int64_t varlen_tile_count(int64_t q_len, int group) { return (q_len * group + 127) / 128; }
 int varlen_tile_threads(int head_dim) { return head_dim == 256 ? 512 : 256; }
 hipError_t launch_decode_varlen(const VarlenArgs& a, int, int, int, int, dim3 grid, hipStream_t,
                                 bool* ok) {

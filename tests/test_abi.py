@@ -400,10 +400,16 @@ def test_plan_varlen_tiles_split_rule():
     p = _pv([65536], [64], (32, 8, 128), cu=10)
     assert p.kernel == vb.KERNEL_VARLEN_TILES
     assert (p.partition_size, p.max_num_partitions) == (512, 128)
-    # G = 6, D = 256: 21 tokens per tile; 4 chunks of 1024 -> 4 * 4 * 49 = 784
-    # workgroups, 3136 waves >= 8 * 256: the chunked-prefill shape runs unsplit.
+    # G = 6, D = 256: a tile is 128 consecutive (token, head) columns, so
+    # 1024 query tokens are 1024 * 6 / 128 = 48 tiles (whole tokens per tile
+    # would need 49); 4 chunks -> 4 * 4 * 48 = 768 workgroups, 6144 waves
+    # >= 8 * 256: the chunked-prefill shape runs unsplit.
     p = _pv([3000, 5000, 8000, 2048], [1024] * 4, (24, 4, 256), bs=32, cu=256)
-    assert (p.kernel, p.partition_size, p.work_full_parts) == (vb.KERNEL_VARLEN_TILES, 0, 784)
+    assert (p.kernel, p.partition_size, p.work_full_parts) == (vb.KERNEL_VARLEN_TILES, 0, 768)
+    # tile counts at G = 6: ceil(q_len * 6 / 128) per sequence, times Hkv = 4
+    for ql, tiles in ((22, 2), (64, 3), (65, 4), (128, 6), (129, 7)):
+        p = _pv([5000], [ql], (24, 4, 256), bs=32, cu=1)
+        assert (p.kernel, p.partition_size, p.work_full_parts) == (vb.KERNEL_VARLEN_TILES, 0, 4 * tiles)
 
 
 def test_plan_varlen_auto_falls_back_under_the_scratch_cap():
