@@ -457,8 +457,11 @@ int32_t vk_select_decode_kernel(int32_t kernel);
  * 64 sequences (others run in grid order whatever the setting), and to the
  * multi-token column kernel's split launches when one tile holds every
  * sequence's queries (the same items; write-through partials come with it
- * there); it changes
- * which workgroup computes which partial, never a result.  Returns the
+ * there).  VK_ORDER_LONGEST_FIRST also puts unsplit LDS-tiled multi-token
+ * launches over at most 64 sequences in global longest-first order of their
+ * (sequence, tile) items (decreasing key range; VK_ORDER_AUTO keeps grid
+ * order there, measured faster).  It changes
+ * which workgroup computes which partial or row, never a result.  Returns the
  * previous setting, or -1 for an unknown value (setting kept).
  */
 int32_t vk_select_work_order(int32_t order);

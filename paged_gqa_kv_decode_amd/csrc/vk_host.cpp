@@ -649,6 +649,14 @@ static vk_status varlen_impl(int32_t dtype, const void* q, const void* k_cache, 
         a.work_order = 1;
         a.write_through = 1;
     }
+    // The LDS-tiled kernel, unsplit, over <= 64 sequences, on request only:
+    // its items in global longest-first order (decreasing key range).  Grid
+    // order stays the default: on the chunked prefill of 4 x 1024 tokens
+    // (768 workgroups) longest-first measured 1049 vs 1007 us on MI355X — it
+    // spreads each (sequence, KV head)'s tiles over the XCDs, whose L2s the
+    // grid order's runs of 8 share, and that outweighed the better balance.
+    if (tiled && partition_size == 0 && num_seqs <= 64 && t_order_choice == VK_ORDER_LONGEST_FIRST)
+        a.work_order = 1;
     va.cu_q = cu_seqlens_q;
     va.tiles = (int32_t)tiles;
     const dim3 grid((unsigned)gx, (unsigned)num_kv_heads, (unsigned)num_seqs);

@@ -170,3 +170,51 @@ def test_tiles_device_side_guards(tiles, P):
     # sequence 3: L = 4, q_len = 6: rows 0, 1 see nothing, rows 2.. see 1..4 tokens
     assert np.all(o[c[3]:c[3] + 2] == 0.0)
     assert np.all(np.isfinite(o[c[3] + 2:c[4]]))
+
+
+@pytest.mark.parametrize("geom", [(24, 4, 256), (32, 8, 128), (16, 1, 128), (16, 16, 128)])
+def test_tiles_longest_first_matches_grid_order(orc, tiles, geom):
+    """Unsplit LDS-tiled launches over <= 64 sequences can take their
+    (sequence, tile) items in global longest-first order (on request; grid
+    order is the default), found on the device from the launch index.  Every workgroup computes what it computes in grid order,
+    so the two orders give bit-identical outputs, each within the oracle's
+    bar.  Query runs sit around the 128-column tile edges (at G = 6 a
+    22-token run's two tiles end on the same token), with an empty run and a
+    one-key sequence; above 64 sequences the launch keeps grid order."""
+    Hq, Hkv, D = geom
+    lens = [700, 3000, 129, 1, 500, 2200, 64, 900, 1500, 40]
+    qlens = [22, 300, 129, 1, 0, 64, 43, 128, 65, 21]
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=Hq, num_kv_heads=Hkv,
+                            head_dim=D, block_size=16, seed=Hq + D + 5, canaries=True)
+    ref = oracle_varlen(orc, wl)
+    outs = {}
+    for order in (vb.ORDER_GRID, vb.ORDER_LONGEST_FIRST):
+        prev = vb.select_work_order(order)
+        try:
+            outs[order], plan, _ = run_varlen(wl, 0)
+            ran = vb.last_plan().work_order
+        finally:
+            vb.select_work_order(prev)
+        assert plan.kernel == vb.KERNEL_VARLEN_TILES and ran == order
+        say(f"[tiles] {geom} order={order}")
+        assert_parity(outs[order], ref, f"tiles {geom} order {order}", dtype="f16_tiles")
+    assert np.array_equal(outs[vb.ORDER_GRID], outs[vb.ORDER_LONGEST_FIRST])
+    # auto keeps grid order for the tiled kernel
+    gpu, _, _ = run_varlen(wl, 0)
+    assert vb.last_plan().work_order == vb.ORDER_GRID
+    assert np.array_equal(gpu, outs[vb.ORDER_GRID])
+
+
+def test_tiles_over_64_sequences_keep_grid_order(orc, tiles):
+    lens = [300 + 37 * (s % 11) for s in range(70)]
+    qlens = [1 + (s * 7) % 40 for s in range(70)]
+    wl = make_varlen_custom(seq_lens=lens, q_lens=qlens, num_q_heads=24, num_kv_heads=4,
+                            head_dim=256, block_size=32, seed=77)
+    prev = vb.select_work_order(vb.ORDER_LONGEST_FIRST)
+    try:
+        gpu, plan, _ = run_varlen(wl, 0)
+        ran = vb.last_plan().work_order
+    finally:
+        vb.select_work_order(prev)
+    assert plan.kernel == vb.KERNEL_VARLEN_TILES and ran == vb.ORDER_GRID
+    assert_parity(gpu, oracle_varlen(orc, wl), "tiles 70 sequences", dtype="f16_tiles")
