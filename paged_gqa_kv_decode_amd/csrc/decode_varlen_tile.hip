@@ -331,9 +331,25 @@ struct TileKernel {
                 pack_bf16_split(p[2], p[3], pb[cb].y, pl[cb].y);
                 pack_bf16_split(p[4], p[5], pb[cb].z, pl[cb].z);
                 pack_bf16_split(p[6], p[7], pb[cb].w, pl[cb].w);
+            } else if constexpr (kSplitMode == 0) {
+                // the rounded weights (round to nearest even) and their sum:
+                // v_dot2_f32_f16 of each packed pair with (1, 1) adds the two
+                // fp16 values exactly as converted back to fp32 (four
+                // instructions instead of eight conversions each way and
+                // eight adds)
+                typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+                const half2_t one2 = {(_Float16)1.f, (_Float16)1.f};
+                pb[cb].x = pack_half2(p[0], p[1]);
+                pb[cb].y = pack_half2(p[2], p[3]);
+                pb[cb].z = pack_half2(p[4], p[5]);
+                pb[cb].w = pack_half2(p[6], p[7]);
+                float hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].x), one2, 0.f, false);
+                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].y), one2, hs, false);
+                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].z), one2, hs, false);
+                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].w), one2, hs, false);
+                s_hi[cb] = s_full[cb] = hs;
             } else {
-                // the rounded weights, their sum and (unless never taken) the
-                // rounded residuals
+                // the rounded weights, their sum and the rounded residuals
                 float h[8];
                 float hs = 0.f, fs = 0.f;
 #pragma unroll
