@@ -16,11 +16,12 @@
 
 #define VK_PARTITION_LARGE 512
 #define VK_PARTITION_SMALL 256
-/* Multi-token calls only (vk_plan_varlen, vk_paged_gqa_varlen*): a third,
- * larger partition, which the planner picks for verification-shaped batches
- * (several query tokens per sequence, one column tile each) when its full
- * partitions alone reach the work budget.  An MI355X addition: half the
- * partials of 512 and half the (partition, KV head) launch items. */
+/* A third, larger partition (an MI355X addition: half the partials of 512).
+ * vk_plan_partitions upgrades 512 to it when the 512-token launch would run
+ * one wave per partition in a single round of the wave slots (the 1024-token
+ * partitions then take two waves of 512 tokens each: the same waves, half
+ * the partials); vk_plan_varlen tries it first for column tiles of several
+ * query tokens.  Every split entry point accepts it. */
 #define VK_PARTITION_XLARGE 1024
 
 #define VK_DEFAULT_BUDGET_PER_CU 33

@@ -128,7 +128,7 @@ enum {
 };
 
 typedef struct vk_plan {
-    int32_t  partition_size;     /* 0 = unsplit, else 256 or 512 (multi-token calls: or 1024) */
+    int32_t  partition_size;     /* 0 = unsplit, else 256, 512 or 1024 */
     int32_t  max_num_partitions; /* NP = ceil(max_s L_s / P); 1 when unsplit */
     int64_t  work_full_parts;    /* W(P) = Hq * sum_s floor(L_s / P) at the chosen P */
     int64_t  budget;             /* budget_per_cu * cu_count */
@@ -149,8 +149,14 @@ typedef struct vk_plan {
  * design notes): budget B = budget_per_cu * cu_count.  Work W(P) =
  * Hq * sum_s floor(L_s / P) counts only full partitions.  With
  * partition_request == -1 the planner picks P = 512 when W(512) >= B, else
- * P = 256; 0 asks for the unsplit path; 256 or 512 forces that size.
- * NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
+ * P = 256.  Then, not from the pages (an MI355X addition): 512 becomes
+ * VK_PARTITION_XLARGE = 1024 when the 512 launch would hold one wave per
+ * partition in a single round of the device's 8 * cu_count resident waves
+ * (2 * S * Hkv * ceil(max L / 512) > 8 * cu_count) and the 1024 launch, two
+ * waves of 512 tokens per partition, fits one round too
+ * (2 * S * Hkv * ceil(max L / 1024) <= 8 * cu_count): the same waves, half
+ * the partials.  0 asks for the unsplit path; 256, 512 or 1024 forces that
+ * size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
  * exceed the cap (no fallback path exists).
  *
  *   seq_lens_host       host int32 [num_seqs], each in [1, max_blocks_per_seq*block_size]
@@ -175,7 +181,7 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs,
  * partition_size == 0 (unsplit): each workgroup covers a whole sequence and
  *   writes out[s, h, :] directly; max_logits/exp_sums/tmp_out may be NULL and
  *   max_num_partitions must be 1.
- * partition_size == 256 or 512 (split): partition i covers tokens
+ * partition_size == 256, 512 or 1024 (split): partition i covers tokens
  *   [i*P, min(L, (i+1)*P)); for each i < ceil(L/P) it writes
  *     max_logits[s,h,i] = max over the partition of z_t * log2(e)
  *     exp_sums[s,h,i]   = sum over the partition of 2^(z_t*log2(e) - max)
@@ -224,7 +230,7 @@ vk_status vk_paged_gqa_decode_dt(int32_t dtype, const void* q, const void* k_cac
  *     M = max_i max_logits[i];  w_i = exp_sums[i] * 2^(max_logits[i] - M)
  *     out[s,h,:] = sum_i w_i * tmp_out[i,:] / sum_i w_i
  * reading only i < n (n == 1 copies tmp_out[0] exactly).  L <= 0 writes
- * zeros.  head_dim must be 128 or 256; partition_size 256 or 512.
+ * zeros.  head_dim must be 128 or 256; partition_size 256, 512 or 1024.
  */
 vk_status vk_paged_gqa_reduce(const float* max_logits, const float* exp_sums,
                               const float* tmp_out, const int32_t* seq_lens, int32_t num_seqs,
@@ -284,7 +290,7 @@ vk_status vk_paged_gqa_decode_fused(const void* q, const void* k_cache, const vo
  * Arguments are those of vk_paged_gqa_decode without the three scratch
  * pointers; `out` (fp32 [num_seqs, num_q_heads, head_dim]) is always required
  * and receives the final normalised result.  partition_size 0 runs the
- * unsplit decode into out (no scratch); 256 or 512 writes the partials into
+ * unsplit decode into out (no scratch); 256, 512 or 1024 writes the partials into
  * the array and merges them into out.  The partials (num_seqs * num_q_heads *
  * max_num_partitions * (head_dim + 2) * 4 bytes, plus alignment) must fit
  * VK_NOALLOC_SCRATCH_BYTES (64 MiB, vk_constants.h): larger calls return
@@ -326,7 +332,9 @@ vk_status vk_paged_gqa_decode_noalloc(const void* q, const void* k_cache, const 
  * sizes tried are 512 and, for column tiles when some sequence brings more
  * than one query token, first VK_PARTITION_XLARGE = 1024 (an MI355X
  * addition: half the partials of 512); with one query token per sequence
- * the two planners agree.  When that split's scratch would exceed the cap,
+ * the two planners agree, except where vk_plan_partitions upgrades 512 to
+ * 1024 for two-wave partitions (the column kernel keeps 512).  When that
+ * split's scratch would exceed the cap,
  * the next larger size, and failing that unsplit.  partition_request may
  * force 256, 512 or 1024.
  * NP = ceil(max L / P); scratch = total_q * Hq * NP * (D + 2) * 4 bytes

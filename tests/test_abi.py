@@ -61,7 +61,7 @@ def _c_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu=0, cap=0):
 
 def _o_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu=0, cap=0):
     try:
-        return oracle.plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap)
+        return oracle.plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu, cap, wave_slots_per_cu=8)
     except oracle.PlanError as e:
         return e.code
 
@@ -78,7 +78,7 @@ def test_planner_matches_oracle_rule_random():
         hi = int(rng.choice([300, 3000, 40000, 200000]))
         lens = rng.integers(1, hi, size=S).tolist()
         mb = -(-max(lens) // bs) + int(rng.integers(0, 3))
-        req = int(rng.choice([-1, -1, -1, 0, 256, 512]))
+        req = int(rng.choice([-1, -1, -1, 0, 256, 512, 1024]))
         cu = int(rng.choice([1, 8, 80, 256, 304]))
         per_cu = int(rng.choice([0, 0, 1, 33, 64]))
         cap = int(rng.choice([0, 0, 1 << 20, 64 << 20]))
@@ -90,9 +90,25 @@ def test_planner_matches_oracle_rule_random():
 
 
 def test_planner_long_context_decisions():
-    # 4 x 131072 tokens (16q, 2kv, 256), bs 32 on 256 CUs: W(512) = 16384 >= 8448.
+    # 4 x 131072 tokens (16q, 2kv, 256), bs 32 on 256 CUs: W(512) = 16384 >= 8448
+    # -> 512; its 4 * 2 * 256 = 2048 workgroups would fill the 2048 wave slots
+    # (8 per CU) once with one wave each, and 4 * 2 * 128 = 1024 workgroups of
+    # two waves over 1024-token partitions fill them too -> 1024,
+    # W(1024) = 16 * 4 * 128.
     p = vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 256)
-    assert (p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget) == (512, 256, 16384, 8448)
+    assert (p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget) == (1024, 128, 8192, 8448)
+    # 304 CUs (2432 slots): 2 * 2048 > 2432 and 2 * 1024 <= 2432 -> 1024
+    assert vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 304).partition_size == 1024
+    # 32 x 16k (24q, 4kv, 256): 1024-token workgroups 32 * 4 * 16 = 2048, two
+    # waves each > 2048 slots -> stays at 512 (several rounds: longest first)
+    assert vb.plan_partitions([16384] * 32, 24, 4, 256, 32, 512, -1, 256).partition_size == 512
+    # both sides of the regime on 1 CU (8 slots), budget 1 per CU, Hkv = 2:
+    # 2 * 2 * ceil(L / 512) > 8 and 2 * 2 * ceil(L / 1024) <= 8 <=> 1024 < L <= 2048
+    for L, P in ((1024, 512), (1025, 1024), (2048, 1024), (2049, 512)):
+        assert vb.plan_partitions([L], 16, 2, 128, 16, 129, -1, 1, 1).partition_size == P, L
+    # a forced 1024 is taken as it is
+    p = vb.plan_partitions([5000, 3000], 32, 8, 128, 16, 313, 1024, 256)
+    assert (p.partition_size, p.max_num_partitions) == (1024, 5)
     # 8 seqs up to 2048 tokens: too few full 512 partitions -> 256.
     p = vb.plan_partitions([2048, 1, 100, 1500, 2000, 512, 513, 7], 32, 8, 128, 16, 128, -1, 256)
     assert p.partition_size == 256 and p.max_num_partitions == 8
@@ -150,7 +166,7 @@ def _decode(**kw):
     (dict(Hq=24, Hkv=8), "GEOMETRY"), (dict(Hq=16, Hkv=2, D=64), "GEOMETRY"),
     (dict(bs=64), "BLOCK_SIZE"), (dict(P=128), "PARTITION"), (dict(P=512, NP=0), "PARTITION"),
     (dict(P=0, NP=2), "PARTITION"), (dict(P=512, NP=5_000_000), "PARTITION"),
-    (dict(mb=200_000_000), "BAD_DIM"), (dict(P=1024), "PARTITION"),
+    (dict(mb=200_000_000), "BAD_DIM"), (dict(P=768), "PARTITION"),
 ])
 def test_decode_validation(kw, code):
     assert _decode(**kw) == CODES[code]
@@ -180,7 +196,7 @@ def test_reduce_validation():
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 96, 512, 4, FAKE, None) == CODES["GEOMETRY"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 0, 4, FAKE, None) == CODES["PARTITION"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 0, FAKE, None) == CODES["PARTITION"]
-    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 1024, 4, FAKE, None) == CODES["PARTITION"]
+    assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 768, 4, FAKE, None) == CODES["PARTITION"]
     assert R(FAKE, FAKE, FAKE + 4, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
     assert R(FAKE, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE + 8, None) == CODES["ALIGN"]
     assert R(FAKE + 2, FAKE, FAKE, FAKE, 1, 32, 128, 512, 4, FAKE, None) == CODES["ALIGN"]
@@ -290,12 +306,17 @@ def test_plan_varlen_large_partition_at_the_budget(columns):
     assert (p.partition_size, p.work_full_parts, p.budget) == (512, 528, 528)
     p = _pv([33 * 512 - 1], [2], (16, 2, 256), bs=32, cu=16)
     assert (p.partition_size, p.work_full_parts) == (256, 16 * 65)
-    # one query token per sequence: the decode planner's choice
+    # one query token per sequence: the decode planner's choice, except its
+    # one-round upgrade to 1024 (two waves per partition, which the one-wave
+    # column kernel does not have): there 512
     for lens in ([8192, 4096], [1023, 600], [33 * 512], [33 * 512 - 1]):
         for cu in (1, 16):
             a = _pv(lens, [1] * len(lens), (16, 2, 256), bs=32, cu=cu)
             d = vb.plan_partitions(np.array(lens, dtype=np.int32), 16, 2, 256, 32, 600, -1, cu)
-            assert (a.partition_size, a.work_full_parts) == (d.partition_size, d.work_full_parts)
+            if d.partition_size == 1024:
+                assert (a.partition_size, a.work_full_parts) == (512, 16 * sum(L // 512 for L in lens))
+            else:
+                assert (a.partition_size, a.work_full_parts) == (d.partition_size, d.work_full_parts)
     # 16 * (4 + 2) = 96 full 1024-token units >= 33
     p = _pv([4096, 2048], [2, 2], (16, 2, 256), bs=32, cu=1)
     assert (p.partition_size, p.max_num_partitions) == (1024, 4)
@@ -335,10 +356,8 @@ def test_plan_varlen_xlarge_partition_rule(columns):
     assert (p.partition_size, p.max_num_partitions) == (1024, 2)
     p = _pv([1500, 1500], [4, 4], (32, 8, 128), cu=3, cap=8 * 32 * 2 * 130 * 4 - 1)
     assert p.partition_size == 0
-    # the decode planner does not take it
-    with pytest.raises(vb.VkError) as e:
-        vb.plan_partitions(np.array([4096], dtype=np.int32), 32, 8, 128, 16, 256, 1024, 4)
-    assert e.value.name == "PARTITION"
+    # the decode planner takes 1024 only when asked, or in its one-round regime
+    assert vb.plan_partitions(np.array([4096], dtype=np.int32), 32, 8, 128, 16, 256, 1024, 4).partition_size == 1024
 
 
 @pytest.mark.parametrize("lens,qlens,name", [([100, 50], [101, 1], "SEQ_LEN"),

@@ -148,7 +148,7 @@ def test_fused_all_specialisations_ragged(orc, geom, bs, kernel):
                      seed=Hq * 1000 + D + bs + 7, pool_factor=1.7, canaries=True,
                      extra_blocks_per_seq=2, sigma_k=2.0)
     ref = orc.paged_attention(wl)
-    for P in (256, 512):
+    for P in (256, 512, 1024):
         gpu, _, _, _ = run_hip(wl, P, kernel=kernel, fused=True)
         assert_parity(gpu, ref, f"fused {geom} bs{bs} P{P}")
 

@@ -41,8 +41,8 @@ def test_named_workload_parity(orc, name, P, kernel):
     wl = named(name)
     ref = oracle_ref(orc, name)
     gpu, plan, last, _ = run_hip(wl, P, kernel=kernel)
-    if P == -1:
-        assert plan.partition_size == 512, "planner should pick 512 for 4 x 131072 tokens"
+    if P == -1:   # one round of two-wave 1024-token partitions on 256 CUs
+        assert plan.partition_size == 1024, "planner should pick 1024 for 4 x 131072 tokens"
     if kernel == vb.KERNEL_MFMA_W4P2 and plan.partition_size == 0:
         assert last.kernel == vb.KERNEL_MFMA_W4    # two partitions per workgroup need a split
     else:
@@ -52,7 +52,8 @@ def test_named_workload_parity(orc, name, P, kernel):
 
 @pytest.mark.parametrize("kernel", [vb.KERNEL_DOT, vb.KERNEL_MFMA_W1, vb.KERNEL_MFMA_W4,
                                     vb.KERNEL_MFMA_W4P2])
-@pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512), ("long32_16k", 256)])
+@pytest.mark.parametrize("name,P", [("batch8_2k", 512), ("mixed64_32k", 512), ("long32_16k", 256),
+                                    ("batch8_2k", 1024), ("mixed64_32k", 1024)])
 def test_partials_match_oracle(orc, name, P, kernel):
     say(f"[partials] {name} P={P} kernel={kernel}")
     wl = named(name)
@@ -317,7 +318,7 @@ def test_work_orders_bit_identical(orc, geom, bs, S, kernel, fused):
     wl = make_custom(seq_lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                      seed=Hq + D + bs + S, pool_factor=1.3, canaries=True, sigma_k=2.0)
     ref = orc.paged_attention(wl)
-    for P in (256, 512):
+    for P in (256, 512, 1024):
         a, _, la, pa = run_hip(wl, P, kernel=kernel, keep_partials=True, fused=fused,
                                order=vb.ORDER_GRID)
         b, _, lb, pb = run_hip(wl, P, kernel=kernel, keep_partials=True, fused=fused,

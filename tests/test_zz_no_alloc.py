@@ -54,7 +54,7 @@ def test_noalloc_matches_decode_and_reduce(orc, P):
 
 
 def test_noalloc_named_long_context_workload(orc):
-    """long4_128k at the planner's partition size (16.9 MB of partials):
+    """long4_128k at the planner's partition size (1024 on 256 CUs: 8.5 MB of partials):
     bit-identical to decode + reduce."""
     from gpu_helpers import named
     wl = named("long4_128k")
