@@ -388,8 +388,11 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         kernel = 2 * wgs <= slots ? VK_KERNEL_MFMA_W4 : wgs <= slots ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2;
         // 1024-token partitions in one round of two waves each (the
         // planner's choice in place of one wave per 512): 512 tokens per wave.
+        // fp32 at head dim 256 holds one wave per SIMD (half the slots the
+        // planner counts): one wave per 1024-token partition keeps that one
+        // round (two waves per partition measured 514 vs 365 us at 512).
         if (partition_size == VK_PARTITION_XLARGE && 2 * wgs <= slots && 4 * wgs > slots)
-            kernel = VK_KERNEL_MFMA_W2;
+            kernel = (dtype == VK_DTYPE_F32 && head_dim == 256) ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2;
     }
     a.work_order = 0;
     a.write_through = 0;

@@ -67,7 +67,7 @@ def test_element_types_decode(orc, geom, bs, kernel, dtype):
     wl = make_custom(seq_lens=LENS, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                      seed=Hq + D + bs, pool_factor=1.5, canaries=True, sigma_k=2.0, dtype=dtype)
     ref = orc.paged_attention(wl)
-    for P in (0, 512):
+    for P in (0, 512, 1024):
         gpu, _, last, _ = run_hip(wl, P, kernel=kernel)
         assert_parity(gpu, ref, f"{dtype} {geom} P{P} kernel {last.kernel}", dtype=dtype)
 
