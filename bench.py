@@ -265,9 +265,10 @@ def cpu_baseline_varlen(wl, min_seconds: float, max_seconds: float, flops_unit: 
             "seconds": round(total, 3)}
 
 
-def bench_varlen(args, wl, gen_s):
+def bench_varlen(args, wl, gen_s, emit=True):
     """Several query tokens per sequence: plan (host) + the multi-token kernel
-    (+ its reduce when split) per step, pools rotated as for the decode."""
+    (+ its reduce when split) per step, pools rotated as for the decode.
+    Prints the JSON line (with the CPU baseline) when `emit`, and returns it."""
     import numpy as np
     import torch
     from paged_gqa_kv_decode_amd import binding as vb
@@ -368,10 +369,12 @@ def bench_varlen(args, wl, gen_s):
         "kv_read_bytes": kv_bytes, "causal_flops": flops, "kv_pool_copies": ncopies,
         "input_gen_s": round(gen_s, 1),
     }
-    result["cpu_baseline"] = (None if args.no_cpu_baseline else
-                              cpu_baseline_varlen(wl, args.cpu_seconds, 3 * args.cpu_seconds,
-                                                  compute_bound))
-    print(json.dumps(result), flush=True)
+    if emit:
+        result["cpu_baseline"] = (None if args.no_cpu_baseline else
+                                  cpu_baseline_varlen(wl, args.cpu_seconds, 3 * args.cpu_seconds,
+                                                      compute_bound))
+        print(json.dumps(result), flush=True)
+    return result
 
 
 ORDER_NAMES = {1: "grid", 2: "longest_first"}
@@ -844,6 +847,27 @@ def main():
             print(f"bench: {name} P={p_req}: decode {t2['kernel_us']['decode_mean']} us "
                   f"({configs[f'{name}_P{p_req}']['frac']:.3f} of peak)", file=sys.stderr,
                   flush=True)
+        # The multi-token workloads (verification rows, a chunked prefill),
+        # timed as `--workload <name>` would, planner and kernel choice auto.
+        import copy
+        import torch
+        from paged_gqa_kv_decode_amd.workloads import make_varlen
+        for name in VARLEN:
+            a3 = copy.copy(args)
+            a3.partition, a3.varlen_kernel, a3.order, a3.dtype = None, "auto", "auto", "f16"
+            r3 = bench_varlen(a3, make_varlen(name), 0.0, emit=False)
+            torch.cuda.empty_cache()
+            roof = r3["roofline"]
+            configs[name] = {
+                "partition_size": r3["config"]["partition_size"],
+                "kernel": r3["config"]["decode_kernel"],
+                "kernel_us_mean": r3["kernel_us"]["varlen_mean"],
+                "reduce_us_median": r3["kernel_us"]["reduce_median"],
+                "us_per_step": r3["us_per_step"],
+                "bound": roof["bound"], "rate": roof["achieved"], "rate_unit": roof["unit"],
+                "frac": roof["frac"]}
+            print(f"bench: {name}: kernel {r3['kernel_us']['varlen_mean']} us "
+                  f"({roof['frac']:.3f} of the {roof['bound']} peak)", file=sys.stderr, flush=True)
         result["configs"] = configs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, 3 * args.cpu_seconds)
