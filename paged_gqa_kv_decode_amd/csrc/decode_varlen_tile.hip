@@ -11,7 +11,7 @@
 // of one (sequence, KV head) — columns are (token, head) pairs in token-major
 // order, so a workgroup covers 128 / G query tokens and, where G does not
 // divide 128, runs across token boundaries — and streams the keys through LDS
-// in 32-key tiles: each tile is fetched once per workgroup and serves all 128
+// in 64-key tiles: each tile is fetched once per workgroup and serves all 128
 // columns.  At G = 6, 1024 query tokens are then exactly 48 workgroups (whole
 // tokens per workgroup would take 49, the last one partial; on the chunked
 // prefill of 4 x 1024 tokens that is 768 workgroups, three full rounds of the
@@ -19,7 +19,11 @@
 //
 //  * Loads: the tile's K and V go straight from the paged cache into LDS
 //    (global_load_lds_dwordx4: lane l's 16 bytes land at slot base + 16 l),
-//    four buffers, tiles t + 1 .. t + 3 in flight while tile t is computed.
+//    two buffers, tile t + 1 in flight while tile t is computed (a build
+//    option takes 32-key tiles through four buffers, three in flight; at
+//    D = 256 either fills 128 KiB).  Measured on MI355X, 64-key tiles: chunked
+//    prefill fp16 1046 -> 958 us, bf16 1198 -> 1118 us (half the barriers and
+//    per-tile softmax reductions); D = 128 unsplit verification 501 -> 392 us.
 //    K: a slot is one matrix-core operand register of the whole wave, so
 //    every K read is one conflict-free ds_read_b128 of 1 KiB; K slot
 //    (kb, kk): lane (i, c) holds K[16 kb + i][32 kk + 8 c, +8).  V: rows in
@@ -34,8 +38,8 @@
 //    rare tiles that move it.
 //  * Waves whose columns see none of a tile's keys skip its arithmetic but
 //    still take part in its loads and barriers.
-//  * Page ids of a tile go into a per-wave LDS ring three tiles ahead of its
-//    K/V loads.
+//  * Page ids of a tile go into a per-wave LDS ring NBUF - 1 tiles ahead of
+//    its K/V loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +51,9 @@
 #endif
 #ifndef VK_TILE_PV_AHEAD
 #define VK_TILE_PV_AHEAD 4         // PV: V reads kept this many products ahead (0: compiler's order)
+#endif
+#ifndef VK_TILE_KEYS
+#define VK_TILE_KEYS 64            // keys per tile: 64 (two LDS buffers) or 32 (four)
 #endif
 #ifndef VK_TILE_SPLIT_WEIGHTS
 #define VK_TILE_SPLIT_WEIGHTS 0    // fp16 residual PV product: 0 never, 1 on heavy tiles, 2 always
@@ -74,23 +81,28 @@ struct TileKernel {
     static constexpr int CB = tile_blocks(D);    // 16-column blocks per wave
     static constexpr int NW = tile_waves(D);     // waves per workgroup
     static constexpr int NC = NW * CB * 16;      // columns per workgroup (128)
-    static constexpr int KT = 32;                // keys per tile
+    static constexpr int KT = VK_TILE_KEYS;      // keys per tile
+    static constexpr int KB = KT / 16;           // 16-key blocks per tile
+    static constexpr int KH = KT / 32;           // 32-key PV steps per tile
     static constexpr int NKC = D / 32;           // QK k-chunks of 32 dims
     static constexpr int NDH = D / 128;          // 128-dim halves of a V row
     static constexpr int NACC = D / 16;          // PV output tiles per column block (dims 16 m + 4 c + rr)
-    static constexpr int KSLOTS = 2 * NKC;       // [key block][dim chunk]
-    static constexpr int VSLOTS = 8 * NDH;       // V: 32 rows of 2D bytes
+    static constexpr int KSLOTS = KB * NKC;      // [key block][dim chunk]
+    static constexpr int VSLOTS = (KT / 4) * NDH;   // V: KT rows of 2D bytes
     static constexpr int SLOTS = KSLOTS + VSLOTS;
     static constexpr int RB = 2 * D;             // bytes of a V row
     static constexpr int RPI = 1024 / RB;        // V rows per slot
     static constexpr int CPR = RB / 16;          // 16-byte chunks of a V row
     static constexpr int BUF = SLOTS * 1024;     // bytes of one tile in LDS
     static constexpr int NPG = KT / BS;          // pages per tile
-    static constexpr int NBUF = 4;               // tiles in LDS: 3 in flight while 1 is computed
+    // tiles in LDS: with 32 keys 3 in flight while 1 is computed, with 64
+    // keys 1 (both 128 KiB at D = 256)
+    static constexpr int NBUF = KT == 32 ? 4 : 2;
     static constexpr int ISSUE = SLOTS / NW;     // loads into LDS per wave and tile
     static_assert(KSLOTS % NW == 0 && VSLOTS % NW == 0, "slots split evenly over the waves");
     static_assert(RPI <= BS, "the rows of a V slot sit in one page");
     static_assert(BS <= KT && KT % BS == 0, "a tile covers whole pages");
+    static_assert(KT == 32 || KT == 64, "tile of 32 or 64 keys");
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
     // Per column: m is the running max score (log2 units); the weights are
@@ -277,27 +289,32 @@ struct TileKernel {
     static __device__ __forceinline__ void compute(const DecodeArgs& a, Col (&st)[CB], const char* lb,
                                                    const uint4 (&qb)[CB][NKC], const int (&rem)[CB],
                                                    const int (&voff)[8], int lane, int c) {
-        floatx4 sc[CB][2];
+        floatx4 sc[CB][KB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sc[cb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKC; ++kk) {
-            const uint4 k0 = lds16(lb, kk, lane);
-            const uint4 k1 = lds16(lb, NKC + kk, lane);
+            uint4 kv[KB];
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                sc[cb][0] = qk_mma(k0, qb[cb][kk], sc[cb][0]);
-                sc[cb][1] = qk_mma(k1, qb[cb][kk], sc[cb][1]);
-            }
+            for (int kb = 0; kb < KB; ++kb) kv[kb] = lds16(lb, kb * NKC + kk, lane);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sc[cb][kb] = qk_mma(kv[kb], qb[cb][kk], sc[cb][kb]);
         }
-        uint4 pb[CB], pl[CB];   // weights and their residuals
+        // weights and their residuals, per 32-key PV step h: keys 32 h + 4c + e,
+        // then 32 h + 16 + 4c + e
+        uint4 pb[CB][KH], pl[CB][KH];
         float s_hi[CB], s_full[CB];   // fp16: the lane's sum of the rounded / exact weights
         bool heavy = false;           // fp16: some column block of this lane needs the residual
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            float x[8];
+            constexpr int NX = 4 * KB;
+            float x[NX];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float v = mul_rounded(sc[cb][kb][r], a.scale_log2e);
@@ -305,7 +322,7 @@ struct TileKernel {
                 }
             float mx = x[0];
 #pragma unroll
-            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+            for (int j = 1; j < NX; ++j) mx = fmaxf(mx, x[j]);
             mx = max_rows4(mx);
             const float mnew = fmaxf(st[cb].m, mx);
             st[cb].m = mnew;
@@ -319,18 +336,22 @@ struct TileKernel {
                 for (int t = 0; t < NACC; ++t) st[cb].acc[t] *= alpha;
             }
             const float rref = (st[cb].r == -INFINITY) ? 0.f : st[cb].r;
-            float p[8];
+            float p[NX];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(x[j] - rref) * kPScale;
+            for (int j = 0; j < NX; ++j) p[j] = exp2_fast(x[j] - rref) * kPScale;
             if constexpr (DT == 1) {
                 float ps = 0.f;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) ps += p[j];
+                for (int j = 0; j < NX; ++j) ps += p[j];
                 st[cb].l += ps;
-                pack_bf16_split(p[0], p[1], pb[cb].x, pl[cb].x);
-                pack_bf16_split(p[2], p[3], pb[cb].y, pl[cb].y);
-                pack_bf16_split(p[4], p[5], pb[cb].z, pl[cb].z);
-                pack_bf16_split(p[6], p[7], pb[cb].w, pl[cb].w);
+#pragma unroll
+                for (int h = 0; h < KH; ++h) {
+                    const float* ph = p + 8 * h;
+                    pack_bf16_split(ph[0], ph[1], pb[cb][h].x, pl[cb][h].x);
+                    pack_bf16_split(ph[2], ph[3], pb[cb][h].y, pl[cb][h].y);
+                    pack_bf16_split(ph[4], ph[5], pb[cb][h].z, pl[cb][h].z);
+                    pack_bf16_split(ph[6], ph[7], pb[cb][h].w, pl[cb][h].w);
+                }
             } else if constexpr (kSplitMode == 0) {
                 // the rounded weights (round to nearest even) and their sum:
                 // v_dot2_f32_f16 of each packed pair with (1, 1) adds the two
@@ -339,36 +360,47 @@ struct TileKernel {
                 // eight adds)
                 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
                 const half2_t one2 = {(_Float16)1.f, (_Float16)1.f};
-                pb[cb].x = pack_half2(p[0], p[1]);
-                pb[cb].y = pack_half2(p[2], p[3]);
-                pb[cb].z = pack_half2(p[4], p[5]);
-                pb[cb].w = pack_half2(p[6], p[7]);
-                float hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].x), one2, 0.f, false);
-                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].y), one2, hs, false);
-                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].z), one2, hs, false);
-                hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb[cb].w), one2, hs, false);
+                float hs = 0.f;
+#pragma unroll
+                for (int h = 0; h < KH; ++h) {
+                    const float* ph = p + 8 * h;
+                    uint4& w = pb[cb][h];
+                    w.x = pack_half2(ph[0], ph[1]);
+                    w.y = pack_half2(ph[2], ph[3]);
+                    w.z = pack_half2(ph[4], ph[5]);
+                    w.w = pack_half2(ph[6], ph[7]);
+                    hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.x), one2, hs, false);
+                    hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.y), one2, hs, false);
+                    hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.z), one2, hs, false);
+                    hs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.w), one2, hs, false);
+                }
                 s_hi[cb] = s_full[cb] = hs;
             } else {
                 // the rounded weights, their sum and the rounded residuals
-                float h[8];
+                float h[NX];
                 float hs = 0.f, fs = 0.f;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < NX; ++j) {
                     h[j] = (float)(_Float16)p[j];
                     hs += h[j];
                     fs += p[j];
                 }
-                pb[cb].x = pack_half2(h[0], h[1]);
-                pb[cb].y = pack_half2(h[2], h[3]);
-                pb[cb].z = pack_half2(h[4], h[5]);
-                pb[cb].w = pack_half2(h[6], h[7]);
-                if constexpr (kSplitMode > 0) {
-                    pl[cb].x = pack_half2(p[0] - h[0], p[1] - h[1]);
-                    pl[cb].y = pack_half2(p[2] - h[2], p[3] - h[3]);
-                    pl[cb].z = pack_half2(p[4] - h[4], p[5] - h[5]);
-                    pl[cb].w = pack_half2(p[6] - h[6], p[7] - h[7]);
-                    heavy = heavy || hs >= kSplitShare * (st[cb].l + hs);
+#pragma unroll
+                for (int u = 0; u < KH; ++u) {
+                    const float* hu = h + 8 * u;
+                    const float* pu = p + 8 * u;
+                    pb[cb][u].x = pack_half2(hu[0], hu[1]);
+                    pb[cb][u].y = pack_half2(hu[2], hu[3]);
+                    pb[cb][u].z = pack_half2(hu[4], hu[5]);
+                    pb[cb][u].w = pack_half2(hu[6], hu[7]);
+                    if constexpr (kSplitMode > 0) {
+                        pl[cb][u].x = pack_half2(pu[0] - hu[0], pu[1] - hu[1]);
+                        pl[cb][u].y = pack_half2(pu[2] - hu[2], pu[3] - hu[3]);
+                        pl[cb][u].z = pack_half2(pu[4] - hu[4], pu[5] - hu[5]);
+                        pl[cb][u].w = pack_half2(pu[6] - hu[6], pu[7] - hu[7]);
+                    }
                 }
+                if constexpr (kSplitMode > 0) heavy = heavy || hs >= kSplitShare * (st[cb].l + hs);
                 s_hi[cb] = hs;
                 s_full[cb] = fs;
             }
@@ -380,8 +412,9 @@ struct TileKernel {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) st[cb].l += split ? s_full[cb] : s_hi[cb];
         }
-        // O^T += V^T P^T, 16 dims at a time: k-slots of lane group c are keys
-        // 4c + e, then 16 + 4c + e (the order of the weights in pb).  fp16:
+        // O^T += V^T P^T, 16 dims at a time: in 32-key step h the k-slots of
+        // lane group c are keys 32 h + 4c + e, then 32 h + 16 + 4c + e (the
+        // order of the weights in pb).  fp16:
         // the residual weights' product, on the tiles that need it, is a
         // second pass over V (its own loop: a branch among the products would
         // keep the compiler from scheduling them together).
@@ -396,27 +429,31 @@ struct TileKernel {
     }
 
     // PV of one tile: W = 0 the rounded weights, 1 the residuals, 2 both.
+    // The 32-key steps run outermost, so consecutive products update
+    // different accumulators.
     template <int W>
-    static __device__ __forceinline__ void pv(Col (&st)[CB], const char* lb, const uint4 (&pb)[CB],
-                                              const uint4 (&pl)[CB], const int (&voff)[8]) {
+    static __device__ __forceinline__ void pv(Col (&st)[CB], const char* lb, const uint4 (&pb)[CB][KH],
+                                              const uint4 (&pl)[CB][KH], const int (&voff)[8]) {
         const char* vb = lb + KSLOTS * 1024;
 #pragma unroll
-        for (int m = 0; m < NACC; ++m) {
-            const char* p = vb + voff[m & 7] + 256 * (m >> 3);
-            const uint2 lo = read_vt(p), hi = read_vt(p + 16 * RB);
-            const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int h = 0; h < KH; ++h)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                if constexpr (DT == 1) {
-                    st[cb].acc[m] = mfma32_bf16(av, pb[cb], st[cb].acc[m]);
-                    st[cb].acc[m] = mfma32_bf16(av, pl[cb], st[cb].acc[m]);
-                } else {
-                    if constexpr (W != 1) st[cb].acc[m] = mfma32(av, pb[cb], st[cb].acc[m]);
-                    if constexpr (W != 0) st[cb].acc[m] = mfma32(av, pl[cb], st[cb].acc[m]);
+            for (int m = 0; m < NACC; ++m) {
+                const char* p = vb + voff[m & 7] + 256 * (m >> 3) + 32 * h * RB;
+                const uint2 lo = read_vt(p), hi = read_vt(p + 16 * RB);
+                const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    if constexpr (DT == 1) {
+                        st[cb].acc[m] = mfma32_bf16(av, pb[cb][h], st[cb].acc[m]);
+                        st[cb].acc[m] = mfma32_bf16(av, pl[cb][h], st[cb].acc[m]);
+                    } else {
+                        if constexpr (W != 1) st[cb].acc[m] = mfma32(av, pb[cb][h], st[cb].acc[m]);
+                        if constexpr (W != 0) st[cb].acc[m] = mfma32(av, pl[cb][h], st[cb].acc[m]);
+                    }
                 }
             }
-        }
-        lds_ahead<NACC, 2, CB * ((DT == 1 || W == 2) ? 2 : 1), VK_TILE_PV_AHEAD>();
+        lds_ahead<KH * NACC, 2, CB * ((DT == 1 || W == 2) ? 2 : 1), VK_TILE_PV_AHEAD>();
     }
 
     // Page ids of the tile at k0 into a 256-byte LDS slot: lane k holds page
@@ -446,7 +483,8 @@ struct TileKernel {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     static __device__ __forceinline__ void wait_tile(int later_tiles) {
-        static_assert(NBUF == 4 && 2 * (ISSUE + 1) < 64, "vmcnt range");
+        // (two buffers: no later tile is in flight, later_tiles is 0)
+        static_assert((NBUF == 4 || NBUF == 2) && 2 * (ISSUE + 1) < 64, "vmcnt range");
         // each later tile: its page-id load and its K/V loads
         if (later_tiles >= 2)
             wait_vm<2 * (ISSUE + 1)>();

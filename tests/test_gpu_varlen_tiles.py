@@ -7,7 +7,7 @@ Same tolerance as the decode: max |gpu - ref| <= 2e-3 and per-row relative
 L2 <= 1e-2.  Every (G, D) instantiation and page size, unsplit and both
 partition sizes, with query runs shorter than, equal to and longer than a
 workgroup's 128 / G tokens, prefixes that put the causal diagonal off the
-32-key tiles, an empty sequence and canaries around every page.
+key tiles' boundaries, an empty sequence and canaries around every page.
 """
 import copy
 
