@@ -110,6 +110,41 @@ def test_tiles_agree_with_columns(orc):
     assert np.max(np.abs(out[vb.KERNEL_VARLEN_COLUMNS] - out[vb.KERNEL_VARLEN_TILES])) <= 2e-3
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiles_negative_and_zero_scale(orc, tiles, dtype):
+    """A negative scale and a zero scale (equal weights: the mean of the
+    visible V rows) against the oracle, unsplit and split; and (q, scale)
+    against (-q, -scale), which must give bit-identical rows (negating q
+    negates every score exactly, and the scaled scores are then equal)."""
+    from test_gpu_varlen_bf16 import oracle_bf16, run as run_bf16
+    for (Hq, Hkv, D), bs in (((24, 4, 256), 32), ((32, 8, 128), 16)):
+        wl = make_varlen_custom(seq_lens=[300, 1000, 77], q_lens=[90, 64, 70], num_q_heads=Hq,
+                                num_kv_heads=Hkv, head_dim=D, block_size=bs, seed=40 + D,
+                                dtype=dtype)
+
+        def run(w, P):
+            if dtype == "bf16":
+                return run_bf16(w, vb.KERNEL_VARLEN_TILES, P)
+            out, plan, _ = run_varlen(w, P)
+            assert plan.kernel == vb.KERNEL_VARLEN_TILES
+            return out
+
+        tol = "bf16" if dtype == "bf16" else "f16_tiles"
+        s0 = float(np.float32(1.0 / np.sqrt(D)))   # exact in fp32, as the kernel takes it
+        for scale in (-s0, 0.0):
+            wl.scale = scale
+            ref = oracle_bf16(orc, wl) if dtype == "bf16" else oracle_varlen(orc, wl)
+            for P in (0, 512):
+                say(f"[tiles scale] {dtype} D{D} scale {scale:+.4f} P{P}")
+                assert_parity(run(wl, P), ref, f"tiles {dtype} D{D} scale {scale:+.4f} P{P}",
+                              dtype=tol)
+        wl.scale = -s0
+        neg = copy.copy(wl)
+        neg.q = wl.q ^ np.uint16(0x8000) if dtype == "bf16" else -wl.q
+        neg.scale = s0
+        assert np.array_equal(run(wl, 0), run(neg, 0)), "(q, scale) and (-q, -scale) differ"
+
+
 def test_tiles_causality_is_structural(tiles):
     """Changing the K/V of the last token of every sequence leaves every row
     that does not see it bit-identical, and changes the last row."""
