@@ -21,6 +21,10 @@ still runs on the host every step.  Prints ONE JSON line:
                    (profiles/), null if the kernel sources changed since
   cpu_baseline     the float64 oracle on a bounded sample of the same workload,
                    on this host's cores
+  ceiling          this box's read ceilings on the workload's KV pools
+  configs          (default run) the other long-context decode workloads, each
+                   with its own read ceiling and the fraction of it reached,
+                   and the multi-token workloads, timed the same way
 
 Default workload: 4 sequences x 131072 tokens, (16 q, 2 kv, 256) heads,
 block 32, the planner choosing the partition size.
@@ -842,6 +846,14 @@ def main():
                 "frac": round(t2["achieved_GBps"] / HBM_PEAK_GBS, 4),
                 "decode_kernel": KERNEL_NAMES.get(t2["kernel"], str(t2["kernel"])),
                 "work_order": ORDER_NAMES.get(t2["order"], str(t2["order"]))}
+            if not args.no_ceiling:
+                # this workload's own read ceiling (its page size and page list)
+                c2 = ceilings(wl2, db2.dev, db2.P)
+                configs[f"{name}_P{p_req}"].update({
+                    "read_ceiling_GBps": c2["read_ceiling_GBps"],
+                    "read_ceiling_kernel": c2["read_ceiling_kernel"],
+                    "page_bytes": c2["page_bytes"],
+                    "of_ceiling": round(t2["achieved_GBps"] / c2["read_ceiling_GBps"], 4)})
             db2.release()
             del wl2
             print(f"bench: {name} P={p_req}: decode {t2['kernel_us']['decode_mean']} us "
