@@ -373,6 +373,11 @@ def bench_varlen(args, wl, gen_s, emit=True):
         "kv_read_bytes": kv_bytes, "causal_flops": flops, "kv_pool_copies": ncopies,
         "input_gen_s": round(gen_s, 1),
     }
+    if not compute_bound and not args.no_ceiling:
+        # an HBM-bound launch: this box's read ceilings on the workload's pools
+        result["ceiling"] = ceilings(wl, (q, k, v, bt, sl), P)
+        result["roofline"]["of_ceiling"] = round(roof["achieved"] /
+                                                 result["ceiling"]["read_ceiling_GBps"], 4)
     if emit:
         result["cpu_baseline"] = (None if args.no_cpu_baseline else
                                   cpu_baseline_varlen(wl, args.cpu_seconds, 3 * args.cpu_seconds,
@@ -878,6 +883,11 @@ def main():
                 "us_per_step": r3["us_per_step"],
                 "bound": roof["bound"], "rate": roof["achieved"], "rate_unit": roof["unit"],
                 "frac": roof["frac"]}
+            if "ceiling" in r3:
+                configs[name].update({"read_ceiling_GBps": r3["ceiling"]["read_ceiling_GBps"],
+                                      "read_ceiling_kernel": r3["ceiling"]["read_ceiling_kernel"],
+                                      "page_bytes": r3["ceiling"]["page_bytes"],
+                                      "of_ceiling": roof["of_ceiling"]})
             print(f"bench: {name}: kernel {r3['kernel_us']['varlen_mean']} us "
                   f"({roof['frac']:.3f} of the {roof['bound']} peak)", file=sys.stderr, flush=True)
         result["configs"] = configs
