@@ -59,7 +59,7 @@ def test_bf16_mixed_batch(orc, geom, bs, kernel):
                             canaries=True, sigma_k=2.0, dtype="bf16")
     assert wl.q.dtype == np.uint16
     ref = oracle_bf16(orc, wl)
-    for P in (0, 256):
+    for P in (0, 256, 1024):
         gpu = run(wl, kernel, P)
         say(f"[bf16 varlen] {geom} bs{bs} kernel {kernel} P{P}")
         assert_parity(gpu, ref, f"bf16 {geom} bs{bs} k{kernel} P{P}", dtype="bf16")

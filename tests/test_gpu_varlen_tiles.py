@@ -4,8 +4,8 @@ at D = 256, K/V tiles shared through LDS)
 against the float64 oracle.
 
 Same tolerance as the decode: max |gpu - ref| <= 2e-3 and per-row relative
-L2 <= 1e-2.  Every (G, D) instantiation and page size, unsplit and both
-partition sizes, with query runs shorter than, equal to and longer than a
+L2 <= 1e-2.  Every (G, D) instantiation and page size, unsplit and split in
+256-, 512- and 1024-token partitions, with query runs shorter than, equal to and longer than a
 workgroup's 128 / G tokens, prefixes that put the causal diagonal off the
 key tiles' boundaries, an empty sequence and canaries around every page.
 """
@@ -76,7 +76,7 @@ def test_tiles_all_specialisations(orc, tiles, geom, bs):
                             head_dim=D, block_size=bs, seed=Hq * 7 + D + bs, pool_factor=1.5,
                             canaries=True, sigma_k=2.0)
     ref = oracle_varlen(orc, wl)
-    for P in (0, 256, 512):
+    for P in (0, 256, 512, 1024):
         gpu, plan, _ = run_varlen(wl, P)
         assert plan.kernel == vb.KERNEL_VARLEN_TILES
         assert_parity(gpu, ref, f"tiles {geom} bs{bs} P{P}", dtype="f16_tiles")
