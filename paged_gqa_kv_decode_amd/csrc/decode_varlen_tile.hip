@@ -52,6 +52,9 @@
 #ifndef VK_TILE_PV_AHEAD
 #define VK_TILE_PV_AHEAD 4         // PV: V reads kept this many products ahead (0: compiler's order)
 #endif
+#ifndef VK_TILE_QK_AHEAD
+#define VK_TILE_QK_AHEAD 2         // QK: K reads kept this many 32-dim chunks ahead (0: compiler's order)
+#endif
 #ifndef VK_TILE_KEYS
 #define VK_TILE_KEYS 64            // keys per tile: 64 (two LDS buffers) or 32 (four)
 #endif
@@ -304,6 +307,9 @@ struct TileKernel {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) sc[cb][kb] = qk_mma(kv[kb], qb[cb][kk], sc[cb][kb]);
         }
+        // the compiler issued most of the tile's K reads before the first
+        // product; two chunks ahead: 855 vs 862 us on the chunked prefill
+        lds_ahead<NKC, KB, KB * CB, VK_TILE_QK_AHEAD>();
         // weights and their residuals, per 32-key PV step h: keys 32 h + 4c + e,
         // then 32 h + 16 + 4c + e
         uint4 pb[CB][KH], pl[CB][KH];
