@@ -150,12 +150,11 @@ typedef struct vk_plan {
  * Hq * sum_s floor(L_s / P) counts only full partitions.  With
  * partition_request == -1 the planner picks P = 512 when W(512) >= B, else
  * P = 256.  Then, not from the pages (an MI355X addition): 512 becomes
- * VK_PARTITION_XLARGE = 1024 when the 512 launch would hold one wave per
- * partition in a single round of the device's 8 * cu_count resident waves
- * (2 * S * Hkv * ceil(max L / 512) > 8 * cu_count) and the 1024 launch, two
- * waves of 512 tokens per partition, fits one round too
- * (2 * S * Hkv * ceil(max L / 1024) <= 8 * cu_count): the same waves, half
- * the partials.  0 asks for the unsplit path; 256, 512 or 1024 forces that
+ * VK_PARTITION_XLARGE = 1024 when the 1024 launch fits in a single round of
+ * the device's 8 * cu_count resident waves with at least two waves per
+ * partition (2 * S * Hkv * ceil(max L / 1024) <= 8 * cu_count): half the
+ * partials, longer streams per wave.  0 asks for the unsplit path; 256, 512
+ * or 1024 forces that
  * size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
  * exceed the cap (no fallback path exists).
  *

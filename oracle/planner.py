@@ -13,10 +13,10 @@ item 4 (split-KV partitions of 256 or 512 tokens):
 
 Not from the pages: the MI355X library adds a third partition size, 1024,
 in one regime (plan(..., wave_slots_per_cu=8) models it; without that
-argument this is the pages' rule alone): when the 512 launch would hold one
-wave per partition in a single round of cu_count * wave_slots_per_cu
-resident waves, 1024-token partitions over two waves each do the same work
-with half the partials.
+argument this is the pages' rule alone): when the pages' rule picks 512 and
+1024-token partitions fit in a single round of cu_count * wave_slots_per_cu
+resident waves with at least two waves each, the launch takes 1024: the
+same work with half the partials.
 
 Readings where the page is silent (each stated in the design notes):
   * work W(P) = Hq * sum_s floor(L_s / P): one unit per (query head, full
@@ -83,7 +83,7 @@ def plan(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_siz
         if wave_slots_per_cu and P == 512:   # the MI355X regime above
             slots = wave_slots_per_cu * cu_count
             items = lambda p: S * num_kv_heads * -(-max_len // p)
-            if 2 * items(512) > slots and 2 * items(1024) <= slots:
+            if 2 * items(1024) <= slots:
                 P = 1024
     else:
         P = partition_request

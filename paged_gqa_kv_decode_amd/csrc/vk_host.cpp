@@ -257,16 +257,19 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int
             // Largest partition first; it is kept only if its full partitions
             // alone reach the budget, otherwise the smaller size is used.
             P = ((int64_t)num_q_heads * full512 >= p.budget) ? VK_PARTITION_LARGE : VK_PARTITION_SMALL;
-            // MI355X: a 512-token launch that the wave slots (8 per CU) hold
-            // in one round with one wave per partition takes 1024-token
-            // partitions instead, two waves of 512 tokens each: the same
-            // waves, half the partials to write and merge (measured on 4 x
-            // 131072 tokens: decode 176.0 -> 170.6 us, reduce 10.1 -> 7.7).
+            // MI355X: when 1024-token partitions fit in one round of the
+            // wave slots (8 per CU) with at least two waves each, the launch
+            // takes them instead of 512: half the partials to write and
+            // merge, longer streams per wave.  Measured: 4 x 131072 tokens
+            // (16, 2, 256), decode 176.0 -> 170.6 us, reduce 10.1 -> 7.7;
+            // multi-query (16, 1, 256) on 16 x 32768 and 4 x 131072 tokens
+            // 95.5 -> 90.5 us, (16, 1, 128) on 6 x 65536 41.1 -> 39.9 us.
+            // Under the budget rule above only G = 16 reaches it while a
+            // 512 launch would still get four waves per partition.
             if (P == VK_PARTITION_LARGE) {
                 const int64_t slots = 8 * (int64_t)cu_count;
-                const int64_t wgs512 = (int64_t)num_seqs * num_kv_heads * ((max_len + 511) / 512);
                 const int64_t wgs1024 = (int64_t)num_seqs * num_kv_heads * ((max_len + 1023) / 1024);
-                if (2 * wgs512 > slots && 2 * wgs1024 <= slots) P = VK_PARTITION_XLARGE;
+                if (2 * wgs1024 <= slots) P = VK_PARTITION_XLARGE;
             }
         }
         p.partition_size = P;

@@ -102,9 +102,14 @@ def test_planner_long_context_decisions():
     # 32 x 16k (24q, 4kv, 256): 1024-token workgroups 32 * 4 * 16 = 2048, two
     # waves each > 2048 slots -> stays at 512 (several rounds: longest first)
     assert vb.plan_partitions([16384] * 32, 24, 4, 256, 32, 512, -1, 256).partition_size == 512
+    # multi-query 16 x 32768 (16q, 1kv, 256): W(512) = 16 * 16 * 64 >= 8448 ->
+    # 512, whose 1024 workgroups would still get four waves each; 1024-token
+    # partitions, 512 workgroups, fit the slots twice over -> 1024
+    assert vb.plan_partitions([32768] * 16, 16, 1, 256, 32, 1024, -1, 256).partition_size == 1024
     # both sides of the regime on 1 CU (8 slots), budget 1 per CU, Hkv = 2:
-    # 2 * 2 * ceil(L / 512) > 8 and 2 * 2 * ceil(L / 1024) <= 8 <=> 1024 < L <= 2048
-    for L, P in ((1024, 512), (1025, 1024), (2048, 1024), (2049, 512)):
+    # 512 needs W(512) = 16 * floor(L / 512) >= 1, i.e. L >= 512, and 1024 then
+    # needs 2 * 2 * ceil(L / 1024) <= 8, i.e. L <= 2048
+    for L, P in ((511, 256), (512, 1024), (1024, 1024), (2048, 1024), (2049, 512)):
         assert vb.plan_partitions([L], 16, 2, 128, 16, 129, -1, 1, 1).partition_size == P, L
     # a forced 1024 is taken as it is
     p = vb.plan_partitions([5000, 3000], 32, 8, 128, 16, 313, 1024, 256)
