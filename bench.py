@@ -588,14 +588,88 @@ def cpu_single_thread():
     return res
 
 
+def partition_sweep(args):
+    """Multi-head and multi-query geometries, which the planner's budget was
+    not calibrated on: decode + reduce at P = 256, 512 and 1024 (waves and
+    order on auto; HIP events on the launch stream, 10 steps per segment in
+    the order 256, 512, 1024, 1024, 512, 256, K/V pools rotated as in the
+    timed step), beside the planner's own choice.  Inputs are random fp16
+    drawn on the device (timing only).  One JSON line per batch."""
+    import numpy as np
+    import torch
+    from paged_gqa_kv_decode_amd import binding as vb
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    geoms = [((16, 16, 128), 16), ((8, 8, 256), 16), ((16, 1, 128), 16), ((16, 1, 256), 32)]
+    rng = np.random.default_rng(5)
+    batches = [(f"{S}x32768", [32768] * S) for S in (1, 2, 4, 8, 16, 32)]
+    batches += [(f"{S}xU[1,32768]", list(rng.integers(1, 32769, S))) for S in (8, 32, 64)]
+    stream = torch.cuda.current_stream()
+    sizes = (256, 512, 1024)
+    for (Hq, Hkv, D), bs in geoms:
+        for name, lens in batches:
+            lens = np.asarray(lens, dtype=np.int32)
+            S = len(lens)
+            pages = [-(-int(L) // bs) for L in lens]
+            pool = int(sum(pages))
+            perm = rng.permutation(pool).astype(np.int32)
+            bt = np.zeros((S, max(pages)), dtype=np.int32)
+            o = 0
+            for i, n in enumerate(pages):
+                bt[i, :n] = perm[o:o + n]
+                o += n
+            kv_bytes = 4 * Hkv * D * int(lens.sum())
+            ncopies = max(2, min(16, -(-(4 * MALL_BYTES) // kv_bytes)))
+            q = torch.randn((S, Hq, D), device="cuda").half()
+            pools = [(torch.randn((pool, Hkv, bs, D), device="cuda").half(),
+                      torch.randn((pool, Hkv, bs, D), device="cuda").half()) for _ in range(ncopies)]
+            btd, sld = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+            steps = {P: vb.DecodeStep(q, pools[0][0], pools[0][1], btd, sld, lens, D ** -0.5, P)
+                     for P in sizes}
+            times = {P: [] for P in sizes}
+            ctr = [0]
+
+            def seg(P, n, record):
+                st = steps[P]
+                for _ in range(n):
+                    k, v = pools[ctr[0] % ncopies]
+                    ctr[0] += 1
+                    st.args = (q, k, v, btd, sld)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    st.run()
+                    e1.record(stream)
+                    if record:
+                        times[P].append((e0, e1))
+            for P in sizes:
+                seg(P, 3, False)
+            for P in sizes + sizes[::-1]:
+                seg(P, 10, True)
+            torch.cuda.synchronize()
+            us = {P: round(float(np.mean([a.elapsed_time(b) for a, b in times[P]])) * 1e3, 2)
+                  for P in sizes}
+            plan = vb.plan_partitions(lens, Hq, Hkv, D, bs, bt.shape[1], -1, cu)
+            best = min(us, key=us.get)
+            print(json.dumps({"partition_sweep": f"{Hq}q{Hkv}kv{D}", "block_size": bs, "batch": name,
+                              "us_per_step": {str(P): us[P] for P in sizes},
+                              "planner": plan.partition_size, "best": best,
+                              "planner_loss_pct": round(100 * (us[plan.partition_size] / us[best] - 1), 1),
+                              "w512_per_cu": round(Hq * int((lens // 512).sum()) / cu, 1),
+                              "kv_GB": round(kv_bytes / 1e9, 3)}), flush=True)
+            del pools, steps
+            torch.cuda.empty_cache()
+
+
 def planner_sweep(args):
     """The data behind the partition planner's budget: for the four
     grouped-query geometries and a range of batches, decode + reduce at P =
     256 against P = 512 (HIP events on the launch stream, 10 steps per
     segment in ABBA order, K/V pools rotated as in the timed step), beside
-    the full-partition work W(512) = Hq * sum_s floor(L_s / 512) per CU that
-    the planner compares with its budget (33 per CU: P = 512 when W(512) >=
-    33 * CUs).  Inputs are random fp16 drawn on the device (timing only)."""
+    the full-partition work W(512) = Hq * sum_s floor(L_s / 512) per CU in
+    the pages' query-head units (their budget: 33 per CU) and in workgroups,
+    Hkv * sum_s floor(L_s / 512) per CU (the library's default budget: 4 per
+    CU, i.e. 4 * G query-head units).  The summary scores both rules and the
+    best threshold in each unit by the time lost against the faster size.
+    Inputs are random fp16 drawn on the device (timing only)."""
     import numpy as np
     import torch
     from paged_gqa_kv_decode_amd import binding as vb
@@ -650,26 +724,32 @@ def planner_sweep(args):
             w512 = Hq * int((lens // 512).sum())
             plan = vb.plan_partitions(lens, Hq, Hkv, D, bs, bt.shape[1], -1, cu)
             r = {"geometry": [Hq, Hkv, D], "block_size": bs, "batch": name,
-                 "w512_per_cu": round(w512 / cu, 2), "us_P256": round(us[256], 2),
+                 "w512_per_cu": round(w512 / cu, 2),
+                 "wg512_per_cu": round(Hkv * int((lens // 512).sum()) / cu, 3),
+                 "us_P256": round(us[256], 2),
                  "us_P512": round(us[512], 2), "faster": 256 if us[256] < us[512] else 512,
                  "planner": plan.partition_size}
             rows.append(r)
             print(json.dumps(r), flush=True)
             del pools, steps, q
             torch.cuda.empty_cache()
-    # the budget per CU that the data favour: the threshold on W(512)/CU
-    # that picks the faster size for the most batches (ties: the smallest
-    # loss in us)
-    cands = sorted({r["w512_per_cu"] for r in rows} | {33.0})
-    def score(b):
-        wrong = [r for r in rows if (512 if r["w512_per_cu"] >= b else 256) != r["faster"]]
+    # each rule's misses against the faster size and the time they lose; the
+    # best threshold per unit is the one losing the least time (ties: fewer
+    # misses)
+    def score(key, b):
+        wrong = [r for r in rows if (512 if r[key] >= b else 256) != r["faster"]]
         loss = sum(abs(r["us_P256"] - r["us_P512"]) for r in wrong)
-        return (len(wrong), loss)
-    best = min(cands, key=score)
+        return (round(loss, 2), len(wrong))
+    best_q = min(sorted({r["w512_per_cu"] for r in rows} | {33.0}), key=lambda b: score("w512_per_cu", b))
+    best_w = min(sorted({r["wg512_per_cu"] for r in rows} | {4.0}), key=lambda b: score("wg512_per_cu", b))
     print(json.dumps({"planner_sweep": "summary", "cu_count": cu, "configs": len(rows),
-                      "budget_33_wrong": score(33.0)[0], "budget_33_loss_us": round(score(33.0)[1], 2),
-                      "best_threshold_per_cu": best, "best_wrong": score(best)[0],
-                      "best_loss_us": round(score(best)[1], 2)}), flush=True)
+                      "pages_budget_33": dict(zip(("loss_us", "wrong"), score("w512_per_cu", 33.0))),
+                      "default_4_workgroups": dict(zip(("loss_us", "wrong"), score("wg512_per_cu", 4.0))),
+                      "best_query_head_threshold": best_q,
+                      "best_query_head": dict(zip(("loss_us", "wrong"), score("w512_per_cu", best_q))),
+                      "best_workgroup_threshold": best_w,
+                      "best_workgroup": dict(zip(("loss_us", "wrong"), score("wg512_per_cu", best_w)))}),
+          flush=True)
 
 
 def main():
@@ -717,6 +797,9 @@ def main():
     ap.add_argument("--planner-sweep", action="store_true",
                     help="time P=256 against P=512 over geometries and batches (the data "
                          "behind the planner's budget); prints one JSON line per batch")
+    ap.add_argument("--partition-sweep", action="store_true",
+                    help="time P=256, 512 and 1024 on multi-head and multi-query geometries "
+                         "beside the planner's choice; prints one JSON line per batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, --steps times (the "
                          "known-size reference for the HBM byte counters)")
@@ -735,6 +818,8 @@ def main():
 
     if args.planner_sweep:
         return planner_sweep(args)
+    if args.partition_sweep:
+        return partition_sweep(args)
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -149,18 +149,22 @@ typedef struct vk_plan {
  * design notes): budget B = budget_per_cu * cu_count.  Work W(P) =
  * Hq * sum_s floor(L_s / P) counts only full partitions.  With
  * partition_request == -1 the planner picks P = 512 when W(512) >= B, else
- * P = 256.  Then, not from the pages (an MI355X addition): 512 becomes
+ * P = 256.  The default budget is an MI355X calibration, not the pages' 33:
+ * 4 * G units per CU (G = Hq / Hkv), i.e. P = 512 once the full 512-token
+ * partitions give 4 workgroups per CU.  Then, not from the pages (an MI355X
+ * addition): 512 becomes
  * VK_PARTITION_XLARGE = 1024 when the 1024 launch fits in a single round of
  * the device's 8 * cu_count resident waves with at least two waves per
  * partition (2 * S * Hkv * ceil(max L / 1024) <= 8 * cu_count): half the
  * partials, longer streams per wave.  0 asks for the unsplit path; 256, 512
- * or 1024 forces that
- * size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
+ * or 1024 forces that size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
  * exceed the cap (no fallback path exists).
  *
  *   seq_lens_host       host int32 [num_seqs], each in [1, max_blocks_per_seq*block_size]
  *   cu_count            compute units; 0 = query the current HIP device
- *   budget_per_cu       0 = 33
+ *   budget_per_cu       query-head units per CU; 0 = 4 * Hq / Hkv (four
+ *                       workgroups of full 512-token partitions per CU, an
+ *                       MI355X calibration; the pages' constant is 33)
  *   scratch_cap_bytes   0 = 512 MiB
  *   plan_out            host struct, written on VK_OK only
  * Also recorded as this thread's vk_last_plan.

@@ -13,7 +13,9 @@ item 4 (split-KV partitions of 256 or 512 tokens):
 
 Not from the pages: the MI355X library adds a third partition size, 1024,
 in one regime (plan(..., wave_slots_per_cu=8) models it; without that
-argument this is the pages' rule alone): when the pages' rule picks 512 and
+argument this is the pages' rule alone), and its default budget is 4 * G
+query-head units per CU (four workgroups of one KV head's G query heads)
+instead of the pages' 33 (an MI355X calibration); when the rule picks 512 and
 1024-token partitions fit in a single round of cu_count * wave_slots_per_cu
 resident waves with at least two waves each, the launch takes 1024: the
 same work with half the partials.
@@ -72,6 +74,8 @@ def plan(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_siz
         if int(L) < 1 or int(L) > cap_tokens:
             raise PlanError("SEQ_LEN", f"seq_len {L} outside [1, {cap_tokens}]")
     per_cu = budget_per_cu if budget_per_cu > 0 else DEFAULT_BUDGET_PER_CU
+    if wave_slots_per_cu and budget_per_cu <= 0:   # the MI355X default above
+        per_cu = 4 * (num_q_heads // num_kv_heads)
     budget = per_cu * cu_count
     cap = scratch_cap_bytes if scratch_cap_bytes > 0 else DEFAULT_SCRATCH_CAP
     max_len = max(int(L) for L in seq_lens)

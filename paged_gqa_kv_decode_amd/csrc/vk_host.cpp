@@ -240,7 +240,11 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int
         if (e != hipSuccess) return hip_fail(e);
         cu_count = n;
     }
-    const int64_t per_cu = budget_per_cu > 0 ? budget_per_cu : VK_DEFAULT_BUDGET_PER_CU;
+    // Default budget: 4 workgroups of full 512-token partitions per CU, each
+    // workgroup serving the G query heads of one KV head (MI355X calibration).
+    const int64_t per_cu = budget_per_cu > 0
+                               ? budget_per_cu
+                               : (int64_t)VK_DECODE_BUDGET_WG_PER_CU * (num_q_heads / num_kv_heads);
     const uint64_t cap = scratch_cap_bytes > 0 ? scratch_cap_bytes : VK_DEFAULT_SCRATCH_CAP;
 
     vk_plan p = {};
@@ -264,8 +268,6 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int
             // (16, 2, 256), decode 176.0 -> 170.6 us, reduce 10.1 -> 7.7;
             // multi-query (16, 1, 256) on 16 x 32768 and 4 x 131072 tokens
             // 95.5 -> 90.5 us, (16, 1, 128) on 6 x 65536 41.1 -> 39.9 us.
-            // Under the budget rule above only G = 16 reaches it while a
-            // 512 launch would still get four waves per partition.
             if (P == VK_PARTITION_LARGE) {
                 const int64_t slots = 8 * (int64_t)cu_count;
                 const int64_t wgs1024 = (int64_t)num_seqs * num_kv_heads * ((max_len + 1023) / 1024);

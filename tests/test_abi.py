@@ -90,13 +90,24 @@ def test_planner_matches_oracle_rule_random():
 
 
 def test_planner_long_context_decisions():
-    # 4 x 131072 tokens (16q, 2kv, 256), bs 32 on 256 CUs: W(512) = 16384 >= 8448
-    # -> 512; its 4 * 2 * 256 = 2048 workgroups would fill the 2048 wave slots
-    # (8 per CU) once with one wave each, and 4 * 2 * 128 = 1024 workgroups of
-    # two waves over 1024-token partitions fill them too -> 1024,
-    # W(1024) = 16 * 4 * 128.
+    # 4 x 131072 tokens (16q, 2kv, 256), bs 32 on 256 CUs: W(512) = 16384 >=
+    # the default budget 4 * G * 256 = 8192 -> 512; its 4 * 2 * 256 = 2048
+    # workgroups would fill the 2048 wave slots (8 per CU) once with one wave
+    # each, and 4 * 2 * 128 = 1024 workgroups of two waves over 1024-token
+    # partitions fill them too -> 1024, W(1024) = 16 * 4 * 128.
     p = vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 256)
-    assert (p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget) == (1024, 128, 8192, 8448)
+    assert (p.partition_size, p.max_num_partitions, p.work_full_parts, p.budget) == (1024, 128, 8192, 8192)
+    # the default budget is 4 * G query-head units per CU: 4 workgroups per CU
+    for (Hq, Hkv, D), bs in (((32, 8, 128), 16), ((24, 4, 256), 32), ((16, 1, 128), 16),
+                             ((16, 16, 128), 16)):
+        assert vb.plan_partitions([4096], Hq, Hkv, D, bs, 4096 // bs, -1, 80).budget == 4 * (Hq // Hkv) * 80
+    # both sides of 4 workgroups per CU on 16 CUs, (32q, 8kv, 128): W(512) =
+    # 32 * floor(L / 512) against 4 * 4 * 16 = 256, i.e. 8 full partitions
+    # (512, and one round of 1024-token partitions: 32 workgroups <= 128 / 2 slots -> 1024)
+    assert vb.plan_partitions([8 * 512], 32, 8, 128, 16, 256, -1, 16).partition_size == 1024
+    assert vb.plan_partitions([8 * 512 - 1], 32, 8, 128, 16, 256, -1, 16).partition_size == 256
+    # the pages' budget, 33 units per CU, on request
+    assert vb.plan_partitions([8 * 512], 32, 8, 128, 16, 256, -1, 16, 33).partition_size == 256
     # 304 CUs (2432 slots): 2 * 2048 > 2432 and 2 * 1024 <= 2432 -> 1024
     assert vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 304).partition_size == 1024
     # 32 x 16k (24q, 4kv, 256): 1024-token workgroups 32 * 4 * 16 = 2048, two
@@ -317,7 +328,8 @@ def test_plan_varlen_large_partition_at_the_budget(columns):
     for lens in ([8192, 4096], [1023, 600], [33 * 512], [33 * 512 - 1]):
         for cu in (1, 16):
             a = _pv(lens, [1] * len(lens), (16, 2, 256), bs=32, cu=cu)
-            d = vb.plan_partitions(np.array(lens, dtype=np.int32), 16, 2, 256, 32, 600, -1, cu)
+            # (the multi-token planner keeps the pages' budget of 33 per CU)
+            d = vb.plan_partitions(np.array(lens, dtype=np.int32), 16, 2, 256, 32, 600, -1, cu, 33)
             if d.partition_size == 1024:
                 assert (a.partition_size, a.work_full_parts) == (512, 16 * sum(L // 512 for L in lens))
             else:
