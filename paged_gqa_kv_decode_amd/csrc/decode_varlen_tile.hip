@@ -30,7 +30,7 @@
 //    order, 16-byte chunks permuted per row against bank conflicts, read with
 //    the transposing ds_read_b64_tr_b16, which hands each lane four keys of
 //    one dim, so V^T needs no register shuffles.
-//  * Per wave and tile: S^T = K Q^T for two 16-column blocks (16x16x32
+//  * Per wave and tile: S^T = K Q^T for its 16-column blocks (16x16x32
 //    products, Q^T held in registers), log2 online softmax per column with
 //    the causal limit applied by select on the diagonal tiles only, then
 //    O^T += V^T P^T (16x16x32).  The softmax's exponent reference trails the
@@ -286,8 +286,8 @@ struct TileKernel {
         }
     }
 
-    // One tile for this wave's two column blocks; rem[cb]: keys of the tile
-    // the lane's column sees (MASK: some column sees fewer than 32).
+    // One tile for this wave's column blocks; rem[cb]: keys of the tile the
+    // lane's column sees (MASK: some column sees fewer than KT).
     template <bool MASK>
     static __device__ __forceinline__ void compute(const DecodeArgs& a, Col (&st)[CB], const char* lb,
                                                    const uint4 (&qb)[CB][NKC], const int (&rem)[CB],
