@@ -791,7 +791,7 @@ def main():
                     help="skip the box's read-bandwidth ceilings on the KV pools")
     ap.add_argument("--no-configs", action="store_true",
                     help="default workload: skip timing the other long-context workloads "
-                         "(long32_16k at P=256 and 512, mixed64_32k at 512)")
+                         "(long32_16k at P=256, 512 and the planner's choice, mixed64_32k at 512 and the planner's choice)")
     ap.add_argument("--flush", action="store_true",
                     help="also time the decode with a 512 MiB cache flush before each run")
     ap.add_argument("--planner-sweep", action="store_true",
@@ -922,11 +922,13 @@ def main():
             and args.workload == "long4_128k" and args.partition is None):
         # The other long-context workloads, timed the same way in this run.
         configs = {}
-        for name, p_req in (("long32_16k", 256), ("long32_16k", 512), ("mixed64_32k", 512)):
+        for name, p_req in (("long32_16k", 256), ("long32_16k", 512), ("long32_16k", -1),
+                            ("mixed64_32k", 512), ("mixed64_32k", -1)):
+            key = f"{name}_P{p_req}" if p_req > 0 else f"{name}_planner"
             wl2 = make_workload(name)
             db2 = DecodeBench(wl2, p_req, args.max_copies)
             t2 = db2.time(args.steps, args.warmup)
-            configs[f"{name}_P{p_req}"] = {
+            configs[key] = {
                 "partition_size": db2.P, "kv_read_bytes": db2.kv_bytes,
                 "decode_us_mean": t2["kernel_us"]["decode_mean"],
                 "decode_us_median": t2["kernel_us"]["decode_median"],
@@ -939,15 +941,15 @@ def main():
             if not args.no_ceiling:
                 # this workload's own read ceiling (its page size and page list)
                 c2 = ceilings(wl2, db2.dev, db2.P)
-                configs[f"{name}_P{p_req}"].update({
+                configs[key].update({
                     "read_ceiling_GBps": c2["read_ceiling_GBps"],
                     "read_ceiling_kernel": c2["read_ceiling_kernel"],
                     "page_bytes": c2["page_bytes"],
                     "of_ceiling": round(t2["achieved_GBps"] / c2["read_ceiling_GBps"], 4)})
             db2.release()
             del wl2
-            print(f"bench: {name} P={p_req}: decode {t2['kernel_us']['decode_mean']} us "
-                  f"({configs[f'{name}_P{p_req}']['frac']:.3f} of peak)", file=sys.stderr,
+            print(f"bench: {key}: decode {t2['kernel_us']['decode_mean']} us "
+                  f"({configs[key]['frac']:.3f} of peak)", file=sys.stderr,
                   flush=True)
         # The multi-token workloads (verification rows, a chunked prefill),
         # timed as `--workload <name>` would, planner and kernel choice auto.

@@ -32,6 +32,10 @@
  * the faster partition size in all, the pages' 33 units per CU 43-45 us;
  * over 36 multi-head and multi-query batches 158 us against 231 us. */
 #define VK_DECODE_BUDGET_WG_PER_CU 4
+/* With the default budget the decode planner tries 1024-token partitions
+ * first: taken once their full partitions give this many workgroups per CU
+ * (MI355X calibration, not from the pages). */
+#define VK_DECODE_XLARGE_WG_PER_CU 2
 #define VK_DEFAULT_SCRATCH_CAP (512ull * 1024ull * 1024ull)
 
 /* Admitted geometries (Hq, Hkv, D): the four grouped-query triples of the

@@ -18,7 +18,8 @@ query-head units per CU (four workgroups of one KV head's G query heads)
 instead of the pages' 33 (an MI355X calibration); when the rule picks 512 and
 1024-token partitions fit in a single round of cu_count * wave_slots_per_cu
 resident waves with at least two waves each, the launch takes 1024: the
-same work with half the partials.
+same work with half the partials; and with the default budget 1024 is taken
+first once its full partitions give 2 workgroups per CU.
 
 Readings where the page is silent (each stated in the design notes):
   * work W(P) = Hq * sum_s floor(L_s / P): one unit per (query head, full
@@ -89,6 +90,11 @@ def plan(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_siz
             items = lambda p: S * num_kv_heads * -(-max_len // p)
             if 2 * items(1024) <= slots:
                 P = 1024
+        # MI355X default budget: 1024 first once its full partitions give 2
+        # workgroups (KV head, partition) per CU
+        if wave_slots_per_cu and budget_per_cu <= 0 and \
+                num_kv_heads * sum(int(L) // 1024 for L in seq_lens) >= 2 * cu_count:
+            P = 1024
     else:
         P = partition_request
     NP = -(-max_len // P)

@@ -273,6 +273,14 @@ vk_status vk_plan_partitions(const int32_t* seq_lens_host, int32_t num_seqs, int
                 const int64_t wgs1024 = (int64_t)num_seqs * num_kv_heads * ((max_len + 1023) / 1024);
                 if (2 * wgs1024 <= slots) P = VK_PARTITION_XLARGE;
             }
+            // MI355X default (no caller budget): 1024-token partitions first,
+            // once their full partitions give 2 workgroups per CU (launched
+            // with four waves each): over 84 timed batches of the eight
+            // geometries this lost 65 us against the fastest size, the 512 /
+            // 256 rule above 460 us.
+            if (budget_per_cu == 0 &&
+                (int64_t)num_kv_heads * full1024 >= (int64_t)VK_DECODE_XLARGE_WG_PER_CU * cu_count)
+                P = VK_PARTITION_XLARGE;
         }
         p.partition_size = P;
         p.max_num_partitions = (int32_t)((max_len + P - 1) / P);
@@ -396,8 +404,15 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         // fp32 at head dim 256 holds one wave per SIMD (half the slots the
         // planner counts): one wave per 1024-token partition keeps that one
         // round (two waves per partition measured 514 vs 365 us at 512).
-        if (partition_size == VK_PARTITION_XLARGE && 2 * wgs <= slots && 4 * wgs > slots)
-            kernel = (dtype == VK_DTYPE_F32 && head_dim == 256) ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2;
+        // Other 1024-token launches: four waves of 256 tokens per partition.
+        // The grid counts every (partition, KV head, sequence) slot, empty
+        // ones included, so on mixed lengths it can fit one round while few
+        // partitions exist; one wave each then left the CUs short of loads
+        // (e.g. 16 sequences of 1-32768 tokens, (24, 4, 256): 194 vs 136 us).
+        if (partition_size == VK_PARTITION_XLARGE)
+            kernel = (2 * wgs <= slots && 4 * wgs > slots)
+                         ? ((dtype == VK_DTYPE_F32 && head_dim == 256) ? VK_KERNEL_MFMA_W1 : VK_KERNEL_MFMA_W2)
+                         : VK_KERNEL_MFMA_W4;
     }
     a.work_order = 0;
     a.write_through = 0;

@@ -110,9 +110,20 @@ def test_planner_long_context_decisions():
     assert vb.plan_partitions([8 * 512], 32, 8, 128, 16, 256, -1, 16, 33).partition_size == 256
     # 304 CUs (2432 slots): 2 * 2048 > 2432 and 2 * 1024 <= 2432 -> 1024
     assert vb.plan_partitions([131072] * 4, 16, 2, 256, 32, 4096, -1, 304).partition_size == 1024
-    # 32 x 16k (24q, 4kv, 256): 1024-token workgroups 32 * 4 * 16 = 2048, two
-    # waves each > 2048 slots -> stays at 512 (several rounds: longest first)
-    assert vb.plan_partitions([16384] * 32, 24, 4, 256, 32, 512, -1, 256).partition_size == 512
+    # 32 x 16k (24q, 4kv, 256): full 1024-token partitions 4 * 32 * 16 = 2048
+    # workgroups >= 2 per CU (512) -> 1024 first (the default budget's rule)
+    assert vb.plan_partitions([16384] * 32, 24, 4, 256, 32, 512, -1, 256).partition_size == 1024
+    # under the pages' budget (33 per CU) the same batch takes 512: its 2048
+    # two-wave 1024-token workgroups would not fit one round of 2048 slots
+    assert vb.plan_partitions([16384] * 32, 24, 4, 256, 32, 512, -1, 256, 33).partition_size == 512
+    # no full 1024-token partition, 300 * 4 = 1200 full 512-token ones
+    # (>= 4 per CU) and 1024-token workgroups of two waves over 2048 slots -> 512
+    assert vb.plan_partitions([1000] * 300, 24, 4, 256, 32, 32, -1, 256).partition_size == 512
+    # both sides of 2 full 1024-token workgroups per CU (16 CUs, Hkv = 2):
+    # 2 * floor(L / 1024) >= 32 <=> L >= 16 * 1024
+    assert vb.plan_partitions([16 * 1024], 16, 2, 256, 32, 512, -1, 16).partition_size == 1024
+    # (one token less: 2 * 15 = 30 < 32, and W(512) = 16 * 31 = 496 < 4 * 8 * 16 -> 256)
+    assert vb.plan_partitions([16 * 1024 - 1], 16, 2, 256, 32, 512, -1, 16).partition_size == 256
     # multi-query 16 x 32768 (16q, 1kv, 256): W(512) = 16 * 16 * 64 >= 8448 ->
     # 512, whose 1024 workgroups would still get four waves each; 1024-token
     # partitions, 512 workgroups, fit the slots twice over -> 1024
@@ -353,7 +364,8 @@ def test_plan_varlen_xlarge_partition_rule(columns):
     assert (p.partition_size, p.work_full_parts) == (512, 16 * 65)
     # one query token per sequence: the decode planner's sizes only
     p = _pv([33 * 1024], [1], (16, 2, 256), bs=32, cu=16)
-    d = vb.plan_partitions(np.array([33 * 1024], dtype=np.int32), 16, 2, 256, 32, 1100, -1, 16)
+    # (against the decode planner under the same, pages' budget of 33 per CU)
+    d = vb.plan_partitions(np.array([33 * 1024], dtype=np.int32), 16, 2, 256, 32, 1100, -1, 16, 33)
     assert p.partition_size == d.partition_size == 512
     # the verification shape: 32 x 4 tokens (32, 8, 128) on 4k-16k contexts
     lens = [4096 + 384 * k for k in range(32)]
