@@ -17,11 +17,12 @@
 #define VK_PARTITION_LARGE 512
 #define VK_PARTITION_SMALL 256
 /* A third, larger partition (an MI355X addition: half the partials of 512).
- * vk_plan_partitions upgrades 512 to it when the 512-token launch would run
- * one wave per partition in a single round of the wave slots (the 1024-token
- * partitions then take two waves of 512 tokens each: the same waves, half
- * the partials); vk_plan_varlen tries it first for column tiles of several
- * query tokens.  Every split entry point accepts it. */
+ * vk_plan_partitions takes it first under its default budget once the full
+ * 1024-token partitions give VK_DECODE_XLARGE_WG_PER_CU workgroups per CU,
+ * and upgrades 512 to it when the 1024-token launch fits one round of the
+ * wave slots with two or more waves per partition; vk_plan_varlen tries it
+ * first for column tiles of several query tokens.  Every split entry point
+ * accepts it. */
 #define VK_PARTITION_XLARGE 1024
 
 #define VK_DEFAULT_BUDGET_PER_CU 33

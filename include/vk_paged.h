@@ -151,13 +151,14 @@ typedef struct vk_plan {
  * partition_request == -1 the planner picks P = 512 when W(512) >= B, else
  * P = 256.  The default budget is an MI355X calibration, not the pages' 33:
  * 4 * G units per CU (G = Hq / Hkv), i.e. P = 512 once the full 512-token
- * partitions give 4 workgroups per CU.  Then, not from the pages (an MI355X
- * addition): 512 becomes
- * VK_PARTITION_XLARGE = 1024 when the 1024 launch fits in a single round of
- * the device's 8 * cu_count resident waves with at least two waves per
- * partition (2 * S * Hkv * ceil(max L / 1024) <= 8 * cu_count): half the
- * partials, longer streams per wave.  0 asks for the unsplit path; 256, 512
- * or 1024 forces that size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
+ * partitions give 4 workgroups per CU.  Then, not from the pages (MI355X
+ * additions): 512 becomes VK_PARTITION_XLARGE = 1024 when the 1024 launch
+ * fits in a single round of the device's 8 * cu_count resident waves with
+ * at least two waves per partition (2 * S * Hkv * ceil(max L / 1024) <=
+ * 8 * cu_count): half the partials, longer streams per wave; and with the
+ * default budget 1024 is taken first whenever Hkv * sum_s floor(L_s / 1024)
+ * >= 2 * cu_count (two workgroups of full 1024-token partitions per CU).
+ * 0 asks for the unsplit path; 256, 512 or 1024 forces that size.  NP = ceil(max L / P); scratch = S*Hq*NP*(D+2)*4 bytes, which must not
  * exceed the cap (no fallback path exists).
  *
  *   seq_lens_host       host int32 [num_seqs], each in [1, max_blocks_per_seq*block_size]
