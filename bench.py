@@ -659,6 +659,83 @@ def partition_sweep(args):
             torch.cuda.empty_cache()
 
 
+def wave_sweep(args):
+    """The data behind the 1024-first planner step and the four-wave launch
+    of 1024-token partitions: decode + reduce at P = 512 (waves on auto) and
+    at P = 1024 with auto, one, two and four waves per partition, over the
+    eight geometries and 15 batches (HIP events, 8 steps per segment in the
+    order of the variants and back, K/V pools rotated).  Random fp16 inputs
+    drawn on the device (timing only).  One JSON line per batch."""
+    import numpy as np
+    import torch
+    from paged_gqa_kv_decode_amd import binding as vb
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    geoms = [((32, 8, 128), 16), ((24, 4, 256), 32), ((16, 2, 128), 8), ((16, 2, 256), 32),
+             ((16, 16, 128), 16), ((8, 8, 256), 16), ((16, 1, 128), 16), ((16, 1, 256), 32)]
+    rng = np.random.default_rng(5)
+    batches = [(f"{S}x32768", [32768] * S) for S in (1, 2, 3, 4, 6, 8, 10, 12, 16, 24)]
+    batches += [(f"{S}xU[1,32768]", list(rng.integers(1, 32769, S))) for S in (8, 16, 32, 64)]
+    batches += [("32xU[4k,16k]", list(rng.integers(4096, 16385, 32)))]
+    stream = torch.cuda.current_stream()
+    variants = [("512", 512, vb.KERNEL_AUTO), ("1024", 1024, vb.KERNEL_AUTO),
+                ("1024_w1", 1024, vb.KERNEL_MFMA_W1), ("1024_w2", 1024, vb.KERNEL_MFMA_W2),
+                ("1024_w4", 1024, vb.KERNEL_MFMA_W4)]
+    for (Hq, Hkv, D), bs in geoms:
+        for name, lens in batches:
+            lens = np.asarray(lens, dtype=np.int32)
+            S = len(lens)
+            pages = [-(-int(L) // bs) for L in lens]
+            pool = int(sum(pages))
+            perm = rng.permutation(pool).astype(np.int32)
+            bt = np.zeros((S, max(pages)), dtype=np.int32)
+            o = 0
+            for i, n in enumerate(pages):
+                bt[i, :n] = perm[o:o + n]
+                o += n
+            kv_bytes = 4 * Hkv * D * int(lens.sum())
+            ncopies = max(2, min(16, -(-(4 * MALL_BYTES) // kv_bytes)))
+            q = torch.randn((S, Hq, D), device="cuda").half()
+            pools = [(torch.randn((pool, Hkv, bs, D), device="cuda").half(),
+                      torch.randn((pool, Hkv, bs, D), device="cuda").half()) for _ in range(ncopies)]
+            btd, sld = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+            steps = {t: vb.DecodeStep(q, pools[0][0], pools[0][1], btd, sld, lens, D ** -0.5, P)
+                     for t, P, _ in variants}
+            kern = {t: k for t, _, k in variants}
+            times = {t: [] for t, _, _ in variants}
+            ctr = [0]
+
+            def seg(t, n, record):
+                prev = vb.select_decode_kernel(kern[t])
+                try:
+                    st = steps[t]
+                    for _ in range(n):
+                        k, v = pools[ctr[0] % ncopies]
+                        ctr[0] += 1
+                        st.args = (q, k, v, btd, sld)
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        st.run()
+                        e1.record(stream)
+                        if record:
+                            times[t].append((e0, e1))
+                finally:
+                    vb.select_decode_kernel(prev)
+            tags = [t for t, _, _ in variants]
+            for t in tags:
+                seg(t, 3, False)
+            for t in tags + tags[::-1]:
+                seg(t, 8, True)
+            torch.cuda.synchronize()
+            us = {t: round(float(np.mean([a.elapsed_time(b) for a, b in times[t]])) * 1e3, 2) for t in tags}
+            plan = vb.plan_partitions(lens, Hq, Hkv, D, bs, bt.shape[1], -1, cu)
+            print(json.dumps({"wave_sweep": f"{Hq}q{Hkv}kv{D}", "block_size": bs, "batch": name,
+                              "us_per_step": us, "planner": plan.partition_size,
+                              "full1024_workgroups_per_cu": round(Hkv * int((lens // 1024).sum()) / cu, 2),
+                              "kv_GB": round(kv_bytes / 1e9, 3)}), flush=True)
+            del pools, steps
+            torch.cuda.empty_cache()
+
+
 def planner_sweep(args):
     """The data behind the partition planner's budget: for the four
     grouped-query geometries and a range of batches, decode + reduce at P =
@@ -800,6 +877,9 @@ def main():
     ap.add_argument("--partition-sweep", action="store_true",
                     help="time P=256, 512 and 1024 on multi-head and multi-query geometries "
                          "beside the planner's choice; prints one JSON line per batch")
+    ap.add_argument("--wave-sweep", action="store_true",
+                    help="time P=512 against P=1024 with 1, 2 and 4 waves per partition over "
+                         "eight geometries and 15 batches; prints one JSON line per batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, --steps times (the "
                          "known-size reference for the HBM byte counters)")
@@ -820,6 +900,8 @@ def main():
         return planner_sweep(args)
     if args.partition_sweep:
         return partition_sweep(args)
+    if args.wave_sweep:
+        return wave_sweep(args)
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
