@@ -421,6 +421,15 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
     } else {
         int waves = kernel == VK_KERNEL_MFMA_W1 ? 1 : kernel == VK_KERNEL_MFMA_W2 ? 2 : 4;
+        // fp32 at head dim 256 holds one wave per SIMD (its registers): one
+        // wave per partition in every case, the work order decided for that
+        // (32 sequences of 4k-16k tokens, (24, 4, 256): four waves 822 /
+        // 817 us at P = 512 / 1024, one wave 452.6 / 488 us).
+        const bool f32_wide = auto_waves && dtype == VK_DTYPE_F32 && head_dim == 256;
+        if (f32_wide) {
+            waves = 1;
+            kernel = VK_KERNEL_MFMA_W1;
+        }
         int parts_per_wg = kernel == VK_KERNEL_MFMA_W4P2 ? 2 : 1;
         // Longest-first work order when the split grid takes more than one
         // round of the wave slots, so the order decides the tail.  Measured on
@@ -438,10 +447,11 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         // dirty in L2 until the launch ends; single-round and grid-order
         // launches gained nothing from writing through.
         a.write_through = a.work_order;
-        if (auto_waves && a.work_order == 1) {
+        if (auto_waves && a.work_order == 1 && !f32_wide) {
             waves = partition_size >= VK_PARTITION_LARGE ? 4 : 2;
             kernel = waves == 4 ? VK_KERNEL_MFMA_W4 : VK_KERNEL_MFMA_W2;
         }
+
         if (parts_per_wg == 2) grid.x = (grid.x + 1) / 2;
         e = vk::launch_decode_mfma(a, dtype, group, head_dim, block_size, waves, parts_per_wg,
                                    grid, st, &ok, &block);
