@@ -421,11 +421,15 @@ vk_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         e = vk::launch_decode_dot(a, group, head_dim, block_size, grid, st, &ok, &block);
     } else {
         int waves = kernel == VK_KERNEL_MFMA_W1 ? 1 : kernel == VK_KERNEL_MFMA_W2 ? 2 : 4;
-        // fp32 at head dim 256 holds one wave per SIMD (its registers): one
-        // wave per partition in every case, the work order decided for that
-        // (32 sequences of 4k-16k tokens, (24, 4, 256): four waves 822 /
-        // 817 us at P = 512 / 1024, one wave 452.6 / 488 us).
-        const bool f32_wide = auto_waves && dtype == VK_DTYPE_F32 && head_dim == 256;
+        // fp32 at head dim 256 holds one wave per SIMD (its registers): a
+        // split grid of at least two workgroups per CU runs one wave per
+        // partition, the work order decided for that (32 sequences of
+        // 4k-16k tokens, (24, 4, 256): four waves 822 / 817 us at P = 512 /
+        // 1024, one wave 452.6 / 488 us; 512 workgroups: one wave 65.9 vs
+        // four 87.4 us); at one workgroup per CU four waves still win
+        // (46.6 vs 55.9 us).
+        const bool f32_wide = auto_waves && dtype == VK_DTYPE_F32 && head_dim == 256 &&
+                              partition_size > 0 && 4 * wgs >= slots;
         if (f32_wide) {
             waves = 1;
             kernel = VK_KERNEL_MFMA_W1;
