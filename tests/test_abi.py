@@ -67,12 +67,15 @@ def _o_plan(lens, Hq, Hkv, D, bs, mb, req, cu, per_cu=0, cap=0):
 
 
 GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256)]
+# with the multi-head and multi-query triples (G = 1 and 16), where the
+# default budget of 4 * G per CU and the 1024-first step differ most
+ALL_GEOMS = GEOMS + [(16, 16, 128), (8, 8, 256), (16, 1, 128), (16, 1, 256)]
 
 
 def test_planner_matches_oracle_rule_random():
     rng = np.random.default_rng(2024)
-    for it in range(3000):
-        Hq, Hkv, D = GEOMS[rng.integers(4)]
+    for it in range(4000):
+        Hq, Hkv, D = ALL_GEOMS[rng.integers(len(ALL_GEOMS))]
         bs = int(rng.choice([8, 16, 32]))
         S = int(rng.integers(1, 70))
         hi = int(rng.choice([300, 3000, 40000, 200000]))
